@@ -1,0 +1,100 @@
+// kernels.h -- host-side launchers of the libmoe kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+    int T, E, k, kind, renorm, n_group, topk_group;
+    float scale;
+    int logits_bf16;             // 1: bf16 bits, 0: fp32
+    const void *logits;
+    const float *bias;           // may be null
+    int32_t *ids;
+    float *weights;
+    uint32_t *zero_ptr;          // words cleared by the launch (scratch counters), may be null
+    int zero_n;                  // <= 256
+};
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+
+struct AlignArgs {
+    int T, k, E, BM, nbits;
+    int64_t cap;
+    const int32_t *ids;
+    int32_t *sorted, *eids, *npp, *counts, *inv_pos;
+};
+hipError_t launch_align(const AlignArgs &a, hipStream_t s);
+
+// One grouped GEMM over the align layout.  Rows of the M dimension are the sorted rows;
+// block b (block_m rows) multiplies by the weights of expert expert_ids[b].
+struct GemmArgs {
+    const void *A;               // gate/up: hidden [T, H] (gathered); down: h [cap, I]
+    int64_t lda;                 // elements of A per row
+    const void *B;               // expert weights, [E, rows, K]
+    int64_t ldb;                 // bytes per B row  (K elements, packed for int4)
+    int64_t b_expert_stride;     // bytes per expert
+    const uint16_t *bs, *bz;     // int4: fp16 scales / zeros [E, rows, K/128]
+    int64_t sz_expert_stride;    // int4: elements per expert of bs / bz
+    void *C;                     // gate/up: h [cap, N] bf16; down: out rows [cap, N] bf16 or fp32 partials
+    int64_t ldc;                 // elements per row of C
+    int64_t partial_stride;      // elements between split-K partial planes
+    const int32_t *sorted, *eids, *npp;
+    const float *topk_w;         // down: pair weights
+    int K, N;                    // reduction length; output columns
+    int I;                       // gate/up: offset of the up rows in w13
+    int top_k, pairs;            // pairs = T*k (the filler value)
+    int split, ksplit;           // number of K splits and the K length of each
+    const float *a_scale;        // fp8: activation scale (device scalar)
+    const float *b_scale;        // fp8: per-expert weight scales [E]
+    uint32_t *amax_out;          // fp8 gate/up: |h| max as float bits (atomicMax), may be null
+};
+
+enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
+
+struct TileInfo {
+    int BM, BN, BK, WM, WN;      // tile rows, B rows per tile, K step, wave grid
+};
+
+// Compiled tiles per weight type (MOE_DT_*).  Returns the count; fills info when non-null.
+int gemm_tile_count(int wdtype);
+bool gemm_tile_info(int wdtype, int tile, TileInfo *info);
+// Workgroups the launch uses (persistent grid) for a given upper bound of tiles.
+hipError_t launch_gemm(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
+                       int64_t max_tiles, hipStream_t s);
+
+struct ReduceArgs {
+    const void *Y;               // bf16 [cap, H] or fp32 partials [split, cap, H]
+    int64_t partial_stride;
+    int split;                   // 0: bf16 rows; >=1: fp32 partial planes
+    const int32_t *inv_pos;
+    uint16_t *out;               // bf16 [T, H]
+    int T, k, H;
+};
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
+
+// fp8 activation quantisation
+struct AbsmaxArgs {
+    const uint16_t *x;           // bf16
+    int64_t n;                   // elements
+    uint32_t *amax;              // float bits, atomicMax
+};
+hipError_t launch_absmax(const AbsmaxArgs &a, hipStream_t s);
+
+struct QuantArgs {
+    const uint16_t *x;           // bf16 rows
+    uint8_t *q;                  // e4m3 codes
+    int64_t rows, cols;
+    const uint32_t *amax;        // float bits
+    float *scale_out;            // amax/448 (or 1), written by block 0
+    const int32_t *row_valid;    // optional: sorted ids; rows with value >= pairs are zeroed
+    const int32_t *npp;          // optional: rows past *npp are skipped
+    int pairs;
+};
+hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

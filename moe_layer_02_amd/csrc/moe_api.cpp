@@ -1,0 +1,469 @@
+// moe_api.cpp -- the C ABI of libmoe (declared in include/moe.h): argument checks, plans,
+// workspace carving and the stream-ordered launch sequence.  No host synchronisation and no
+// allocation anywhere, so moe_forward can be captured into a hipGraph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace moe {
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int nbits_for(int E) {
+    int b = 0;
+    while ((1 << b) < E) b++;
+    return b;
+}
+
+moe_status check_route(const moe_route_cfg *c) {
+    if (!c) return MOE_ERR_INVALID_ARGUMENT;
+    const int E = c->num_experts, k = c->top_k;
+    if (E < 1 || E > 256 || k < 1 || k > E || k > 64) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->logits_dtype != MOE_DT_BF16 && c->logits_dtype != MOE_DT_FP32) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->kind == MOE_ROUTE_GROUPED_SIGMOID_BIAS) {
+        const int ng = c->n_group, tg = c->topk_group;
+        if (ng < 1 || ng > 64 || E % ng != 0 || tg < 1 || tg > ng) return MOE_ERR_INVALID_ARGUMENT;
+        if (k > tg * (E / ng)) return MOE_ERR_INVALID_ARGUMENT;
+    } else if (c->kind != MOE_ROUTE_SOFTMAX && c->kind != MOE_ROUTE_SIGMOID) {
+        return MOE_ERR_INVALID_ARGUMENT;
+    }
+    return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer *L) {
+    if (!L) return MOE_ERR_INVALID_ARGUMENT;
+    moe_status st = check_route(&L->route);
+    if (st != MOE_OK) return st;
+    if (L->E != L->route.num_experts) return MOE_ERR_INVALID_ARGUMENT;
+    if (L->H < 128 || L->I < 128 || L->H % 128 || L->I % 128) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)L->H * L->I > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+    if (!L->w13 || !L->w2 || !aligned(L->w13, 16) || !aligned(L->w2, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    switch (L->weight_dtype) {
+    case MOE_DT_BF16:
+        break;
+    case MOE_DT_FP8_E4M3:
+        if (!L->w13_scale || !L->w2_scale || !aligned(L->w13_scale, 4) || !aligned(L->w2_scale, 4))
+            return MOE_ERR_INVALID_ARGUMENT;
+        break;
+    case MOE_DT_INT4_G128:
+        if (!L->w13_s || !L->w13_z || !L->w2_s || !L->w2_z) return MOE_ERR_INVALID_ARGUMENT;
+        if (!aligned(L->w13_s, 2) || !aligned(L->w13_z, 2) || !aligned(L->w2_s, 2) || !aligned(L->w2_z, 2))
+            return MOE_ERR_INVALID_ARGUMENT;
+        break;
+    default:
+        return MOE_ERR_INVALID_ARGUMENT;
+    }
+    if (L->route.kind == MOE_ROUTE_GROUPED_SIGMOID_BIAS && !L->correction_bias) return MOE_ERR_INVALID_ARGUMENT;
+    if (L->correction_bias && !aligned(L->correction_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+// A plan is valid when both tiles exist for the weight type, share the block height, and
+// tile the layer's dimensions exactly.
+moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileInfo *t2) {
+    if (!p) return MOE_ERR_INVALID_ARGUMENT;
+    const int wd = L->weight_dtype;
+    if (!gemm_tile_info(wd, p->gemm1_tile, t1) || !gemm_tile_info(wd, p->gemm2_tile, t2))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (p->block_m != t1->BM || p->block_m != t2->BM) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->split_k < 1 || p->split_k > 16) return MOE_ERR_INVALID_ARGUMENT;
+    // GEMM1: K = H, output columns I (each tile covers BN/2 gate and BN/2 up rows)
+    if (L->H % t1->BK || L->I % (t1->BN / 2)) return MOE_ERR_INVALID_ARGUMENT;
+    // GEMM2: K = I split split_k ways, output columns H
+    if (L->I % (t2->BK * p->split_k) || L->H % t2->BN) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+struct Workspace {
+    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, total;
+    int64_t cap;
+};
+
+// scal words: [0] amax(x) bits, [1] amax(h) bits, [2] s1, [3] s2
+constexpr int kScalarWords = 4;
+
+Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
+    Workspace w{};
+    const int k = L->route.top_k, E = L->E;
+    const int64_t pairs = (int64_t)T * k;
+    w.cap = moe_align_capacity(T, k, E, p->block_m);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + bytes, kAlign);
+        return at;
+    };
+    w.ids = take(pairs * 4);
+    w.weights = take(pairs * 4);
+    w.sorted = take(w.cap * 4);
+    w.eids = take(w.cap / p->block_m * 4);
+    w.npp = take(4);
+    w.counts = take((size_t)E * 4);
+    w.inv_pos = take(pairs * 4);
+    w.scal = take(kScalarWords * 4);
+    const bool fp8 = L->weight_dtype == MOE_DT_FP8_E4M3;
+    w.xq = take(fp8 ? (size_t)T * L->H : 0);
+    w.h = take((size_t)w.cap * L->I * 2);
+    w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
+    w.y = take(p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
+    w.total = o;
+    return w;
+}
+
+RouteArgs route_args(const moe_route_cfg *c, int T, const void *logits, const float *bias, int32_t *ids,
+                     float *weights) {
+    RouteArgs a{};
+    a.T = T;
+    a.E = c->num_experts;
+    a.k = c->top_k;
+    a.kind = c->kind;
+    a.renorm = c->renormalize;
+    a.n_group = c->n_group;
+    a.topk_group = c->topk_group;
+    a.scale = c->routed_scaling;
+    a.logits_bf16 = c->logits_dtype == MOE_DT_BF16;
+    a.logits = logits;
+    a.bias = c->kind == MOE_ROUTE_SOFTMAX ? nullptr : bias;
+    a.ids = ids;
+    a.weights = weights;
+    return a;
+}
+
+// The stream-ordered sequence of moe_forward; events (optional) are recorded before each
+// step and after the last.
+moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const void *logits, void *out,
+                        void *workspace, size_t ws_bytes, const moe_plan *plan_in, hipStream_t stream,
+                        void *const *events, int32_t n_events, int32_t *stages, int32_t *n_stages) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if (T < 0) return MOE_ERR_INVALID_ARGUMENT;
+    moe_plan plan;
+    if (plan_in) plan = *plan_in;
+    else if ((st = moe_default_plan(L, T, &plan)) != MOE_OK) return st;
+    TileInfo t1, t2;
+    if ((st = check_plan(L, &plan, &t1, &t2)) != MOE_OK) return st;
+    if (events && n_events < MOE_STAGE_COUNT + 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (events && (!stages || !n_stages)) return MOE_ERR_INVALID_ARGUMENT;
+    if (n_stages) *n_stages = 0;
+    if (T == 0) return MOE_OK;
+    if ((int64_t)T * L->route.top_k > (int64_t)1 << 24) return MOE_ERR_UNSUPPORTED;
+    if (!hidden || !logits || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(workspace, kAlign)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(logits, L->route.logits_dtype == MOE_DT_BF16 ? 2 : 4)) return MOE_ERR_INVALID_ARGUMENT;
+    const Workspace w = layout(L, T, &plan);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+    char *ws = (char *)workspace;
+    int32_t *ids = (int32_t *)(ws + w.ids), *sorted = (int32_t *)(ws + w.sorted);
+    int32_t *eids = (int32_t *)(ws + w.eids), *npp = (int32_t *)(ws + w.npp);
+    int32_t *counts = (int32_t *)(ws + w.counts), *inv_pos = (int32_t *)(ws + w.inv_pos);
+    float *topk_w = (float *)(ws + w.weights);
+    uint32_t *scal = (uint32_t *)(ws + w.scal);
+    const bool fp8 = L->weight_dtype == MOE_DT_FP8_E4M3;
+    const int k = L->route.top_k, H = L->H, I = L->I, E = L->E;
+    const int pairs = T * k;
+    int nst = 0;
+    auto mark = [&](moe_stage s) -> hipError_t {
+        if (!events) return hipSuccess;
+        stages[nst] = s;
+        return hipEventRecord((hipEvent_t)events[nst++], stream);
+    };
+    auto fail = [&](hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; };
+    hipError_t err;
+
+    // 1. route (its first workgroup also clears the scratch words)
+    if ((err = mark(MOE_STAGE_ROUTE)) != hipSuccess) return MOE_ERR_HIP;
+    RouteArgs ra = route_args(&L->route, T, logits, L->correction_bias, ids, topk_w);
+    ra.zero_ptr = scal;
+    ra.zero_n = kScalarWords;
+    if ((err = launch_route(ra, stream)) != hipSuccess) return fail(err);
+
+    // 2. align
+    if ((err = mark(MOE_STAGE_ALIGN)) != hipSuccess) return MOE_ERR_HIP;
+    AlignArgs aa{T, k, E, plan.block_m, nbits_for(E), w.cap, ids, sorted, eids, npp, counts, inv_pos};
+    if ((err = launch_align(aa, stream)) != hipSuccess) return fail(err);
+
+    // 3. fp8: quantise the hidden states with one dynamic scale
+    const void *a1 = hidden;
+    if (fp8) {
+        if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
+        AbsmaxArgs ab{(const uint16_t *)hidden, (int64_t)T * H, &scal[0]};
+        if ((err = launch_absmax(ab, stream)) != hipSuccess) return fail(err);
+        QuantArgs q{(const uint16_t *)hidden, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2],
+                    nullptr, nullptr, pairs};
+        if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
+        a1 = ws + w.xq;
+    }
+
+    // 4. GEMM1: gate/up with SiLU * up
+    if ((err = mark(MOE_STAGE_GEMM1)) != hipSuccess) return MOE_ERR_HIP;
+    const int wd = L->weight_dtype;
+    const size_t b13_row = wd == MOE_DT_FP8_E4M3 ? H : wd == MOE_DT_INT4_G128 ? H / 2 : (size_t)H * 2;
+    const size_t b2_row = wd == MOE_DT_FP8_E4M3 ? I : wd == MOE_DT_INT4_G128 ? I / 2 : (size_t)I * 2;
+    GemmArgs g{};
+    g.A = a1;
+    g.lda = H;
+    g.B = L->w13;
+    g.ldb = (int64_t)b13_row;
+    g.b_expert_stride = (int64_t)b13_row * 2 * I;
+    g.bs = L->w13_s;
+    g.bz = L->w13_z;
+    g.sz_expert_stride = (int64_t)2 * I * (H / 128);
+    g.C = ws + w.h;
+    g.ldc = I;
+    g.sorted = sorted;
+    g.eids = eids;
+    g.npp = npp;
+    g.topk_w = topk_w;
+    g.K = H;
+    g.N = I;
+    g.I = I;
+    g.top_k = k;
+    g.pairs = pairs;
+    g.split = 1;
+    g.ksplit = H;
+    g.a_scale = (const float *)&scal[2];
+    g.b_scale = L->w13_scale;
+    g.amax_out = fp8 ? &scal[1] : nullptr;
+    const int64_t mblocks_max = w.cap / plan.block_m;
+    if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, false, g,
+                           mblocks_max * (I / (t1.BN / 2)), stream)) != hipSuccess)
+        return fail(err);
+
+    // 5. fp8: quantise h with its dynamic scale
+    const void *a2 = ws + w.h;
+    if (fp8) {
+        if ((err = mark(MOE_STAGE_H_QUANT)) != hipSuccess) return MOE_ERR_HIP;
+        QuantArgs q{(const uint16_t *)(ws + w.h), (uint8_t *)(ws + w.hq), w.cap, I, &scal[1], (float *)&scal[3],
+                    sorted, npp, pairs};
+        if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
+        a2 = ws + w.hq;
+    }
+
+    // 6. GEMM2: down projection times the top-k weight
+    if ((err = mark(MOE_STAGE_GEMM2)) != hipSuccess) return MOE_ERR_HIP;
+    GemmArgs d = g;
+    d.A = a2;
+    d.lda = I;
+    d.B = L->w2;
+    d.ldb = (int64_t)b2_row;
+    d.b_expert_stride = (int64_t)b2_row * H;
+    d.bs = L->w2_s;
+    d.bz = L->w2_z;
+    d.sz_expert_stride = (int64_t)H * (I / 128);
+    d.C = ws + w.y;
+    d.ldc = H;
+    d.partial_stride = w.cap * (int64_t)H;
+    d.K = I;
+    d.N = H;
+    d.split = plan.split_k;
+    d.ksplit = I / plan.split_k;
+    d.a_scale = (const float *)&scal[3];
+    d.b_scale = L->w2_scale;
+    d.amax_out = nullptr;
+    if ((err = launch_gemm(wd, plan.gemm2_tile, GEMM_DOWN, plan.split_k > 1, d,
+                           mblocks_max * (H / t2.BN) * plan.split_k, stream)) != hipSuccess)
+        return fail(err);
+
+    // 7. unpermute and reduce
+    if ((err = mark(MOE_STAGE_REDUCE)) != hipSuccess) return MOE_ERR_HIP;
+    ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out, T, k, H};
+    if ((err = launch_reduce(r, stream)) != hipSuccess) return fail(err);
+    if (events) {
+        if (hipEventRecord((hipEvent_t)events[nst], stream) != hipSuccess) return MOE_ERR_HIP;
+        *n_stages = nst;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(moe_status s) {
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+int64_t moe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m) {
+    if (T < 0 || k < 1 || E < 1 || block_m < 1) return -1;
+    const int64_t pairs = (int64_t)T * k;
+    const int64_t used = std::min<int64_t>(pairs, E);
+    const int64_t cap = pairs + used * (block_m - 1);
+    return (cap + block_m - 1) / block_m * block_m;
+}
+
+moe_status moe_route(const moe_route_cfg *cfg, int32_t T, const void *logits, const float *bias,
+                     int32_t *topk_ids, float *topk_weights, void *stream) {
+    moe_status st = check_route(cfg);
+    if (st != MOE_OK) return st;
+    if (T < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->kind == MOE_ROUTE_GROUPED_SIGMOID_BIAS && !bias) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(logits, cfg->logits_dtype == MOE_DT_BF16 ? 2 : 4) || !aligned(topk_ids, 4) ||
+        !aligned(topk_weights, 4) || (bias && !aligned(bias, 4)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    RouteArgs a = route_args(cfg, T, logits, bias, topk_ids, topk_weights);
+    return launch_route(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_align(int32_t T, int32_t k, int32_t E, int32_t block_m, const int32_t *topk_ids,
+                     int32_t *sorted_token_ids, int32_t *expert_ids, int32_t *num_tokens_post_padded,
+                     int32_t *expert_counts, int32_t *inv_pos, void *stream) {
+    if (T < 0 || k < 1 || E < 1 || E > 256 || block_m < 1 || block_m > 1024) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * k > (int64_t)1 << 24) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    const int32_t *ptrs[] = {topk_ids, sorted_token_ids, expert_ids, num_tokens_post_padded, expert_counts, inv_pos};
+    for (const int32_t *p : ptrs)
+        if (!p || !aligned(p, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    AlignArgs a{T, k, E, block_m, nbits_for(E), moe_align_capacity(T, k, E, block_m), topk_ids, sorted_token_ids,
+                expert_ids, num_tokens_post_padded, expert_counts, inv_pos};
+    return launch_align(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (T < 0 || !plan) return MOE_ERR_INVALID_ARGUMENT;
+    const int wd = layer->weight_dtype;
+    const double rows_per_expert = (double)T * layer->route.top_k / layer->E;
+    // Candidate (block_m, gemm1 tile, gemm2 tile) by rows per expert; the first that tiles
+    // the layer's shape is taken, with split-K on GEMM2 while its tiles underfill the GPU.
+    struct Cand { int bm, g1, g2; };
+    Cand cands[8];
+    int nc = 0;
+    if (wd == MOE_DT_BF16) {
+        if (rows_per_expert <= 16) { cands[nc++] = {16, 0, 0}; cands[nc++] = {16, 1, 1}; }
+        if (rows_per_expert <= 48) cands[nc++] = {32, 2, 2};
+        if (rows_per_expert <= 160) cands[nc++] = {64, 3, 3};
+        cands[nc++] = {128, 4, 4};
+        cands[nc++] = {16, 1, 1};
+    } else if (wd == MOE_DT_FP8_E4M3) {
+        if (rows_per_expert <= 16) { cands[nc++] = {16, 0, 0}; cands[nc++] = {16, 0, 1}; cands[nc++] = {16, 1, 1}; }
+        if (rows_per_expert <= 48) cands[nc++] = {32, 2, 2};
+        if (rows_per_expert <= 160) cands[nc++] = {64, 3, 3};
+        cands[nc++] = {128, 4, 4};
+        cands[nc++] = {16, 1, 1};
+    } else {
+        if (rows_per_expert <= 16) cands[nc++] = {16, 0, 0};
+        if (rows_per_expert <= 48) cands[nc++] = {32, 1, 1};
+        if (rows_per_expert <= 160) cands[nc++] = {64, 2, 2};
+        cands[nc++] = {128, 3, 3};
+        cands[nc++] = {16, 0, 0};
+    }
+    for (int c = 0; c < nc; c++) {
+        moe_plan p{cands[c].bm, cands[c].g1, cands[c].g2, 1};
+        TileInfo t1, t2;
+        if (check_plan(layer, &p, &t1, &t2) != MOE_OK) continue;
+        // split GEMM2's K while its tiles (for the experts in use) underfill the GPU
+        const int64_t used = std::min<int64_t>((int64_t)T * layer->route.top_k, layer->E);
+        const int64_t blocks = std::max<int64_t>(used, (int64_t)T * layer->route.top_k / p.block_m);
+        int64_t tiles2 = blocks * (layer->H / t2.BN);
+        for (int sk = 2; sk <= 8; sk *= 2) {
+            if (tiles2 * p.split_k >= 512) break;
+            moe_plan q = p;
+            q.split_k = sk;
+            if (check_plan(layer, &q, &t1, &t2) == MOE_OK) p = q;
+            else break;
+        }
+        *plan = p;
+        return MOE_OK;
+    }
+    return MOE_ERR_UNSUPPORTED;
+}
+
+moe_status moe_workspace_bytes(const moe_layer *layer, int32_t T, const moe_plan *plan, size_t *bytes) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (T < 0 || !bytes) return MOE_ERR_INVALID_ARGUMENT;
+    moe_plan p;
+    if (plan) p = *plan;
+    else if ((st = moe_default_plan(layer, T, &p)) != MOE_OK) return st;
+    TileInfo t1, t2;
+    if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
+    *bytes = layout(layer, T, &p).total;
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_layer *layer, int32_t T, const void *hidden, const void *logits, void *out,
+                       void *workspace, size_t workspace_bytes, const moe_plan *plan, void *stream) {
+    return forward_impl(layer, T, hidden, logits, out, workspace, workspace_bytes, plan, (hipStream_t)stream,
+                        nullptr, 0, nullptr, nullptr);
+}
+
+moe_status moe_forward_profiled(const moe_layer *layer, int32_t T, const void *hidden, const void *logits,
+                                void *out, void *workspace, size_t workspace_bytes, const moe_plan *plan,
+                                void *stream, void *const *events, int32_t n_events, int32_t *stages,
+                                int32_t *n_stages) {
+    if (!events) return MOE_ERR_INVALID_ARGUMENT;
+    return forward_impl(layer, T, hidden, logits, out, workspace, workspace_bytes, plan, (hipStream_t)stream,
+                        events, n_events, stages, n_stages);
+}
+
+moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *plan, char *buf, size_t len) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (T < 0 || !plan || !buf || len == 0) return MOE_ERR_INVALID_ARGUMENT;
+    TileInfo t1, t2;
+    if ((st = check_plan(layer, plan, &t1, &t2)) != MOE_OK) return st;
+    std::snprintf(buf, len,
+                  "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d] gemm2=%d[BM%d BN%d BK%d waves%dx%d] split_k=%d",
+                  plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, plan->gemm2_tile, t2.BM,
+                  t2.BN, t2.BK, t2.WM, t2.WN, plan->split_k);
+    return MOE_OK;
+}
+
+moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_plan *plan, int64_t *offsets) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (T < 0 || !offsets) return MOE_ERR_INVALID_ARGUMENT;
+    moe_plan p;
+    if (plan) p = *plan;
+    else if ((st = moe_default_plan(layer, T, &p)) != MOE_OK) return st;
+    TileInfo t1, t2;
+    if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
+    const Workspace w = layout(layer, T, &p);
+    const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos,
+                                    w.scal, w.xq, w.h, w.hq, w.y};
+    for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// quant.hip -- dynamic per-tensor E4M3 quantisation of activations for the w8a8 layer.
+//
+// fp8 w8a8 with per-tensor scales is how SGLang PR #2333 serves Qwen2-57B-A14B-FP8 and what
+// the FBGEMM article's grouped GEMM supports.  A tensor's scale is its largest magnitude
+// over 448 (the largest E4M3 value), so the largest element lands on +-448.  Two kernels:
+//   absmax: largest |x| over the tensor, combined across workgroups with an integer
+//           atomicMax on the fp32 bit pattern (non-negative floats order like their bits;
+//           max is order-independent, so the result is exact and reproducible);
+//   quant:  code = RNE_E4M3(x * (448 / amax)) (the product in fp32, clamped to +-448), and
+//           block 0 publishes scale = amax / 448 (1 when amax is 0) for the GEMM epilogue.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_absmax(AbsmaxArgs a) {
+    float m = 0.0f;
+    const int64_t n8 = a.n / 8;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+        const uint4 v = ((const uint4 *)a.x)[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if (lane_id() == 0) atomicMax(a.amax, __float_as_uint(m));
+}
+
+__device__ __forceinline__ void scales_from_amax(uint32_t bits, float *scale, float *inv) {
+    const float amax = __uint_as_float(bits);
+    if (amax == 0.0f) {
+        *scale = 1.0f;
+        *inv = 1.0f;
+    } else {
+        *scale = amax / 448.0f;   // IEEE division: the same rounding on every side
+        *inv = 448.0f / amax;
+    }
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float inv) {
+    const float lim = 448.0f;
+    a = fminf(fmaxf(a * inv, -lim), lim);
+    b = fminf(fmaxf(b * inv, -lim), lim);
+    c = fminf(fmaxf(c * inv, -lim), lim);
+    d = fminf(fmaxf(d * inv, -lim), lim);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// 8 elements (one 16-byte bf16 load) per thread -> 8 codes (one 8-byte store)
+__global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
+    float scale, inv;
+    scales_from_amax(*a.amax, &scale, &inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.scale_out = scale;
+    const int64_t c8 = a.cols / 8;
+    int64_t rows = a.rows;
+    if (a.npp) rows = min(rows, (int64_t)*a.npp);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * c8; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / c8;
+        uint2 out = make_uint2(0, 0);
+        if (!a.row_valid || a.row_valid[r] < a.pairs) {
+            const uint4 v = ((const uint4 *)a.x)[i];
+            out.x = e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u), inv);
+            out.y = e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                           __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u), inv);
+        }
+        ((uint2 *)a.q)[i] = out;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_absmax(const AbsmaxArgs &a, hipStream_t s) {
+    int64_t blocks = (a.n / 8 + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_absmax, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant(const QuantArgs &a, hipStream_t s) {
+    int64_t blocks = (a.rows * (a.cols / 8) + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_quant, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

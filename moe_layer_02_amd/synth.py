@@ -21,10 +21,14 @@ shape):
             popularity follows Zipf(1.2)
 
 Distribution conventions: N(0, v) names the variance v; weights ~ N(0, 1/fan_in) with
-fan_in the reduction length (H for w13, I for w2).  Every tensor is drawn in fp32 from
-numpy's PCG64 seeded by SeedSequence([seed, tensor id, block]) and rounded to nearest
-even into its storage type.  Hidden states and logits are drawn in blocks of 64 rows, so
-the first T rows do not depend on how many rows are drawn (the T-prefix property).
+fan_in the reduction length (H for w13, I for w2).  Every tensor is drawn in fp32 and
+rounded to nearest even into its storage type.  Hidden states, logits and biases come from
+numpy's PCG64 seeded by SeedSequence([seed, tensor id, block]); hidden states and logits
+are drawn in blocks of 64 rows, so the first T rows do not depend on how many rows are
+drawn (the T-prefix property).  Expert weights are drawn per expert, either on the host
+(numpy PCG64, SeedSequence([seed, tensor id, expert])) or, for the multi-GB full-size
+layers, on the GPU (torch's Philox generator seeded from the same SeedSequence); the two
+streams differ, so a test or benchmark uses one of them for both the GPU and the oracle.
 """
 from __future__ import annotations
 
@@ -145,36 +149,44 @@ def correction_bias(cfg: LayerConfig):
     return torch.from_numpy(b)
 
 
-def _expert_matrix(cfg, tensor_id, e, rows, cols):
-    """fp32 [rows, cols] ~ N(0, 1/cols) for expert e."""
-    return _rng(cfg.seed, tensor_id, e).standard_normal((rows, cols), dtype=np.float32) * np.float32(
-        1.0 / math.sqrt(cols))
+def _expert_matrix(cfg, tensor_id, e, rows, cols, device="cpu"):
+    """fp32 [rows, cols] ~ N(0, 1/cols) for expert e (numpy array on the host, or a torch
+    tensor drawn on the given CUDA device)."""
+    if device == "cpu":
+        return _rng(cfg.seed, tensor_id, e).standard_normal((rows, cols), dtype=np.float32) * np.float32(
+            1.0 / math.sqrt(cols))
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([cfg.seed, tensor_id, e]).generate_state(1, np.uint64)[0] >> 1))
+    return torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32) * (1.0 / math.sqrt(cols))
 
 
-def _fp8_encode(w32: np.ndarray):
+def _fp8_encode(w32):
     """Per-tensor E4M3 storage of one expert matrix: scale = amax / 448, codes = the
     nearest E4M3 value of w / scale (torch's float8_e4m3fn cast)."""
-    amax = float(np.abs(w32).max())
+    w = torch.from_numpy(w32) if isinstance(w32, np.ndarray) else w32
+    amax = float(w.abs().max())
     scale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
-    q = torch.from_numpy(np.clip(w32 / scale, -448.0, 448.0)).to(torch.float8_e4m3fn)
+    q = torch.clamp(w / float(scale), -448.0, 448.0).to(torch.float8_e4m3fn)
     return q.view(torch.uint8), scale
 
 
-def _int4_encode(w32: np.ndarray):
+def _int4_encode(w32):
     """Asymmetric int4 with group size 128 along the row: per (row, group) an fp16 scale
     s = (max - min) / 15 and an integer-valued fp16 zero point z = clamp(rint(-min / s),
-    0, 15); nibble q = clamp(rint(w / s + z), 0, 15).  Column c goes to byte c/2, the low
-    nibble when c is even.  Returns (packed uint8 [rows, cols/2], s fp16, z fp16)."""
-    rows, cols = w32.shape
-    g = w32.reshape(rows, cols // 128, 128)
-    lo, hi = g.min(axis=2), g.max(axis=2)
-    s = ((hi - lo) / 15.0).astype(np.float16)
-    s = np.where(s == 0, np.float16(1.0), s)
-    s32 = s.astype(np.float32)
-    z = np.clip(np.rint(-lo / s32), 0, 15).astype(np.float16)
-    q = np.clip(np.rint(g / s32[..., None] + z.astype(np.float32)[..., None]), 0, 15).astype(np.uint8)
+    0, 15); nibble q = clamp(rint(w / s + z), 0, 15) (rint: round half to even).  Column c
+    goes to byte c/2, the low nibble when c is even.  Returns torch tensors (packed uint8
+    [rows, cols/2], s fp16, z fp16) on the input's device."""
+    w = torch.from_numpy(w32) if isinstance(w32, np.ndarray) else w32
+    rows, cols = w.shape
+    g = w.reshape(rows, cols // 128, 128)
+    lo, hi = g.amin(dim=2), g.amax(dim=2)
+    s = ((hi - lo) / 15.0).to(torch.float16)
+    s = torch.where(s == 0, torch.ones_like(s), s)
+    s32 = s.float()
+    z = torch.clamp(torch.round(-lo / s32), 0, 15).to(torch.float16)
+    q = torch.clamp(torch.round(g / s32[..., None] + z.float()[..., None]), 0, 15).to(torch.uint8)
     q = q.reshape(rows, cols)
-    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    packed = q[:, 0::2] | (q[:, 1::2] << 4)
     return packed, s, z
 
 
@@ -199,50 +211,37 @@ class ExpertWeights:
                 if isinstance(getattr(self, f.name), torch.Tensor)}
 
 
-def expert_weights(cfg: LayerConfig) -> ExpertWeights:
-    """All E experts' weights, drawn expert by expert (one expert in fp32 at a time)."""
+def expert_weights(cfg: LayerConfig, device: str = "cpu") -> ExpertWeights:
+    """All E experts' weights, drawn expert by expert (one expert in fp32 at a time), stored
+    on `device` ("cpu": numpy stream; a CUDA device: torch's Philox stream, drawn there)."""
     E, H, I = cfg.E, cfg.H, cfg.I
+    mat = lambda tid, e, r, c: _expert_matrix(cfg, tid, e, r, c, device)  # noqa: E731
+    to_bf16 = (lambda a: _bf16(a)) if device == "cpu" else (lambda a: a.to(torch.bfloat16))
     if cfg.wdtype == WDT_BF16:
-        w13 = torch.empty((E, 2 * I, H), dtype=torch.bfloat16)
-        w2 = torch.empty((E, H, I), dtype=torch.bfloat16)
+        w13 = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device=device)
+        w2 = torch.empty((E, H, I), dtype=torch.bfloat16, device=device)
         for e in range(E):
-            w13[e] = _bf16(_expert_matrix(cfg, _T_W13, e, 2 * I, H))
-            w2[e] = _bf16(_expert_matrix(cfg, _T_W2, e, H, I))
+            w13[e] = to_bf16(mat(_T_W13, e, 2 * I, H))
+            w2[e] = to_bf16(mat(_T_W2, e, H, I))
         return ExpertWeights(WDT_BF16, w13, w2)
     if cfg.wdtype == WDT_FP8:
-        w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8)
-        w2 = torch.empty((E, H, I), dtype=torch.uint8)
+        w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+        w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
         s13 = torch.empty(E, dtype=torch.float32)
         s2 = torch.empty(E, dtype=torch.float32)
         for e in range(E):
-            w13[e], s13[e] = _fp8_encode(_expert_matrix(cfg, _T_W13, e, 2 * I, H))
-            w2[e], s2[e] = _fp8_encode(_expert_matrix(cfg, _T_W2, e, H, I))
-        return ExpertWeights(WDT_FP8, w13, w2, w13_scale=s13, w2_scale=s2)
+            w13[e], s13[e] = _fp8_encode(mat(_T_W13, e, 2 * I, H))
+            w2[e], s2[e] = _fp8_encode(mat(_T_W2, e, H, I))
+        return ExpertWeights(WDT_FP8, w13, w2, w13_scale=s13.to(device), w2_scale=s2.to(device))
     if cfg.wdtype == WDT_INT4:
-        w13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8)
-        w2 = torch.empty((E, H, I // 2), dtype=torch.uint8)
-        s13 = torch.empty((E, 2 * I, H // 128), dtype=torch.float16)
+        w13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device)
+        w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=device)
+        s13 = torch.empty((E, 2 * I, H // 128), dtype=torch.float16, device=device)
         z13 = torch.empty_like(s13)
-        s2 = torch.empty((E, H, I // 128), dtype=torch.float16)
+        s2 = torch.empty((E, H, I // 128), dtype=torch.float16, device=device)
         z2 = torch.empty_like(s2)
         for e in range(E):
-            p, s, z = _int4_encode(_expert_matrix(cfg, _T_W13, e, 2 * I, H))
-            w13[e], s13[e], z13[e] = torch.from_numpy(p), torch.from_numpy(s), torch.from_numpy(z)
-            p, s, z = _int4_encode(_expert_matrix(cfg, _T_W2, e, H, I))
-            w2[e], s2[e], z2[e] = torch.from_numpy(p), torch.from_numpy(s), torch.from_numpy(z)
+            w13[e], s13[e], z13[e] = _int4_encode(mat(_T_W13, e, 2 * I, H))
+            w2[e], s2[e], z2[e] = _int4_encode(mat(_T_W2, e, H, I))
         return ExpertWeights(WDT_INT4, w13, w2, w13_s=s13, w13_z=z13, w2_s=s2, w2_z=z2)
     raise ValueError("unknown weight dtype")
-
-
-def layer_flops(cfg: LayerConfig, T: int) -> float:
-    """Algorithmic FLOPs of one layer call: 2*T*k*(2I*H) for gate/up plus 2*T*k*(H*I)
-    for down; routing, activation and reduction terms are negligible and excluded."""
-    return 6.0 * T * cfg.k * cfg.H * cfg.I
-
-
-def bytes_per_weight(cfg: LayerConfig) -> float:
-    if cfg.wdtype == WDT_BF16:
-        return 2.0
-    if cfg.wdtype == WDT_FP8:
-        return 1.0
-    return 0.5 + 4.0 / 128.0          # nibble + fp16 scale and zero per 128 weights

@@ -296,12 +296,34 @@ double orc_weight(const orc_weights *W, int m, int e, int64_t n, int64_t c)
     return ((double)q - z) * s;
 }
 
-/* Dequantise one row of matrix m of expert e into buf (length cols). */
+/* Dequantise one row of matrix m of expert e into buf (length cols): the value orc_weight
+ * gives for every column, walking the row once (an int4 group's scale and zero point are
+ * decoded once per group). */
 static void weight_row(const orc_weights *W, int m, int e, int64_t n, double *buf)
 {
     int64_t rows, cols;
     mat_shape(W, m, &rows, &cols);
-    for (int64_t c = 0; c < cols; c++) buf[c] = orc_weight(W, m, e, n, c);
+    if (W->wdtype == ORC_BF16) {
+        const uint16_t *row = (const uint16_t *)(m == 0 ? W->w13 : W->w2) + ((int64_t)e * rows + n) * cols;
+        for (int64_t c = 0; c < cols; c++) buf[c] = orc_bf16_to_f32(row[c]);
+        return;
+    }
+    if (W->wdtype == ORC_FP8_E4M3) {
+        const uint8_t *row = (const uint8_t *)(m == 0 ? W->w13 : W->w2) + ((int64_t)e * rows + n) * cols;
+        double scale = (m == 0 ? W->w13_scale : W->w2_scale)[e];
+        for (int64_t c = 0; c < cols; c++) buf[c] = (double)orc_e4m3_to_f32(row[c]) * scale;
+        return;
+    }
+    const uint8_t *row = (const uint8_t *)(m == 0 ? W->w13 : W->w2) + ((int64_t)e * rows + n) * (cols / 2);
+    int64_t g0 = ((int64_t)e * rows + n) * (cols / 128);
+    for (int64_t g = 0; g < cols / 128; g++) {
+        double s = orc_f16_to_f32((m == 0 ? W->w13_s : W->w2_s)[g0 + g]);
+        double z = orc_f16_to_f32((m == 0 ? W->w13_z : W->w2_z)[g0 + g]);
+        for (int64_t c = g * 128; c < (g + 1) * 128; c++) {
+            int q = (c % 2 == 0) ? (row[c / 2] & 0xF) : (row[c / 2] >> 4);
+            buf[c] = ((double)q - z) * s;
+        }
+    }
 }
 
 static double dot(const double *a, const double *b, int64_t n)

@@ -1,0 +1,96 @@
+"""Helpers of the GPU parity tests: device layers from the seeded generator, the oracle's
+view of the same inputs, comparison metrics.  (Not a test module.)"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_layer_02_amd import abi, synth
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+# spec tolerances on the layer output (relative L2 over the whole [T, H] output)
+TOL = {synth.WDT_BF16: 1e-2, synth.WDT_FP8: 3e-2, synth.WDT_INT4: 3e-2}
+
+
+def say(*a):
+    """Name the case about to run on the GPU (flushed, so a crash still shows it)."""
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 / fp16 tensor -> its uint16 bit patterns (host numpy)."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy()
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+@functools.lru_cache(maxsize=2)
+def weights(name: str, device: str):
+    """Expert weights of a config: 'cpu' draws them on the host, 'cuda' on the GPU."""
+    return synth.expert_weights(synth.CONFIGS[name], device=device)
+
+
+def oracle_weights(cfg, w: synth.ExpertWeights) -> oracle.Weights:
+    wd = {synth.WDT_BF16: oracle.BF16, synth.WDT_FP8: oracle.FP8_E4M3, synth.WDT_INT4: oracle.INT4_G128}[cfg.wdtype]
+    if cfg.wdtype == synth.WDT_BF16:
+        return oracle.Weights(wd, cfg.E, cfg.H, cfg.I, bits(w.w13), bits(w.w2))
+    if cfg.wdtype == synth.WDT_FP8:
+        return oracle.Weights(wd, cfg.E, cfg.H, cfg.I, u8(w.w13), u8(w.w2),
+                              w13_scale=w.w13_scale.cpu().numpy(), w2_scale=w.w2_scale.cpu().numpy())
+    return oracle.Weights(wd, cfg.E, cfg.H, cfg.I, u8(w.w13), u8(w.w2), w13_s=bits(w.w13_s), w13_z=bits(w.w13_z),
+                          w2_s=bits(w.w2_s), w2_z=bits(w.w2_z))
+
+
+def device_layer(cfg, w: synth.ExpertWeights, bias=None) -> abi.MoELayer:
+    d = {k: v.cuda().contiguous() for k, v in w.tensors().items()}
+    return abi.MoELayer.create(cfg.E, cfg.H, cfg.I, cfg.k, cfg.route_kind, cfg.wdtype, d["w13"], d["w2"],
+                               renormalize=cfg.renormalize, n_group=cfg.n_group, topk_group=cfg.topk_group,
+                               routed_scaling=cfg.routed_scaling, w13_scale=d.get("w13_scale"),
+                               w2_scale=d.get("w2_scale"), w13_s=d.get("w13_s"), w13_z=d.get("w13_z"),
+                               w2_s=d.get("w2_s"), w2_z=d.get("w2_z"),
+                               correction_bias=None if bias is None else bias.cuda().contiguous())
+
+
+def oracle_route(cfg, logits_bits, bias):
+    return oracle.route(cfg.route_kind, cfg.E, cfg.k, logits_bits, renormalize=cfg.renormalize,
+                        n_group=cfg.n_group, topk_group=cfg.topk_group, routed_scaling=cfg.routed_scaling,
+                        bias=None if bias is None else bias.numpy())
+
+
+def workspace_view(layer, T, plan, ws, region, dtype, count):
+    off = abi.moe_workspace_offsets(layer.struct, T, plan)[region]
+    return ws[off:off + count * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+
+
+def valid_plans(layer, T):
+    """Every (block_m, tile1, tile2, split) the library accepts for this layer."""
+    n = 8
+    out = []
+    for g1 in range(n):
+        for g2 in range(n):
+            for sk in (1, 2, 4, 8):
+                for bm in (16, 32, 64, 128):
+                    p = abi.Plan(bm, g1, g2, sk)
+                    try:
+                        abi.moe_workspace_bytes(layer.struct, T, p)
+                    except abi.MoEError:
+                        continue
+                    out.append(p)
+    return out

@@ -33,6 +33,13 @@ MUTANTS = {
     "int4_nibbles_swapped": ("(c % 2 == 0) ? (byte & 0xF) : (byte >> 4)", "(c % 2 == 0) ? (byte >> 4) : (byte & 0xF)"),
     "int4_zero_ignored": ("return ((double)q - z) * s;", "return (double)q * s;"),
     "int4_group_64": ("(cols / 128) + c / 128;", "(cols / 128) + c / 256;"),
+    "int4_row_nibbles_swapped": ("(c % 2 == 0) ? (row[c / 2] & 0xF) : (row[c / 2] >> 4)",
+                                 "(c % 2 == 0) ? (row[c / 2] >> 4) : (row[c / 2] & 0xF)"),
+    "int4_row_zero_ignored": ("buf[c] = ((double)q - z) * s;", "buf[c] = (double)q * s;"),
+    "bf16_row_transposed": ("((int64_t)e * rows + n) * cols;\n        for (int64_t c = 0; c < cols; c++) buf[c] = orc_bf16_to_f32(row[c]);",
+                            "((int64_t)e * rows) * cols + n;\n        for (int64_t c = 0; c < cols; c++) buf[c] = orc_bf16_to_f32(row[c * rows]);"),
+    "fp8_row_scale_of_other_matrix": ("double scale = (m == 0 ? W->w13_scale : W->w2_scale)[e];",
+                                      "double scale = W->w13_scale[e];"),
     # fp8 and codecs
     "e4m3_ties_to_odd": ("((lo & 1) ? hi : lo)", "((lo & 1) ? lo : hi)"),
     "e4m3_bias_8": ("ex - 7);\n    return (float)(sign ? -v : v);\n}\n\n/* Round",
