@@ -1,0 +1,265 @@
+"""Benchmark of the fused-MoE layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config mixtral] [--tokens 4096] [--no-sweep]
+
+A step is one moe_forward (route, align, [fp8 quantisation], GEMM1, GEMM2, reduce) over one
+batch of T tokens of seeded synthetic inputs already resident in HBM; steps are replayed
+from a captured hipGraph.  Prints one JSON line: whole-layer tokens/s (the headline),
+TFLOP/s and HBM GB/s with their fractions of the MI355X peaks, the dominant kernel's
+roofline (its duration from HIP events recorded on the launch stream around each step of
+the forward), the CPU oracle's throughput on a bounded sample of the same workload, and a
+sweep of the same numbers over T.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from moe_layer_02_amd import abi, synth  # noqa: E402
+
+METRIC = "fused-MoE layer tokens/s + TFLOP/s & HBM GB/s (% of roofline) vs T, 1 GPU"
+PEAK_HBM = 8.0e12                                  # B/s, MI355X HBM3E
+PEAK_MFMA = {synth.WDT_BF16: 2.5e15, synth.WDT_FP8: 5.0e15, synth.WDT_INT4: 2.5e15}   # dense, fp16 for int4
+DTYPE_NAME = {synth.WDT_BF16: "bf16", synth.WDT_FP8: "fp8-e4m3 w8a8", synth.WDT_INT4: "int4-g128 w / fp16 mfma"}
+WORKLOAD = {
+    "mixtral": "Mixtral-8x7B MoE layer, one TP2 shard (E=8, top-2 softmax renormalised, H=4096, I=7168, bf16)",
+    "qwen2": "Qwen2-57B-A14B routed experts, one TP4 shard (E=64, top-8 softmax, H=3584, I=640, fp8 w8a8)",
+    "deepseek": "DeepSeek-V3 routed experts (E=256, grouped sigmoid top-8, H=7168, I=2048, int4 g128)",
+    "scout": "Llama-4-Scout MoE layer (E=16, top-1 sigmoid, Zipf(1.2) load, H=5120, I=8192, bf16)",
+    "tiny": "tiny MoE layer (E=8, top-2 softmax, H=128, I=256, bf16)",
+}
+
+
+def bytes_per_weight(cfg):
+    return {synth.WDT_BF16: 2.0, synth.WDT_FP8: 1.0, synth.WDT_INT4: 0.5 + 4.0 / 128.0}[cfg.wdtype]
+
+
+def layer_flops(cfg, T):
+    """2*T*k*(2I*H) (gate/up) + 2*T*k*(H*I) (down); routing and elementwise work excluded."""
+    return 6.0 * T * cfg.k * cfg.H * cfg.I
+
+
+def layer_min_bytes(cfg, T, active):
+    """Weights of the experts in use, hidden in, output out (bf16), logits in (bf16)."""
+    return active * 3.0 * cfg.H * cfg.I * bytes_per_weight(cfg) + 4.0 * T * cfg.H + 2.0 * T * cfg.E
+
+
+def gemm_algorithmic(cfg, T, active, stage):
+    """(flops, bytes) one launch of a GEMM stage must do / move at the minimum:
+    gemm1 reads the active experts' w13 and the T hidden rows, writes T*k rows of h (bf16);
+    gemm2 reads the active experts' w2 and the T*k rows of h, writes T*k output rows (bf16)."""
+    bpw = bytes_per_weight(cfg)
+    a_bytes = 1.0 if cfg.wdtype == synth.WDT_FP8 else 2.0
+    if stage == "gemm1":
+        return (4.0 * T * cfg.k * cfg.H * cfg.I,
+                active * 2.0 * cfg.I * cfg.H * bpw + T * cfg.H * a_bytes + T * cfg.k * cfg.I * 2.0)
+    return (2.0 * T * cfg.k * cfg.H * cfg.I,
+            active * 1.0 * cfg.H * cfg.I * bpw + T * cfg.k * cfg.I * a_bytes + T * cfg.k * cfg.H * 2.0)
+
+
+class Bench:
+    def __init__(self, cfg):
+        self.cfg = cfg
+        t0 = time.time()
+        self.w = synth.expert_weights(cfg, device="cuda")
+        self.bias = synth.correction_bias(cfg)
+        d = self.w.tensors()
+        self.layer = abi.MoELayer.create(
+            cfg.E, cfg.H, cfg.I, cfg.k, cfg.route_kind, cfg.wdtype, d["w13"], d["w2"],
+            renormalize=cfg.renormalize, n_group=cfg.n_group, topk_group=cfg.topk_group,
+            routed_scaling=cfg.routed_scaling, w13_scale=d.get("w13_scale"), w2_scale=d.get("w2_scale"),
+            w13_s=d.get("w13_s"), w13_z=d.get("w13_z"), w2_s=d.get("w2_s"), w2_z=d.get("w2_z"),
+            correction_bias=None if self.bias is None else self.bias.cuda())
+        torch.cuda.synchronize()
+        print("[bench] %s weights generated on the GPU in %.1f s" % (cfg.name, time.time() - t0),
+              file=sys.stderr, flush=True)
+
+    def prepare(self, T):
+        x = synth.hidden_states(self.cfg, T).cuda()
+        lg = synth.router_logits(self.cfg, T).cuda()
+        plan = self.layer.plan(T)
+        ws = self.layer.workspace(T, plan)
+        out = torch.empty((T, self.cfg.H), dtype=torch.bfloat16, device="cuda")
+        return x, lg, plan, ws, out
+
+    def active_experts(self, T, plan, ws):
+        off = abi.moe_workspace_offsets(self.layer.struct, T, plan)["expert_counts"]
+        counts = ws[off:off + 4 * self.cfg.E].view(torch.int32).cpu().numpy()
+        return int((counts > 0).sum())
+
+    def time_graph(self, T, steps, warmup):
+        x, lg, plan, ws, out = self.prepare(T)
+        self.layer.forward(x, lg, out=out, workspace=ws, plan=plan)        # eager once (first-use setup)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                self.layer.forward(x, lg, out=out, workspace=ws, plan=plan)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        active = self.active_experts(T, plan, ws)
+        return ms, active, plan, (x, lg, ws, out)
+
+    def time_stages(self, T, plan, bufs, steps):
+        """Average duration of each step of the forward, from HIP events recorded on the
+        launch stream before and after each kernel (eager launches)."""
+        x, lg, ws, out = bufs
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
+        acc = {}
+        names = None
+        for i in range(steps + 1):
+            names = abi.moe_forward_profiled(self.layer.struct, T, x, lg, out, ws, ev, plan)
+            torch.cuda.synchronize()
+            if i == 0:
+                continue                                  # first call: warm
+            for j, n in enumerate(names):
+                acc[n] = acc.get(n, 0.0) + ev[j].elapsed_time(ev[j + 1]) * 1e3
+        return {n: acc[n] / steps for n in names}
+
+
+def measure(b: Bench, T, steps, warmup, stage_steps):
+    cfg = b.cfg
+    ms, active, plan, bufs = b.time_graph(T, steps, warmup)
+    stages = b.time_stages(T, plan, bufs, stage_steps)
+    sec = ms / 1e3
+    flops, mbytes = layer_flops(cfg, T), layer_min_bytes(cfg, T, active)
+    t_hbm, t_mfma = mbytes / PEAK_HBM, flops / PEAK_MFMA[cfg.wdtype]
+    return dict(T=T, ms_per_step=ms, tokens_per_s=T / sec, tflops=flops / sec / 1e12, hbm_gbps=mbytes / sec / 1e9,
+                frac_hbm=mbytes / sec / PEAK_HBM, frac_mfma=flops / sec / PEAK_MFMA[cfg.wdtype],
+                roofline_frac=max(t_hbm, t_mfma) / sec, bound="hbm" if t_hbm >= t_mfma else "mfma",
+                active_experts=active, plan=abi.moe_plan_describe(b.layer.struct, T, plan),
+                stages_us={k: round(v, 2) for k, v in stages.items()})
+
+
+def kernel_roofline(cfg, m):
+    """Roofline of the longest-running kernel of the step."""
+    gemms = {k: v for k, v in m["stages_us"].items() if k in ("gemm1", "gemm2")}
+    name = max(gemms, key=gemms.get)
+    dur = gemms[name] * 1e-6
+    flops, nbytes = gemm_algorithmic(cfg, m["T"], m["active_experts"], name)
+    if flops / PEAK_MFMA[cfg.wdtype] >= nbytes / PEAK_HBM:
+        ach, peak, unit, bound = flops / dur / 1e12, PEAK_MFMA[cfg.wdtype] / 1e12, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = nbytes / dur / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
+    return dict(kernel=name, bound=bound, achieved=round(ach, 2), peak=peak, unit=unit, frac=round(ach / peak, 4),
+                traffic=None, avg_us=round(gemms[name], 2), algorithmic_flops=flops, algorithmic_bytes=nbytes)
+
+
+def cpu_baseline(b: Bench, T, budget_s=15.0):
+    """The oracle (single-threaded C, fp64) on a sample of the same workload: routing of all
+    T tokens, then the layer output token by token until the time budget is spent."""
+    import oracle
+    cfg = b.cfg
+    x, lg = synth.hidden_states(cfg, T), synth.router_logits(cfg, T)
+    bits = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    h = {k: v.cpu() for k, v in b.w.tensors().items()}
+    wd = {synth.WDT_BF16: oracle.BF16, synth.WDT_FP8: oracle.FP8_E4M3, synth.WDT_INT4: oracle.INT4_G128}[cfg.wdtype]
+    if cfg.wdtype == synth.WDT_BF16:
+        W = oracle.Weights(wd, cfg.E, cfg.H, cfg.I, bits(h["w13"]), bits(h["w2"]))
+    elif cfg.wdtype == synth.WDT_FP8:
+        W = oracle.Weights(wd, cfg.E, cfg.H, cfg.I, h["w13"].numpy(), h["w2"].numpy(),
+                           w13_scale=h["w13_scale"].numpy(), w2_scale=h["w2_scale"].numpy())
+    else:
+        W = oracle.Weights(wd, cfg.E, cfg.H, cfg.I, h["w13"].numpy(), h["w2"].numpy(), w13_s=bits(h["w13_s"]),
+                           w13_z=bits(h["w13_z"]), w2_s=bits(h["w2_s"]), w2_z=bits(h["w2_z"]))
+    t0 = time.time()
+    ids, w = oracle.route(cfg.route_kind, cfg.E, cfg.k, bits(lg), renormalize=cfg.renormalize, n_group=cfg.n_group,
+                          topk_group=cfg.topk_group, routed_scaling=cfg.routed_scaling,
+                          bias=None if b.bias is None else b.bias.numpy())
+    t_route = time.time() - t0
+    if cfg.wdtype == synth.WDT_FP8:
+        # w8a8 needs every token's intermediate for its second scale: time the whole layer at
+        # a smaller T of the same layer instead
+        Ts = max(1, min(T, 8))
+        t0 = time.time()
+        oracle.forward(W, bits(x[:Ts]), ids[:Ts], w[:Ts])
+        el = time.time() - t0
+        return dict(value=round(Ts / el, 4), unit="tokens/s", cores=1, kind="oracle",
+                    sample="whole w8a8 layer at T=%d (first %d tokens of the batch), %.1f s" % (Ts, Ts, el))
+    n, el = 0, 0.0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(T)
+    while n < T and (el < budget_s or n < 2):
+        t0 = time.time()
+        oracle.forward(W, bits(x), ids, w, tokens=[int(order[n])])
+        el += time.time() - t0
+        n += 1
+    per_token = el / n + t_route / T
+    return dict(value=round(1.0 / per_token, 4), unit="tokens/s", cores=1, kind="oracle",
+                sample="%d of %d tokens (random), routing of all %d; %.1f s" % (n, T, T, el + t_route))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--tokens", type=int, default=None, help="T of the headline step (default: largest of the sweep)")
+    ap.add_argument("--sweep", default="1,32,256,1024,4096", help="comma-separated T values ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=256,
+                    help="after timing, one device copy of this size (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the layer is one GPU's expert/TP shard and this build has no "
+              "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    cfg = synth.CONFIGS[args.config]
+    T = args.tokens or cfg.t_max
+    b = Bench(cfg)
+    head = measure(b, T, args.steps, args.warmup, stage_steps=max(3, min(args.steps, 10)))
+    print("[bench] T=%d %.3f ms/step %s" % (T, head["ms_per_step"], head["plan"]), file=sys.stderr, flush=True)
+    sweep = []
+    for t in [int(s) for s in args.sweep.split(",") if s.strip()]:
+        if t == T or t > cfg.t_max:
+            continue
+        m = measure(b, t, args.steps, args.warmup, stage_steps=3)
+        sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()})
+        print("[bench] T=%d %.3f ms/step" % (t, m["ms_per_step"]), file=sys.stderr, flush=True)
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(b, T)
+    roof = kernel_roofline(cfg, head)
+    line = {
+        "metric": METRIC, "value": round(head["tokens_per_s"], 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[cfg.wdtype],
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": {"workload": WORKLOAD[cfg.name], "T": T, "E": cfg.E, "top_k": cfg.k, "H": cfg.H, "I": cfg.I,
+                   "plan": head["plan"]},
+        "tflops": round(head["tflops"], 3), "hbm_gbps": round(head["hbm_gbps"], 2),
+        "frac_mfma": round(head["frac_mfma"], 4), "frac_hbm": round(head["frac_hbm"], 4),
+        "layer_roofline_frac": round(head["roofline_frac"], 4), "layer_bound": head["bound"],
+        "stages_us": head["stages_us"], "roofline": roof, "cpu_baseline": cpu, "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -230,7 +230,8 @@ typedef enum {
     MOE_WS_SCALARS = 7,       /* fp8: [0] amax(x) and [1] amax(h) as fp32 bits, [2] the
                                  activation scale s1, [3] the intermediate scale s2     */
     MOE_WS_X_Q = 8,           /* fp8: E4M3 [T, H] quantised hidden states            */
-    MOE_WS_H = 9,             /* bf16 [capacity, I] SiLU(gate) * up per sorted row   */
+    MOE_WS_H = 9,             /* [capacity, I] SiLU(gate) * up per sorted row: bf16, or
+                                 fp32 for fp8 weights (its E4M3 code is chosen in fp32) */
     MOE_WS_H_Q = 10,          /* fp8: E4M3 [capacity, I] quantised h                 */
     MOE_WS_Y = 11,            /* bf16 [capacity, H] weighted expert rows, or with split_k > 1
                                  fp32 [split_k, capacity, H] partial sums             */

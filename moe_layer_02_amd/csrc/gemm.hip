@@ -18,8 +18,9 @@
 //         turns 8 nibbles into fp16 in registers ((q | 0x6400) is 1024 + q in fp16, minus
 //         1024 + z is the exact integer q - z, times the group's fp16 scale) and multiplies
 //         on v_mfma_f32_16x16x32_f16; the bf16 activations go to fp16 on their way into LDS.
-// Gate/up epilogue: SiLU(gate) * up in fp32, stored as bf16 (fp8: also the tile's largest
-// |h| into a device word with an integer atomicMax -- max is order-independent).  Down
+// Gate/up epilogue: SiLU(gate) * up in fp32, stored as bf16 (fp8: kept in fp32, so that
+// its E4M3 code is later decided in fp32, and the tile's largest |h| goes into a device
+// word with an integer atomicMax -- max is order-independent).  Down
 // epilogue: times the pair's top-k weight; either bf16 rows or fp32 split-K partial planes
 // that the reduce step sums in a fixed order (no floating-point atomics: SGLang PR #2333,
 // Background, traces its corrupted outputs to atomic_add).
@@ -309,7 +310,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
         if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
         if constexpr (KIND == GEMM_GATE_UP) {
             float amax = 0.0f;
-            uint16_t *h = (uint16_t *)a.C;
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
@@ -317,11 +317,15 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
-                        const uint16_t hb = f32_to_bf16_bits(silu(g) * u);
+                        const float hv = silu(g) * u;
                         const int row = row0 + wm * C::TM + fm * 16 + 4 * (lane >> 4) + i;
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
-                        h[(int64_t)row * a.ldc + col] = hb;
-                        if constexpr (WT == WT_FP8) amax = fmaxf(amax, fabsf(bf16_bits_to_f32(hb)));
+                        if constexpr (WT == WT_FP8) {   // fp32: its E4M3 code is decided in fp32
+                            ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
+                            amax = fmaxf(amax, fabsf(hv));
+                        } else {
+                            ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
+                        }
                     }
             if constexpr (WT == WT_FP8) {
 #pragma unroll

@@ -38,7 +38,7 @@ struct GemmArgs {
     int64_t b_expert_stride;     // bytes per expert
     const uint16_t *bs, *bz;     // int4: fp16 scales / zeros [E, rows, K/128]
     int64_t sz_expert_stride;    // int4: elements per expert of bs / bz
-    void *C;                     // gate/up: h [cap, N] bf16; down: out rows [cap, N] bf16 or fp32 partials
+    void *C;                     // gate/up: h [cap, N] bf16 (fp8: fp32); down: out rows [cap, N] bf16 or fp32 partials
     int64_t ldc;                 // elements per row of C
     int64_t partial_stride;      // elements between split-K partial planes
     const int32_t *sorted, *eids, *npp;
@@ -84,7 +84,8 @@ struct AbsmaxArgs {
 hipError_t launch_absmax(const AbsmaxArgs &a, hipStream_t s);
 
 struct QuantArgs {
-    const uint16_t *x;           // bf16 rows
+    const void *x;               // bf16 rows, or fp32 rows when x_f32
+    int x_f32;
     uint8_t *q;                  // e4m3 codes
     int64_t rows, cols;
     const uint32_t *amax;        // float bits

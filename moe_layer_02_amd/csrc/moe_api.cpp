@@ -133,7 +133,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.scal = take(kScalarWords * 4);
     const bool fp8 = L->weight_dtype == MOE_DT_FP8_E4M3;
     w.xq = take(fp8 ? (size_t)T * L->H : 0);
-    w.h = take((size_t)w.cap * L->I * 2);
+    w.h = take((size_t)w.cap * L->I * (fp8 ? 4 : 2));
     w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
     w.y = take(p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
     w.total = o;
@@ -219,8 +219,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
         AbsmaxArgs ab{(const uint16_t *)hidden, (int64_t)T * H, &scal[0]};
         if ((err = launch_absmax(ab, stream)) != hipSuccess) return fail(err);
-        QuantArgs q{(const uint16_t *)hidden, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2],
-                    nullptr, nullptr, pairs};
+        QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs};
         if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
         a1 = ws + w.xq;
     }
@@ -264,8 +263,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     const void *a2 = ws + w.h;
     if (fp8) {
         if ((err = mark(MOE_STAGE_H_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-        QuantArgs q{(const uint16_t *)(ws + w.h), (uint8_t *)(ws + w.hq), w.cap, I, &scal[1], (float *)&scal[3],
-                    sorted, npp, pairs};
+        QuantArgs q{ws + w.h, 1, (uint8_t *)(ws + w.hq), w.cap, I, &scal[1], (float *)&scal[3], sorted, npp, pairs};
         if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
         a2 = ws + w.hq;
     }

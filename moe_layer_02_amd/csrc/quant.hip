@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, f
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// 8 elements (one 16-byte bf16 load) per thread -> 8 codes (one 8-byte store)
+// 8 elements (bf16 or fp32) per thread -> 8 codes (one 8-byte store)
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     float scale, inv;
     scales_from_amax(*a.amax, &scale, &inv);
@@ -64,11 +64,17 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
         const int64_t r = i / c8;
         uint2 out = make_uint2(0, 0);
         if (!a.row_valid || a.row_valid[r] < a.pairs) {
-            const uint4 v = ((const uint4 *)a.x)[i];
-            out.x = e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u), inv);
-            out.y = e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
-                           __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u), inv);
+            if (a.x_f32) {
+                const float4 lo = ((const float4 *)a.x)[2 * i], hi = ((const float4 *)a.x)[2 * i + 1];
+                out.x = e4m3x4(lo.x, lo.y, lo.z, lo.w, inv);
+                out.y = e4m3x4(hi.x, hi.y, hi.z, hi.w, inv);
+            } else {
+                const uint4 v = ((const uint4 *)a.x)[i];
+                out.x = e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u), inv);
+                out.y = e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                               __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u), inv);
+            }
         }
         ((uint2 *)a.q)[i] = out;
     }

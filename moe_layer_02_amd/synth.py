@@ -165,8 +165,8 @@ def _fp8_encode(w32):
     nearest E4M3 value of w / scale (torch's float8_e4m3fn cast)."""
     w = torch.from_numpy(w32) if isinstance(w32, np.ndarray) else w32
     amax = float(w.abs().max())
-    scale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
-    q = torch.clamp(w / float(scale), -448.0, 448.0).to(torch.float8_e4m3fn)
+    scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    q = torch.clamp(w / scale, -448.0, 448.0).to(torch.float8_e4m3fn)
     return q.view(torch.uint8), scale
 
 

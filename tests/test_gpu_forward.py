@@ -170,6 +170,32 @@ def test_qwen2_fp8_activation_codes_exact():
     assert sc[2] == np.float32(amax / np.float32(448.0))
 
 
+def test_qwen2_fp8_intermediate_codes():
+    """The intermediate h is quantised from fp32 on both sides: its scale agrees to fp32
+    rounding and almost every code is identical (a code may differ by one step where the
+    two fp32 accumulation orders straddle a rounding midpoint)."""
+    c = case("qwen2")
+    T = 16
+    out, ws = c.gpu(T)
+    plan = c.layer.plan(T)
+    x, lg = c.inputs(T)
+    ids, _ = oracle_route(c.cfg, bits(lg), c.bias)
+    _, ref_codes, ref_sc = oracle.fp8_intermediate(c.W, bits(x), ids)
+    sc = workspace_view(c.layer, T, plan, ws, "scalars", torch.float32, 4).cpu().numpy()
+    assert abs(sc[3] / ref_sc[1] - 1) < 1e-5
+    cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, plan.block_m)
+    hq = workspace_view(c.layer, T, plan, ws, "h_q", torch.uint8, cap * c.cfg.I).cpu().numpy().reshape(cap, -1)
+    inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, T * c.cfg.k).cpu().numpy()
+    got = hq[inv]                                   # rows back in pair order
+    val = lambda q: oracle.e4m3_to_f32(q).astype(np.float64)  # noqa: E731
+    diff = got != ref_codes
+    frac = diff.mean()
+    say("  h codes differing: %.2e" % frac)
+    assert frac < 2e-3
+    a, b = np.abs(val(got[diff])), np.abs(val(ref_codes[diff]))
+    assert (np.abs(a - b) <= np.maximum(a, b) * 0.125 + 2.0 ** -9).all()     # one E4M3 step at most
+
+
 # ---- int4 group 128 --------------------------------------------------------------------
 
 @pytest.mark.parametrize("T", [1, 3])
