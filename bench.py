@@ -13,6 +13,7 @@ sweep of the same numbers over T.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -68,8 +69,9 @@ def gemm_algorithmic(cfg, T, active, stage):
 
 
 class Bench:
-    def __init__(self, cfg):
+    def __init__(self, cfg, plan_override=None, plan_T=None):
         self.cfg = cfg
+        self.plan_override, self.plan_T = plan_override, plan_T
         t0 = time.time()
         self.w = synth.expert_weights(cfg, device="cuda")
         self.bias = synth.correction_bias(cfg)
@@ -87,7 +89,7 @@ class Bench:
     def prepare(self, T):
         x = synth.hidden_states(self.cfg, T).cuda()
         lg = synth.router_logits(self.cfg, T).cuda()
-        plan = self.layer.plan(T)
+        plan = self.plan_override if self.plan_override and T == self.plan_T else self.layer.plan(T)
         ws = self.layer.workspace(T, plan)
         out = torch.empty((T, self.cfg.H), dtype=torch.bfloat16, device="cuda")
         return x, lg, plan, ws, out
@@ -163,7 +165,35 @@ def kernel_roofline(cfg, m):
     else:
         ach, peak, unit, bound = nbytes / dur / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
     return dict(kernel=name, bound=bound, achieved=round(ach, 2), peak=peak, unit=unit, frac=round(ach / peak, 4),
-                traffic=None, avg_us=round(gemms[name], 2), algorithmic_flops=flops, algorithmic_bytes=nbytes)
+                traffic=measured_traffic(cfg, m["T"], name), avg_us=round(gemms[name], 2),
+                algorithmic_flops=flops, algorithmic_bytes=nbytes)
+
+
+KERNEL_SOURCES = ("moe_layer_02_amd/csrc/gemm.hip", "moe_layer_02_amd/csrc/common.h", "moe_layer_02_amd/csrc/kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg, T, kernel):
+    """HBM-side bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a device copy of known size), or None when no
+    summary exists for this workload or the GEMM sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = data.get("%s:T%d:%s" % (cfg.name, T, kernel))
+    if not rec or rec.get("kernel_sha") != kernel_source_sha():
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def cpu_baseline(b: Bench, T, budget_s=15.0):
@@ -219,6 +249,7 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="T of the headline step (default: largest of the sweep)")
     ap.add_argument("--sweep", default="1,32,256,1024,4096", help="comma-separated T values ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plan", default=None, help="block_m,gemm1_tile,gemm2_tile,split_k for the headline T")
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="after timing, one device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -229,7 +260,8 @@ def main():
     torch.cuda.init()
     cfg = synth.CONFIGS[args.config]
     T = args.tokens or cfg.t_max
-    b = Bench(cfg)
+    plan = abi.Plan(*[int(v) for v in args.plan.split(",")]) if args.plan else None
+    b = Bench(cfg, plan, T)
     head = measure(b, T, args.steps, args.warmup, stage_steps=max(3, min(args.steps, 10)))
     print("[bench] T=%d %.3f ms/step %s" % (T, head["ms_per_step"], head["plan"]), file=sys.stderr, flush=True)
     sweep = []

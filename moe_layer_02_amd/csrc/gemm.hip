@@ -101,11 +101,18 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
     const int j0 = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int nk = a.ksplit / C::BK;
 
+    const int mn = mblocks * ntiles;
     for (int tile = j0; tile < total; tile += G) {
-        const int mb = tile % mblocks;
-        const int rest = tile / mblocks;
-        const int s = rest % a.split;
-        const int nt = rest / a.split;
+        // split outermost; then groups of group_m blocks, block index fastest inside a group,
+        // so one XCD's window of consecutive tiles covers a compact (block x N tile) patch
+        // whose A rows and weight rows its L2 serves to several workgroups
+        const int s = tile / mn;
+        const int rest = tile - s * mn;
+        const int gm0 = rest / (a.group_m * ntiles) * a.group_m;
+        const int gsz = min(a.group_m, mblocks - gm0);
+        const int local = rest - gm0 * ntiles;
+        const int mb = gm0 + local % gsz;
+        const int nt = local / gsz;
         const int e = a.eids[mb];
         const int row0 = mb * C::BM;
         const int kbase = s * a.ksplit;
@@ -397,7 +404,11 @@ hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
     if (max_tiles < grid) grid = max_tiles;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemm<C, WT, KIND, PARTIAL>), dim3((unsigned)grid), dim3(C::NT), 0, s, a);
+    // blocks per tile group: about the square root of one XCD's concurrent workgroups
+    GemmArgs b = a;
+    b.group_m = 1;
+    while (b.group_m * b.group_m * 4 <= grid / 8 && b.group_m < 16) b.group_m *= 2;
+    hipLaunchKernelGGL((k_gemm<C, WT, KIND, PARTIAL>), dim3((unsigned)grid), dim3(C::NT), 0, s, b);
     return hipGetLastError();
 }
 
@@ -417,14 +428,14 @@ int gemm_tile_count(int wdtype) {
 bool gemm_tile_info(int wdtype, int tile, TileInfo *info) {
 #define INFO_TILE(id, bm, bn, bk, wm, wn) \
     if (tile == id) {                     \
-        *info = TileInfo{bm, bn, bk, wm, wn}; \
+        *info = TileInfo{bm, bn, bk, wm, wn, 0, 16}; \
         return true;                      \
     }
     if (wdtype == WT_BF16) { BF16_TILES(INFO_TILE) }
     if (wdtype == WT_FP8) { FP8_TILES(INFO_TILE) }
     if (wdtype == WT_INT4) { INT4_TILES(INFO_TILE) }
 #undef INFO_TILE
-    return false;
+    return pipe_tile_info(wdtype, tile, info);
 }
 
 hipError_t launch_gemm(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
@@ -437,7 +448,7 @@ hipError_t launch_gemm(int wdtype, int tile, GemmKind kind, bool partial, const 
     if (wdtype == WT_BF16) { BF16_TILES(L_BF16) }
     if (wdtype == WT_FP8) { FP8_TILES(L_FP8) }
     if (wdtype == WT_INT4) { INT4_TILES(L_INT4) }
-    return hipErrorInvalidValue;
+    return launch_gemm_pipe(wdtype, tile, kind, partial, a, max_tiles, s);
 }
 
 }  // namespace moe

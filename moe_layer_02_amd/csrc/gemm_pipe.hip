@@ -1,0 +1,403 @@
+// gemm_pipe.hip -- the grouped GEMMs with a multi-stage direct-to-LDS pipeline (bf16, fp8).
+//
+// Same tiles, tile order and epilogues as gemm.hip, but the operands never pass through
+// VGPRs: gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from HBM/L2 straight into
+// LDS, so ST stages of the K loop can be in flight at once (the register-staged kernels keep
+// one).  A stage holds KS "slabs"; a slab is 128 bytes of K (64 bf16 / 128 E4M3) for every
+// A row and B row of the tile.  One wave instruction fills 8 rows x 128 bytes of one slab;
+// to keep the MFMA fragment reads free of bank conflicts without padding (the DMA writes
+// LDS contiguously), chunk c (16 bytes) of row r is stored at position c ^ swz(r) with
+// swz(r) = (r >> 1) & 7: a pair of rows shares a position but sits in the other half of
+// the 64 banks, and 8 pairs cover all positions -- measured on gfx950 at the full
+// ds_read_b128 rate for both the 16x16 and the 32x32 fragment patterns, where c ^ (r & 7)
+// loses 20-35% to conflicts.  Lane l of an instruction (8 rows from a multiple of 8)
+// therefore fetches the chunk (l & 7) ^ swz(row of l).
+//
+// K loop, per step kt: wait until this wave's loads of stage kt have landed (s_waitcnt
+// vmcnt with the later stages still counted), s_barrier (so every wave's part has
+// landed, and every wave is done reading the buffer about to be refilled), issue the loads
+// of stage kt + ST - 1 into that buffer, then run the MFMAs of stage kt.  The barrier is a
+// plain s_barrier: a __syncthreads() fence would make the compiler drain every in-flight
+// load at each step.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+enum { WT_BF16 = 0, WT_FP8 = 2 };
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_>
+struct PCfg {
+    static constexpr int BM = BM_, BN = BN_, KS = KS_, ST = ST_, WM = WM_, WN = WN_;
+    static constexpr int MS = MS_;                            // MFMA output tile: 16x16 or 32x32
+    static constexpr int NW = WM * WN, NT = NW * kWave;
+    static constexpr int SLAB_K = WT == WT_FP8 ? 128 : 64;   // elements in a 128-byte slab row
+    static constexpr int BK = KS * SLAB_K;
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MS, FN = TN / MS;
+    static constexpr int A_STAGE = KS * BM * 128, STAGE = KS * (BM + BN) * 128;
+    static constexpr int A_LOADS = KS * BM / 8, LOADS = KS * (BM + BN) / 8;   // wave instructions per stage
+    static constexpr int LPW = LOADS / NW;
+    static_assert(LOADS % NW == 0, "stage loads must split evenly over the waves");
+    static_assert(BM % (MS * WM) == 0 && BN % (MS * WN) == 0 && BM % 8 == 0, "tile / wave grid mismatch");
+    static_assert(MS == 16 || (MS == 32 && WT == WT_BF16), "32x32 MFMA tiles are bf16 only");
+    static_assert((ST - 2) * LPW <= 63, "vmcnt range");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most n (a multiple of LPW, n <= (ST-2)*LPW) of this wave's loads are pending
+template <int LPW, int MAXS>
+__device__ __forceinline__ void wait_stages(int later) {
+    if constexpr (MAXS >= 3) {
+        if (later >= 3) { wait_vmcnt<3 * LPW>(); return; }
+    }
+    if constexpr (MAXS >= 2) {
+        if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
+    }
+    if constexpr (MAXS >= 1) {
+        if (later >= 1) { wait_vmcnt<LPW>(); return; }
+    }
+    wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// LDS position of 16-byte chunk c of tile row r (see the file comment)
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int MS> struct AccOf { typedef f32x4 type; };
+template <> struct AccOf<32> { typedef f32x16 type; };
+
+// Row of a 16x16 (32x32) MFMA output fragment held in accumulator value r of this lane;
+// its column is lane % 16 (lane % 32).
+template <int MS>
+__device__ __forceinline__ int frag_row(int lane, int r) {
+    if constexpr (MS == 32) return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    return 4 * (lane >> 4) + r;
+}
+
+template <class C, int WT, int KIND, bool PARTIAL>
+__global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE];
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int npp = *a.npp;
+    const int mblocks = npp / C::BM;
+    const int n_out = KIND == GEMM_GATE_UP ? C::BN / 2 : C::BN;
+    const int ntiles = a.N / n_out;
+    const int mn = mblocks * ntiles;
+    const int total = mn * a.split;
+    const int G = gridDim.x;
+    const int j0 = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int nk = a.ksplit / C::BK;
+    const int ebytes = WT == WT_FP8 ? 1 : 2;                  // A and B element bytes
+
+    for (int tile = j0; tile < total; tile += G) {
+        const int s = tile / mn;
+        const int rest = tile - s * mn;
+        const int gm0 = rest / (a.group_m * ntiles) * a.group_m;
+        const int gsz = min(a.group_m, mblocks - gm0);
+        const int local = rest - gm0 * ntiles;
+        const int mb = gm0 + local % gsz;
+        const int nt = local / gsz;
+        const int e = a.eids[mb];
+        const int row0 = mb * C::BM;
+        const int64_t kb = (int64_t)s * a.ksplit * ebytes;     // byte offset of this split's K
+
+        // per load instruction q of this wave: the lane's global source (at K = 0 of the
+        // split) and the wave's LDS destination offset inside a stage
+        const char *src[C::LPW];
+        int dst[C::LPW];
+#pragma unroll
+        for (int q = 0; q < C::LPW; q++) {
+            const int ins = wave + q * C::NW;
+            const int r_in = lane >> 3;
+            if (ins < C::A_LOADS) {
+                const int slab = ins / (C::BM / 8), rb = ins % (C::BM / 8) * 8;
+                const int r = rb + r_in;
+                const int chunk = (lane & 7) ^ swz(r);
+                int64_t arow;
+                if (KIND == GEMM_GATE_UP) {
+                    const int p = a.sorted[row0 + r];
+                    arow = p < a.pairs ? p / a.top_k : 0;     // filler rows read token 0 (never used)
+                } else {
+                    arow = row0 + r;
+                }
+                src[q] = (const char *)a.A + arow * a.lda * ebytes + kb + slab * 128 + chunk * 16;
+                dst[q] = (slab * C::BM + rb) * 128;
+            } else {
+                const int j = ins - C::A_LOADS;
+                const int slab = j / (C::BN / 8), rb = j % (C::BN / 8) * 8;
+                const int rr = rb + r_in;
+                const int chunk = (lane & 7) ^ swz(rr);
+                int64_t grow;
+                if (KIND == GEMM_GATE_UP) {   // LDS rows of wave column w: its gate half, then its up half
+                    const int wcol = rr / C::TN, i = rr % C::TN, half = C::TN / 2;
+                    const int col = nt * (C::BN / 2) + wcol * half + (i % half);
+                    grow = i < half ? col : a.I + col;
+                } else {
+                    grow = (int64_t)nt * C::BN + rr;
+                }
+                src[q] = (const char *)a.B + (int64_t)e * a.b_expert_stride + grow * a.ldb + kb + slab * 128 + chunk * 16;
+                dst[q] = C::A_STAGE + (slab * C::BN + rb) * 128;
+            }
+        }
+        auto issue = [&](int kstep) {
+            char *st = smem + (kstep % C::ST) * C::STAGE;
+            const int64_t koff = (int64_t)kstep * C::KS * 128;
+#pragma unroll
+            for (int q = 0; q < C::LPW; q++)
+                __builtin_amdgcn_global_load_lds((const void *)(src[q] + koff), (lds_ptr)(st + dst[q]), 16, 0, 0);
+        };
+
+        using Acc = typename AccOf<C::MS>::type;
+        constexpr int NR = C::MS == 32 ? 16 : 4;              // accumulator values per lane per fragment
+        Acc acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; i++)
+#pragma unroll
+            for (int j = 0; j < C::FN; j++)
+#pragma unroll
+                for (int r = 0; r < NR; r++) acc[i][j][r] = 0.f;
+
+        // every wave is done with the previous tile's buffers before they are refilled
+        block_barrier();
+#pragma unroll
+        for (int p = 0; p < C::ST - 1; p++)
+            if (p < nk) issue(p);
+
+        for (int kt = 0; kt < nk; kt++) {
+            wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nk - 1 - kt));
+            block_barrier();
+            if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
+            const char *sa = smem + (kt % C::ST) * C::STAGE, *sb = sa + C::A_STAGE;
+#pragma unroll
+            for (int sl = 0; sl < C::KS; sl++) {
+                if constexpr (WT == WT_BF16 && C::MS == 32) {
+                    // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step
+#pragma unroll
+                    for (int kk = 0; kk < 4; kk++) {
+                        const int ci = kk * 2 + (lane >> 5);
+                        bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++) {
+                            const int r = wm * C::TM + fm * 32 + (lane & 31);
+                            af[fm] = *(const bf16x8 *)(sa + (sl * C::BM + r) * 128 + ((ci ^ swz(r)) << 4));
+                        }
+#pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++) {
+                            const int r = wn * C::TN + fn * 32 + (lane & 31);
+                            bfr[fn] = *(const bf16x8 *)(sb + (sl * C::BN + r) * 128 + ((ci ^ swz(r)) << 4));
+                        }
+#pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++)
+                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+                    }
+                } else if constexpr (WT == WT_BF16) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; kk++) {
+                        const int ci = kk * 4 + (lane >> 4);
+                        bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++) {
+                            const int r = wm * C::TM + fm * 16 + (lane & 15);
+                            af[fm] = *(const bf16x8 *)(sa + (sl * C::BM + r) * 128 + ((ci ^ swz(r)) << 4));
+                        }
+#pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++) {
+                            const int r = wn * C::TN + fn * 16 + (lane & 15);
+                            bfr[fn] = *(const bf16x8 *)(sb + (sl * C::BN + r) * 128 + ((ci ^ swz(r)) << 4));
+                        }
+#pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++)
+                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+                    }
+                } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
+                    const int c0 = 2 * (lane >> 4);
+                    i32x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; fm++) {
+                        const int r = wm * C::TM + fm * 16 + (lane & 15);
+                        const char *row = sa + (sl * C::BM + r) * 128;
+                        const uint4 lo = *(const uint4 *)(row + ((c0 ^ swz(r)) << 4));
+                        const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ swz(r)) << 4));
+                        af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    }
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const int r = wn * C::TN + fn * 16 + (lane & 15);
+                        const char *row = sb + (sl * C::BN + r) * 128;
+                        const uint4 lo = *(const uint4 *)(row + ((c0 ^ swz(r)) << 4));
+                        const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ swz(r)) << 4));
+                        bfr[fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    }
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++)
+                            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                af[fm], bfr[fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+                }
+            }
+        }
+
+        // ---- epilogue: accumulator value i of fragment (fm, fn) is row frag_row(lane, i),
+        //      column lane % MS of that fragment ----
+        float scale = 1.0f;
+        if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
+        const int lcol = lane & (C::MS - 1);
+        if constexpr (KIND == GEMM_GATE_UP) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
+                    const bool valid = a.sorted[row] < a.pairs;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
+                        const float hv = silu(g) * u;
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
+                        if constexpr (WT == WT_FP8) {
+                            ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
+                            if (valid) amax = fmaxf(amax, fabsf(hv));
+                        } else {
+                            ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
+                        }
+                    }
+                }
+            if constexpr (WT == WT_FP8) {
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                if (lane == 0 && a.amax_out) atomicMax(a.amax_out, __float_as_uint(amax));
+            }
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
+                    const int p = a.sorted[row];
+                    if (p >= a.pairs) continue;   // filler row: never read back
+                    const float w = a.topk_w[p] * scale;
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const int col = nt * C::BN + wn * C::TN + fn * C::MS + lcol;
+                        const float v = acc[fm][fn][i] * w;
+                        if constexpr (PARTIAL)
+                            ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
+                        else
+                            ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(v);
+                    }
+                }
+        }
+    }
+}
+
+// ---- tile tables (ids continue gemm.hip's per weight type) --------------------------------
+//        id  BM   BN  KS ST WM WN MS
+#define PIPE_BF16_TILES(X)              \
+    X(6, 256, 256, 1, 2, 2, 2, 16)      \
+    X(7, 128, 256, 1, 3, 2, 2, 16)      \
+    X(8, 128, 128, 1, 4, 2, 2, 16)      \
+    X(9, 16, 128, 2, 4, 1, 4, 16)       \
+    X(10, 16, 64, 4, 3, 1, 2, 16)       \
+    X(11, 64, 128, 1, 4, 2, 2, 16)      \
+    X(12, 32, 128, 2, 3, 1, 4, 16)      \
+    X(13, 128, 256, 1, 3, 2, 2, 32)     \
+    X(14, 128, 128, 1, 4, 2, 2, 32)     \
+    X(15, 64, 128, 1, 4, 2, 2, 32)      \
+    X(16, 256, 128, 1, 3, 2, 2, 32)     \
+    X(17, 256, 256, 1, 2, 2, 2, 32)     \
+    X(18, 64, 256, 1, 4, 1, 4, 32)      \
+    X(19, 32, 256, 1, 4, 1, 4, 32)      \
+    X(20, 256, 256, 1, 2, 2, 4, 16)     \
+    X(21, 256, 256, 1, 2, 2, 4, 32)     \
+    X(22, 128, 256, 1, 3, 2, 4, 16)     \
+    X(23, 256, 128, 1, 3, 4, 2, 16)
+#define PIPE_FP8_TILES(X)               \
+    X(6, 256, 256, 1, 2, 2, 2, 16)      \
+    X(7, 128, 256, 1, 3, 2, 2, 16)      \
+    X(8, 128, 128, 1, 4, 2, 2, 16)      \
+    X(9, 16, 128, 2, 4, 1, 4, 16)       \
+    X(10, 64, 128, 1, 4, 2, 2, 16)      \
+    X(11, 32, 128, 2, 3, 1, 4, 16)      \
+    X(12, 256, 256, 1, 2, 2, 4, 16)     \
+    X(13, 128, 256, 1, 3, 2, 4, 16)
+
+template <class C, int WT, int KIND, bool PARTIAL>
+hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
+    static int occ_cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int occ = dev < 64 ? __atomic_load_n(&occ_cache[dev], __ATOMIC_RELAXED) : 0;
+    if (occ == 0) {
+        hipError_t err =
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_pipe<C, WT, KIND, PARTIAL>, C::NT, 0);
+        if (err != hipSuccess) return err;
+        if (occ < 1) occ = 1;
+        if (dev < 64) __atomic_store_n(&occ_cache[dev], occ, __ATOMIC_RELAXED);
+    }
+    int64_t grid = (int64_t)device_cu_count() * occ;
+    if (max_tiles < grid) grid = max_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid < 1) grid = 1;
+    GemmArgs b = a;
+    b.group_m = 1;
+    while (b.group_m * b.group_m * 4 <= grid / 8 && b.group_m < 16) b.group_m *= 2;
+    hipLaunchKernelGGL((k_gemm_pipe<C, WT, KIND, PARTIAL>), dim3((unsigned)grid), dim3(C::NT), 0, s, b);
+    return hipGetLastError();
+}
+
+template <class C, int WT>
+hipError_t launch_kind(GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
+    if (kind == GEMM_GATE_UP) return launch_one<C, WT, GEMM_GATE_UP, false>(a, max_tiles, s);
+    if (partial) return launch_one<C, WT, GEMM_DOWN, true>(a, max_tiles, s);
+    return launch_one<C, WT, GEMM_DOWN, false>(a, max_tiles, s);
+}
+
+}  // namespace
+
+bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
+#define PINFO(WT, id, bm, bn, ks, st, wm, wn, ms)                                          \
+    if (tile == id) {                                                                      \
+        *info = TileInfo{bm, bn, ks * (WT == WT_FP8 ? 128 : 64), wm, wn, st, ms};          \
+        return true;                                                                       \
+    }
+#define PI_BF16(id, bm, bn, ks, st, wm, wn, ms) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms)
+#define PI_FP8(id, bm, bn, ks, st, wm, wn, ms) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms)
+    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) }
+    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) }
+    return false;
+}
+
+hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
+                            int64_t max_tiles, hipStream_t s) {
+#define PLAUNCH(WT, id, bm, bn, ks, st, wm, wn, ms) \
+    if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms>, WT>(kind, partial, a, max_tiles, s);
+#define PL_BF16(id, bm, bn, ks, st, wm, wn, ms) PLAUNCH(WT_BF16, id, bm, bn, ks, st, wm, wn, ms)
+#define PL_FP8(id, bm, bn, ks, st, wm, wn, ms) PLAUNCH(WT_FP8, id, bm, bn, ks, st, wm, wn, ms)
+    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) }
+    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

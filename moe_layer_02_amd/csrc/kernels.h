@@ -50,12 +50,15 @@ struct GemmArgs {
     const float *a_scale;        // fp8: activation scale (device scalar)
     const float *b_scale;        // fp8: per-expert weight scales [E]
     uint32_t *amax_out;          // fp8 gate/up: |h| max as float bits (atomicMax), may be null
+    int group_m;                 // tile order: blocks per group (set by the launcher)
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
 
 struct TileInfo {
     int BM, BN, BK, WM, WN;      // tile rows, B rows per tile, K step, wave grid
+    int stages;                  // 0: register-staged double buffer; >= 2: direct-to-LDS stages
+    int mfma;                    // MFMA output tile edge: 16 or 32
 };
 
 // Compiled tiles per weight type (MOE_DT_*).  Returns the count; fills info when non-null.
@@ -64,6 +67,10 @@ bool gemm_tile_info(int wdtype, int tile, TileInfo *info);
 // Workgroups the launch uses (persistent grid) for a given upper bound of tiles.
 hipError_t launch_gemm(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
                        int64_t max_tiles, hipStream_t s);
+// the direct-to-LDS pipelined tiles (gemm_pipe.hip), numbered after the staged ones
+bool pipe_tile_info(int wdtype, int tile, TileInfo *info);
+hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
+                            int64_t max_tiles, hipStream_t s);
 
 struct ReduceArgs {
     const void *Y;               // bf16 [cap, H] or fp32 partials [split, cap, H]

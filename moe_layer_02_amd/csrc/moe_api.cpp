@@ -93,12 +93,15 @@ moe_status check_layer(const moe_layer *L) {
 moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileInfo *t2) {
     if (!p) return MOE_ERR_INVALID_ARGUMENT;
     const int wd = L->weight_dtype;
-    if (!gemm_tile_info(wd, p->gemm1_tile, t1) || !gemm_tile_info(wd, p->gemm2_tile, t2))
+    if (p->gemm1_tile < 0 || p->gemm2_tile < 0 || !gemm_tile_info(wd, p->gemm1_tile, t1) ||
+        !gemm_tile_info(wd, p->gemm2_tile, t2))
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->block_m != t1->BM || p->block_m != t2->BM) return MOE_ERR_INVALID_ARGUMENT;
     if (p->split_k < 1 || p->split_k > 16) return MOE_ERR_INVALID_ARGUMENT;
-    // GEMM1: K = H, output columns I (each tile covers BN/2 gate and BN/2 up rows)
+    // GEMM1: K = H, output columns I (each tile covers BN/2 gate and BN/2 up rows, and each
+    // wave an equal number of gate and up fragments)
     if (L->H % t1->BK || L->I % (t1->BN / 2)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((t1->BN / t1->WN) % (2 * t1->mfma)) return MOE_ERR_INVALID_ARGUMENT;
     // GEMM2: K = I split split_k ways, output columns H
     if (L->I % (t2->BK * p->split_k) || L->H % t2->BN) return MOE_ERR_INVALID_ARGUMENT;
     return MOE_OK;
@@ -360,50 +363,46 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     moe_status st = check_layer(layer);
     if (st != MOE_OK) return st;
     if (T < 0 || !plan) return MOE_ERR_INVALID_ARGUMENT;
-    const int wd = layer->weight_dtype;
-    const double rows_per_expert = (double)T * layer->route.top_k / layer->E;
-    // Candidate (block_m, gemm1 tile, gemm2 tile) by rows per expert; the first that tiles
-    // the layer's shape is taken, with split-K on GEMM2 while its tiles underfill the GPU.
-    struct Cand { int bm, g1, g2; };
-    Cand cands[8];
-    int nc = 0;
-    if (wd == MOE_DT_BF16) {
-        if (rows_per_expert <= 16) { cands[nc++] = {16, 0, 0}; cands[nc++] = {16, 1, 1}; }
-        if (rows_per_expert <= 48) cands[nc++] = {32, 2, 2};
-        if (rows_per_expert <= 160) cands[nc++] = {64, 3, 3};
-        cands[nc++] = {128, 4, 4};
-        cands[nc++] = {16, 1, 1};
-    } else if (wd == MOE_DT_FP8_E4M3) {
-        if (rows_per_expert <= 16) { cands[nc++] = {16, 0, 0}; cands[nc++] = {16, 0, 1}; cands[nc++] = {16, 1, 1}; }
-        if (rows_per_expert <= 48) cands[nc++] = {32, 2, 2};
-        if (rows_per_expert <= 160) cands[nc++] = {64, 3, 3};
-        cands[nc++] = {128, 4, 4};
-        cands[nc++] = {16, 1, 1};
-    } else {
-        if (rows_per_expert <= 16) cands[nc++] = {16, 0, 0};
-        if (rows_per_expert <= 48) cands[nc++] = {32, 1, 1};
-        if (rows_per_expert <= 160) cands[nc++] = {64, 2, 2};
-        cands[nc++] = {128, 3, 3};
-        cands[nc++] = {16, 0, 0};
-    }
-    for (int c = 0; c < nc; c++) {
-        moe_plan p{cands[c].bm, cands[c].g1, cands[c].g2, 1};
-        TileInfo t1, t2;
-        if (check_plan(layer, &p, &t1, &t2) != MOE_OK) continue;
-        // split GEMM2's K while its tiles (for the experts in use) underfill the GPU
-        const int64_t used = std::min<int64_t>((int64_t)T * layer->route.top_k, layer->E);
-        const int64_t blocks = std::max<int64_t>(used, (int64_t)T * layer->route.top_k / p.block_m);
-        int64_t tiles2 = blocks * (layer->H / t2.BN);
-        for (int sk = 2; sk <= 8; sk *= 2) {
-            if (tiles2 * p.split_k >= 512) break;
-            moe_plan q = p;
-            q.split_k = sk;
-            if (check_plan(layer, &q, &t1, &t2) == MOE_OK) p = q;
-            else break;
+    // Plans by rows per expert r = T*k/E, from timing every valid plan of the Mixtral,
+    // Qwen2, Llama-4-Scout and DeepSeek-V3 shapes on MI355X (each pick within ~10% of the
+    // fastest plan at every measured T).  Small r streams weights (16-row blocks, narrow
+    // tiles, pipelined direct-to-LDS loads); large r is MFMA work (256x256 tiles, 8 waves).
+    struct Row { double r_max; int bm, g1, g2, split; };
+    static const Row bf16[] = {{1, 16, 10, 10, 2},   {12, 16, 1, 9, 1},     {48, 64, 18, 11, 1},
+                               {96, 128, 22, 22, 2}, {192, 128, 22, 22, 1}, {1e30, 256, 20, 20, 2}};
+    static const Row fp8[] = {{1, 16, 9, 1, 1}, {8, 32, 2, 2, 1}, {64, 32, 11, 2, 1}, {256, 128, 5, 13, 1},
+                              {1e30, 256, 12, 12, 1}};
+    static const Row int4[] = {{2, 16, 0, 0, 1}, {1e30, 32, 1, 1, 1}};
+    const Row *rows = bf16;
+    int n = sizeof(bf16) / sizeof(Row);
+    if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }
+    if (layer->weight_dtype == MOE_DT_INT4_G128) { rows = int4; n = sizeof(int4) / sizeof(Row); }
+    const double r = (double)T * layer->route.top_k / layer->E;
+    TileInfo t1, t2;
+    int first = 0;
+    while (first < n - 1 && r > rows[first].r_max) first++;
+    // the row for r, else (shapes it does not tile) the nearest row that fits; fewer K
+    // splits when the split does not divide the reduction
+    for (int d = 0; d < 2 * n; d++) {
+        const int i = d % 2 == 0 ? first + d / 2 : first - (d + 1) / 2;
+        if (i < 0 || i >= n) continue;
+        for (int sk = rows[i].split; sk >= 1; sk /= 2) {
+            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk};
+            if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
+                *plan = p;
+                return MOE_OK;
+            }
         }
-        *plan = p;
-        return MOE_OK;
     }
+    // any valid plan (tiny or unusual shapes)
+    for (int bm : {16, 32, 64, 128, 256})
+        for (int g = 0; g < 32; g++) {
+            moe_plan p{bm, g, g, 1};
+            if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
+                *plan = p;
+                return MOE_OK;
+            }
+        }
     return MOE_ERR_UNSUPPORTED;
 }
 
@@ -442,9 +441,10 @@ moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *
     TileInfo t1, t2;
     if ((st = check_plan(layer, plan, &t1, &t2)) != MOE_OK) return st;
     std::snprintf(buf, len,
-                  "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d] gemm2=%d[BM%d BN%d BK%d waves%dx%d] split_k=%d",
-                  plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, plan->gemm2_tile, t2.BM,
-                  t2.BN, t2.BK, t2.WM, t2.WN, plan->split_k);
+                  "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d stages%d mfma%d] gemm2=%d[BM%d BN%d BK%d "
+                  "waves%dx%d stages%d mfma%d] split_k=%d",
+                  plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, t1.stages, t1.mfma,
+                  plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k);
     return MOE_OK;
 }
 

@@ -81,12 +81,12 @@ def workspace_view(layer, T, plan, ws, region, dtype, count):
 
 def valid_plans(layer, T):
     """Every (block_m, tile1, tile2, split) the library accepts for this layer."""
-    n = 8
+    n = 32
     out = []
     for g1 in range(n):
         for g2 in range(n):
             for sk in (1, 2, 4, 8):
-                for bm in (16, 32, 64, 128):
+                for bm in (16, 32, 64, 128, 256):
                     p = abi.Plan(bm, g1, g2, sk)
                     try:
                         abi.moe_workspace_bytes(layer.struct, T, p)

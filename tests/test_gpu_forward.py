@@ -136,6 +136,20 @@ def test_mixtral_mid_T_sampled():
     check_sampled("mixtral", 256, [0, 100, 255])
 
 
+def test_mixtral_every_large_tile_plan_sampled():
+    """Every plan with block_m >= 64 on the full-size Mixtral shard (the tile shapes the
+    large-T bench uses), against one oracle computation of sampled tokens."""
+    c = case("mixtral")
+    T, tokens = 512, [0, 211, 511]
+    ref, _, _ = c.oracle(T, tokens=tokens)
+    plans = [p for p in valid_plans(c.layer, T) if p.block_m >= 64]
+    assert len(plans) >= 10
+    for p in plans:
+        out, ws = c.gpu(T, p)
+        err = rel_l2(bf16_to_f64(out[tokens]), ref)
+        assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+
+
 @pytest.mark.parametrize("T", [1, 5])
 def test_scout_small_T(T):
     check_full("scout", T)
@@ -171,9 +185,11 @@ def test_qwen2_fp8_activation_codes_exact():
 
 
 def test_qwen2_fp8_intermediate_codes():
-    """The intermediate h is quantised from fp32 on both sides: its scale agrees to fp32
-    rounding and almost every code is identical (a code may differ by one step where the
-    two fp32 accumulation orders straddle a rounding midpoint)."""
+    """The intermediate h is quantised from fp32 on both sides.  Its amax comes from a
+    length-3584 dot product accumulated in fp32 (GPU) or fp64 (oracle); with cancellation
+    that relative error reaches ~n*eps = 2e-4, so the scales agree to that, and a code may
+    differ by one step where the two values straddle a rounding midpoint (expected ~1e-3 of
+    the codes; a wrong scale or row order would change most of them)."""
     c = case("qwen2")
     T = 16
     out, ws = c.gpu(T)
@@ -182,7 +198,7 @@ def test_qwen2_fp8_intermediate_codes():
     ids, _ = oracle_route(c.cfg, bits(lg), c.bias)
     _, ref_codes, ref_sc = oracle.fp8_intermediate(c.W, bits(x), ids)
     sc = workspace_view(c.layer, T, plan, ws, "scalars", torch.float32, 4).cpu().numpy()
-    assert abs(sc[3] / ref_sc[1] - 1) < 1e-5
+    assert abs(sc[3] / ref_sc[1] - 1) < 2e-4
     cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, plan.block_m)
     hq = workspace_view(c.layer, T, plan, ws, "h_q", torch.uint8, cap * c.cfg.I).cpu().numpy().reshape(cap, -1)
     inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, T * c.cfg.k).cpu().numpy()
@@ -191,7 +207,7 @@ def test_qwen2_fp8_intermediate_codes():
     diff = got != ref_codes
     frac = diff.mean()
     say("  h codes differing: %.2e" % frac)
-    assert frac < 2e-3
+    assert frac < 1e-2
     a, b = np.abs(val(got[diff])), np.abs(val(ref_codes[diff]))
     assert (np.abs(a - b) <= np.maximum(a, b) * 0.125 + 2.0 ** -9).all()     # one E4M3 step at most
 
