@@ -162,7 +162,8 @@ moe_status moe_route(const moe_route_cfg *cfg, int32_t T, const void *logits, co
                      int32_t *topk_ids, float *topk_weights, void *stream);
 
 /*
- * Align / permute (one workgroup; LDS histogram, prefix sum, stable scatter).  For the
+ * Align / permute (one workgroup; LDS histogram, prefix sum, stable scatter; moe_forward
+ * also has a chunked multi-workgroup form for large T*k with identical output).  For the
  * T*k pairs (flat index t*k + j) of topk_ids [device] int32 [T, k], each in [0, E):
  *  expert_counts [E]     number of pairs routed to each expert;
  *  sorted_token_ids [capacity]: expert e owns rows [off_e, off_e + P_e), P_e = c_e rounded
@@ -235,7 +236,9 @@ typedef enum {
     MOE_WS_H_Q = 10,          /* fp8: E4M3 [capacity, I] quantised h                 */
     MOE_WS_Y = 11,            /* bf16 [capacity, H] weighted expert rows, or with split_k > 1
                                  fp32 [split_k, capacity, H] partial sums             */
-    MOE_WS_COUNT = 12
+    MOE_WS_ALIGN_SCRATCH = 12, /* int32 per-chunk expert histograms of the chunked align
+                                  (T*k > 4096 only)                                   */
+    MOE_WS_COUNT = 13
 } moe_ws_region;
 
 /* Byte offset of each moe_ws_region in the workspace of moe_forward(layer, T, plan) into

@@ -21,7 +21,7 @@ DT_BF16, DT_FP32, DT_FP8_E4M3, DT_INT4_G128 = 0, 1, 2, 3
 STAGES = ("route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce")
 STAGE_COUNT = len(STAGES)
 WS_REGIONS = ("topk_ids", "topk_weights", "sorted_ids", "expert_ids", "num_post_pad", "expert_counts",
-              "inv_pos", "scalars", "x_q", "h", "h_q", "y")
+              "inv_pos", "scalars", "x_q", "h", "h_q", "y", "align_scratch")
 
 # every function include/moe.h declares (checked against the header by the tests)
 EXPORTS = ("moe_status_str", "moe_align_capacity", "moe_route", "moe_align", "moe_default_plan",

@@ -178,8 +178,12 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
         uint4 ra[C::A_IT], rb[C::B_IT];
         uint32_t rs[C::GROUPS][C::FN], rz[C::GROUPS][C::FN];
         uint32_t cs[C::GROUPS][C::FN], cz[C::GROUPS][C::FN];
+        // with rotate_k each tile walks its K range from its own starting step (see
+        // gemm_pipe.hip); the order is fixed per tile
+        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
         auto load_stage = [&](int kstep) {
-            const int koff = kstep * C::BK;
+            const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
+            const int koff = kr * C::BK;
 #pragma unroll
             for (int it = 0; it < C::A_IT; it++) {
                 const int ab = WT == WT_FP8 ? koff : koff * 2;

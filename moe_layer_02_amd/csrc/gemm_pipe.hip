@@ -155,9 +155,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 dst[q] = C::A_STAGE + (slab * C::BN + rb) * 128;
             }
         }
+        // with rotate_k (weight streaming: no two tiles share operands) each tile walks its K
+        // range from its own starting step, cyclically, so that concurrent tiles spread over
+        // DRAM channels instead of all reading the same column slice of rows that share
+        // address bits; tiles that share A or B rows keep K in step for L2 reuse.  The
+        // order is fixed per tile, so results stay reproducible.
+        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
         auto issue = [&](int kstep) {
             char *st = smem + (kstep % C::ST) * C::STAGE;
-            const int64_t koff = (int64_t)kstep * C::KS * 128;
+            const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
+            const int64_t koff = (int64_t)kr * C::KS * 128;
 #pragma unroll
             for (int q = 0; q < C::LPW; q++)
                 __builtin_amdgcn_global_load_lds((const void *)(src[q] + koff), (lds_ptr)(st + dst[q]), 16, 0, 0);
@@ -184,33 +191,45 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             block_barrier();
             if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
             const char *sa = smem + (kt % C::ST) * C::STAGE, *sb = sa + C::A_STAGE;
+            // Fragments of step k + 1 can be read while the MFMAs of step k run (see DB below).
+            if constexpr (WT == WT_BF16 && C::MS == 32) {
+                // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step.
+                // Double-buffered: the reads of step k + 1 are issued before the MFMAs of
+                // step k (scheduling barriers keep that order).
+                constexpr int NK = C::KS * 4;
+                bf16x8 af[2][C::FM], bfr[2][C::FN];
+                auto load = [&](int k, int buf) {
+                    const int sl = k / 4, ci = (k % 4) * 2 + (lane >> 5);
 #pragma unroll
-            for (int sl = 0; sl < C::KS; sl++) {
-                if constexpr (WT == WT_BF16 && C::MS == 32) {
-                    // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step
-#pragma unroll
-                    for (int kk = 0; kk < 4; kk++) {
-                        const int ci = kk * 2 + (lane >> 5);
-                        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-                        for (int fm = 0; fm < C::FM; fm++) {
-                            const int r = wm * C::TM + fm * 32 + (lane & 31);
-                            af[fm] = *(const bf16x8 *)(sa + (sl * C::BM + r) * 128 + ((ci ^ swz(r)) << 4));
-                        }
-#pragma unroll
-                        for (int fn = 0; fn < C::FN; fn++) {
-                            const int r = wn * C::TN + fn * 32 + (lane & 31);
-                            bfr[fn] = *(const bf16x8 *)(sb + (sl * C::BN + r) * 128 + ((ci ^ swz(r)) << 4));
-                        }
-#pragma unroll
-                        for (int fm = 0; fm < C::FM; fm++)
-#pragma unroll
-                            for (int fn = 0; fn < C::FN; fn++)
-                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+                    for (int fm = 0; fm < C::FM; fm++) {
+                        const int r = wm * C::TM + fm * 32 + (lane & 31);
+                        af[buf][fm] = *(const bf16x8 *)(sa + (sl * C::BM + r) * 128 + ((ci ^ swz(r)) << 4));
                     }
-                } else if constexpr (WT == WT_BF16) {
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const int r = wn * C::TN + fn * 32 + (lane & 31);
+                        bfr[buf][fn] = *(const bf16x8 *)(sb + (sl * C::BN + r) * 128 + ((ci ^ swz(r)) << 4));
+                    }
+                };
+                load(0, 0);
+#pragma unroll
+                for (int k = 0; k < NK; k++) {
+                    if (k + 1 < NK) load(k + 1, (k + 1) & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++)
+                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k & 1][fm], bfr[k & 1][fn],
+                                                                                 acc[fm][fn], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else if constexpr (WT == WT_BF16) {
+#pragma unroll
+                for (int sl = 0; sl < C::KS; sl++)
 #pragma unroll
                     for (int kk = 0; kk < 2; kk++) {
+                        // 16x16x32: lane l holds row l%16, K elements 8*(l/16) .. +7 of the step
                         const int ci = kk * 4 + (lane >> 4);
                         bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
@@ -229,16 +248,18 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                             for (int fn = 0; fn < C::FN; fn++)
                                 acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
                     }
-                } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
-                    const int c0 = 2 * (lane >> 4);
-                    i32x8 af[C::FM], bfr[C::FN];
+            } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
+                const int c0 = 2 * (lane >> 4);
+                i32x8 af[2][C::FM], bfr[2][C::FN];
+                auto load = [&](int sl, int buf) {
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++) {
                         const int r = wm * C::TM + fm * 16 + (lane & 15);
                         const char *row = sa + (sl * C::BM + r) * 128;
                         const uint4 lo = *(const uint4 *)(row + ((c0 ^ swz(r)) << 4));
                         const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ swz(r)) << 4));
-                        af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        af[buf][fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     }
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
@@ -246,14 +267,20 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         const char *row = sb + (sl * C::BN + r) * 128;
                         const uint4 lo = *(const uint4 *)(row + ((c0 ^ swz(r)) << 4));
                         const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ swz(r)) << 4));
-                        bfr[fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        bfr[buf][fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     }
+                };
+                load(0, 0);
+#pragma unroll
+                for (int sl = 0; sl < C::KS; sl++) {
+                    if (sl + 1 < C::KS) load(sl + 1, (sl + 1) & 1);
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++)
                             acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                af[fm], bfr[fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+                                af[sl & 1][fm], bfr[sl & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
                 }
             }
         }
@@ -315,7 +342,6 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
 // ---- tile tables (ids continue gemm.hip's per weight type) --------------------------------
 //        id  BM   BN  KS ST WM WN MS
 #define PIPE_BF16_TILES(X)              \
-    X(6, 256, 256, 1, 2, 2, 2, 16)      \
     X(7, 128, 256, 1, 3, 2, 2, 16)      \
     X(8, 128, 128, 1, 4, 2, 2, 16)      \
     X(9, 16, 128, 2, 4, 1, 4, 16)       \
@@ -326,22 +352,24 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     X(14, 128, 128, 1, 4, 2, 2, 32)     \
     X(15, 64, 128, 1, 4, 2, 2, 32)      \
     X(16, 256, 128, 1, 3, 2, 2, 32)     \
-    X(17, 256, 256, 1, 2, 2, 2, 32)     \
     X(18, 64, 256, 1, 4, 1, 4, 32)      \
     X(19, 32, 256, 1, 4, 1, 4, 32)      \
     X(20, 256, 256, 1, 2, 2, 4, 16)     \
     X(21, 256, 256, 1, 2, 2, 4, 32)     \
     X(22, 128, 256, 1, 3, 2, 4, 16)     \
-    X(23, 256, 128, 1, 3, 4, 2, 16)
+    X(23, 256, 128, 1, 3, 4, 2, 16)     \
+    X(24, 256, 256, 1, 2, 4, 4, 32)     \
+    X(25, 256, 256, 1, 2, 4, 4, 16)     \
+    X(26, 128, 256, 1, 3, 4, 4, 32)
 #define PIPE_FP8_TILES(X)               \
-    X(6, 256, 256, 1, 2, 2, 2, 16)      \
     X(7, 128, 256, 1, 3, 2, 2, 16)      \
     X(8, 128, 128, 1, 4, 2, 2, 16)      \
     X(9, 16, 128, 2, 4, 1, 4, 16)       \
     X(10, 64, 128, 1, 4, 2, 2, 16)      \
     X(11, 32, 128, 2, 3, 1, 4, 16)      \
     X(12, 256, 256, 1, 2, 2, 4, 16)     \
-    X(13, 128, 256, 1, 3, 2, 4, 16)
+    X(13, 128, 256, 1, 3, 2, 4, 16)     \
+    X(14, 256, 256, 1, 2, 4, 4, 16)
 
 template <class C, int WT, int KIND, bool PARTIAL>
 hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {

@@ -26,7 +26,10 @@ struct AlignArgs {
     const int32_t *ids;
     int32_t *sorted, *eids, *npp, *counts, *inv_pos;
 };
-hipError_t launch_align(const AlignArgs &a, hipStream_t s);
+// scratch: align_scratch_bytes() of device memory for the chunked path (large T*k), or
+// null to always use the one-workgroup kernel
+int64_t align_scratch_bytes(int64_t pairs, int E);
+hipError_t launch_align(const AlignArgs &a, int32_t *scratch, hipStream_t s);
 
 // One grouped GEMM over the align layout.  Rows of the M dimension are the sorted rows;
 // block b (block_m rows) multiplies by the weights of expert expert_ids[b].
@@ -51,6 +54,7 @@ struct GemmArgs {
     const float *b_scale;        // fp8: per-expert weight scales [E]
     uint32_t *amax_out;          // fp8 gate/up: |h| max as float bits (atomicMax), may be null
     int group_m;                 // tile order: blocks per group (set by the launcher)
+    int rotate_k;                // 1: each tile starts its K walk at its own offset
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };

@@ -108,7 +108,7 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
 }
 
 struct Workspace {
-    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, total;
+    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, total;
     int64_t cap;
 };
 
@@ -139,6 +139,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.h = take((size_t)w.cap * L->I * (fp8 ? 4 : 2));
     w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
     w.y = take(p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
+    w.align_scratch = take((size_t)align_scratch_bytes(pairs, E));
     w.total = o;
     return w;
 }
@@ -214,7 +215,8 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     // 2. align
     if ((err = mark(MOE_STAGE_ALIGN)) != hipSuccess) return MOE_ERR_HIP;
     AlignArgs aa{T, k, E, plan.block_m, nbits_for(E), w.cap, ids, sorted, eids, npp, counts, inv_pos};
-    if ((err = launch_align(aa, stream)) != hipSuccess) return fail(err);
+    int32_t *align_scratch = align_scratch_bytes(pairs, E) ? (int32_t *)(ws + w.align_scratch) : nullptr;
+    if ((err = launch_align(aa, align_scratch, stream)) != hipSuccess) return fail(err);
 
     // 3. fp8: quantise the hidden states with one dynamic scale
     const void *a1 = hidden;
@@ -257,6 +259,9 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     g.a_scale = (const float *)&scal[2];
     g.b_scale = L->w13_scale;
     g.amax_out = fp8 ? &scal[1] : nullptr;
+    // weight streaming (about one block of rows per expert): no two tiles share operands,
+    // so stagger their K walks across DRAM channels
+    g.rotate_k = (int64_t)pairs <= (int64_t)E * plan.block_m;
     const int64_t mblocks_max = w.cap / plan.block_m;
     if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, false, g,
                            mblocks_max * (I / (t1.BN / 2)), stream)) != hipSuccess)
@@ -356,7 +361,7 @@ moe_status moe_align(int32_t T, int32_t k, int32_t E, int32_t block_m, const int
         if (!p || !aligned(p, 4)) return MOE_ERR_INVALID_ARGUMENT;
     AlignArgs a{T, k, E, block_m, nbits_for(E), moe_align_capacity(T, k, E, block_m), topk_ids, sorted_token_ids,
                 expert_ids, num_tokens_post_padded, expert_counts, inv_pos};
-    return launch_align(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return launch_align(a, nullptr, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
@@ -459,7 +464,7 @@ moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_pl
     if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
     const Workspace w = layout(layer, T, &p);
     const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos,
-                                    w.scal, w.xq, w.h, w.hq, w.y};
+                                    w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch};
     for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
     return MOE_OK;
 }

@@ -28,7 +28,12 @@ __global__ __launch_bounds__(256) void k_absmax(AbsmaxArgs a) {
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    if (lane_id() == 0) atomicMax(a.amax, __float_as_uint(m));
+    // one atomic per workgroup: same-address atomics serialise in L2
+    __shared__ float wmax[4];
+    if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(a.amax, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 __device__ __forceinline__ void scales_from_amax(uint32_t bits, float *scale, float *inv) {

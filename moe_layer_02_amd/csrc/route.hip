@@ -95,8 +95,55 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
         z = wave_sum(part);
     }
 
-    if (a.kind == GROUPED) {
-        // group score = sum of the group's two largest keys; lane g keeps group g's score
+    if (a.kind == GROUPED && (E / a.n_group) <= kWave && ((E / a.n_group) & (E / a.n_group - 1)) == 0) {
+        // Groups of G = 2^s <= 64 consecutive experts lie inside one slot on G consecutive
+        // lanes, so every group's two largest keys come from segmented butterflies (xor
+        // offsets < G) over all slots at once.
+        const int G = E / a.n_group;
+        float score[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+            const int e = lane + kWave * i;
+            float k1 = live[i] ? key[i] : -INFINITY;
+            int i1 = live[i] ? e : INT32_MAX;
+            for (int off = G >> 1; off >= 1; off >>= 1) {
+                const float ok = __shfl_xor(k1, off, kWave);
+                const int oi = __shfl_xor(i1, off, kWave);
+                if (ranks_before(ok, oi, k1, i1)) { k1 = ok; i1 = oi; }
+            }
+            float k2 = (live[i] && e != i1) ? key[i] : -INFINITY;
+            int i2 = (live[i] && e != i1) ? e : INT32_MAX;
+            for (int off = G >> 1; off >= 1; off >>= 1) {
+                const float ok = __shfl_xor(k2, off, kWave);
+                const int oi = __shfl_xor(i2, off, kWave);
+                if (ranks_before(ok, oi, k2, i2)) { k2 = ok; i2 = oi; }
+            }
+            score[i] = G >= 2 ? k1 + k2 : k1;
+        }
+        // keep the topk_group best groups; the first lane of each segment stands for its group
+        uint64_t kept = 0;
+        for (int q = 0; q < a.topk_group; q++) {
+            float gk = -INFINITY, gv = 0.0f;
+            int gi = INT32_MAX;
+#pragma unroll
+            for (int i = 0; i < EPL; i++) {
+                const int e = lane + kWave * i, g = e / G;
+                if (e < E && (lane % G) == 0 && !((kept >> g) & 1ull) && ranks_before(score[i], g, gk, gi)) {
+                    gk = score[i];
+                    gi = g;
+                }
+            }
+            wave_argmax(gk, gi, gv);
+            kept |= 1ull << gi;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+            const int e = lane + kWave * i;
+            if (live[i] && !((kept >> (e / G)) & 1ull)) live[i] = false;
+        }
+    } else if (a.kind == GROUPED) {
+        // general group size: group score = sum of the group's two largest keys, from two
+        // wave-wide arg-max rounds per group; lane g keeps group g's score
         const int G = E / a.n_group;
         float my_score = -INFINITY;
         for (int g = 0; g < a.n_group; g++) {

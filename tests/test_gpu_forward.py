@@ -161,6 +161,15 @@ def test_scout_largest_T_sampled():
 
 # ---- fp8 w8a8 --------------------------------------------------------------------------
 
+def test_qwen2_largest_T_route_and_align():
+    """T*k = 32768 pairs: the forward's chunked multi-workgroup align must lay rows out
+    exactly as the oracle's stable sort does."""
+    c = case("qwen2")
+    out, ws = c.gpu(4096)
+    assert torch.isfinite(out.float()).all()
+    check_intermediates(c, 4096, None, ws)
+
+
 @pytest.mark.parametrize("T", [1, 8, 24])
 def test_qwen2_fp8(T):
     check_full("qwen2", T)

@@ -44,7 +44,8 @@ def test_route_on_config_logits(name):
 
 @pytest.mark.parametrize("E,k,kind,ng,tg", [(8, 2, 0, 1, 1), (64, 8, 0, 1, 1), (256, 8, 0, 1, 1),
                                             (16, 1, 1, 1, 1), (64, 6, 1, 1, 1), (256, 8, 2, 8, 4),
-                                            (128, 6, 2, 16, 3), (32, 4, 2, 32, 32), (256, 64, 2, 4, 4)])
+                                            (128, 6, 2, 16, 3), (32, 4, 2, 32, 32), (256, 64, 2, 4, 4),
+                                            (48, 4, 2, 4, 3), (96, 5, 2, 4, 2), (200, 8, 2, 8, 4)])
 def test_route_forced_ties(E, k, kind, ng, tg):
     cfg = synth.CONFIGS["tiny"].with_shape(name="ties", E=E, k=k, route_kind=kind, n_group=ng, topk_group=tg,
                                             renormalize=True, routed_scaling=1.5)
