@@ -169,7 +169,8 @@ def kernel_roofline(cfg, m):
                 algorithmic_flops=flops, algorithmic_bytes=nbytes)
 
 
-KERNEL_SOURCES = ("moe_layer_02_amd/csrc/gemm.hip", "moe_layer_02_amd/csrc/common.h", "moe_layer_02_amd/csrc/kernels.h")
+KERNEL_SOURCES = tuple("moe_layer_02_amd/csrc/" + f for f in
+                       ("gemm.hip", "gemm_pipe.hip", "gemm_i4.hip", "pipe.h", "common.h", "kernels.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -52,24 +52,6 @@ struct Cfg {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// bf16 x8 -> fp16 x8, reordered (0,4,1,5,2,6,3,7) to match the int4 dequant order below.
-__device__ __forceinline__ uint4 bf16x8_to_f16x8_perm(uint4 v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    _Float16 h[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        h[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
-        h[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
-    }
-    const _Float16 p[8] = {h[0], h[4], h[1], h[5], h[2], h[6], h[3], h[7]};
-    uint4 r;
-    r.x = (uint32_t)__builtin_bit_cast(uint16_t, p[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[1]) << 16);
-    r.y = (uint32_t)__builtin_bit_cast(uint16_t, p[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[3]) << 16);
-    r.z = (uint32_t)__builtin_bit_cast(uint16_t, p[4]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[5]) << 16);
-    r.w = (uint32_t)__builtin_bit_cast(uint16_t, p[6]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[7]) << 16);
-    return r;
-}
-
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // 8 nibbles (k = 0..7 of one row, byte b = k/2, low nibble first) -> fp16 (q - z) * s in

@@ -1,0 +1,335 @@
+// gemm_i4.hip -- the grouped GEMMs for int4 group-128 weights, direct-to-LDS pipelined.
+//
+// The w4a16 kernel of vLLM PR #12185 ("[Kernel] add triton fused moe kernel for gptq/awq":
+// one launch for every expert, GPTQ/AWQ packing, dequantisation inside the GEMM), laid out
+// for gfx950.  Weights stay packed all the way into LDS: a stage holds one 128-byte slab of
+// every B row (256 K values, two quantisation groups), the rows' two fp16 scales and two
+// fp16 zero points, and the matching 256 K values of every A row in fp16 -- all moved by
+// global_load_lds (16 bytes per lane for the slabs, 4 for the scales and zeros), ST stages
+// in flight, as in gemm_pipe.hip.
+//
+// Dequantisation is split between the VALU and the MFMA's fp32 accumulation.  OR-ing a
+// nibble into the low bits of fp16 1024.0 (0x6400) gives exactly 1024 + q; two nibbles are
+// taken per 32-bit operation (nibbles i and i + 4 of a word land in the two halves of a
+// packed fp16 pair), so a word of 8 consecutive K values costs 7 VALU operations and comes
+// out in the order (0,4,1,5,2,6,3,7).  The MFMAs of one quantisation group accumulate
+// D = sum a (1024 + q) and, against a fragment of ones, R = sum a; the group then adds
+// s D - s (1024 + z) R = s sum a (q - z) to the output in fp32 -- the exact dequantised
+// product up to fp32 rounding of terms 1024 times larger than the weights (relative error
+// of order 1e-4 for rows of activations with a large mean, far less for centred ones).
+// The activations are stored in the nibble order inside every group of 8 (the fp16
+// conversion pass permutes the hidden states; GEMM1 writes h permuted), so A and B agree
+// element for element and the dot products are unchanged.
+//
+// K assignment per MFMA (v_mfma_f32_16x16x32_f16, lane group g = lane / 16): in step
+// (half, d), half = 0..1 the group of the slab and d = 0..3, lane group g takes the K
+// values 128 half + 32 g + 8 d .. +7 -- dword d of 16-byte chunk g + 4 half of its B row,
+// and 16-byte chunk 4 (g & 1) + d of fp16 A slab 2 half + g / 2.  Each B row is therefore
+// read with two 16-byte LDS reads per stage, and each A row with one per MFMA.
+#include "common.h"
+#include "kernels.h"
+#include "pipe.h"
+
+namespace moe {
+namespace {
+
+template <int BM_, int BN_, int ST_, int WM_, int WN_>
+struct ICfg {
+    static constexpr int BM = BM_, BN = BN_, ST = ST_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = NW * kWave;
+    static constexpr int BK = 256;                             // K per stage: one packed slab
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+    static constexpr int A_SLABS = 4;                          // 4 x 64 fp16 per A row
+    static constexpr int A_STAGE = A_SLABS * BM * 128, B_STAGE = BN * 128, SZ = BN * 4;
+    static constexpr int STAGE = A_STAGE + B_STAGE + 2 * SZ;
+    static constexpr int A_LOADS = A_SLABS * BM / 8, B_LOADS = BN / 8, SZ_LOADS = 2 * BN / 64;
+    static constexpr int LOADS = A_LOADS + B_LOADS + SZ_LOADS;
+    static constexpr int LPW = LOADS / NW;
+    static_assert(LOADS % NW == 0, "stage loads must split evenly over the waves");
+    static_assert(BN % 64 == 0 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile / wave grid mismatch");
+    static_assert((ST - 2) * LPW <= 63, "vmcnt range");
+    static constexpr bool SKIP_FILLER = BM <= 32;   // as in gemm_pipe.hip
+};
+
+// 8 nibbles (K values 0..7 of one row, low nibble first in each byte) -> fp16 1024 + q in
+// the order (0,4,1,5,2,6,3,7)
+__device__ __forceinline__ f16x8 raw8(uint32_t w) {
+    uint4 r;
+    r.x = (w & 0x000F000Fu) | 0x64006400u;
+    r.y = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
+    r.z = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
+    r.w = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
+    return __builtin_bit_cast(f16x8, r);
+}
+
+__device__ __forceinline__ _Float16 half_of(uint32_t w, int hi) {
+    return __builtin_bit_cast(_Float16, (uint16_t)(hi ? w >> 16 : w & 0xFFFFu));
+}
+
+// column c of h is stored at this position (the (0,4,1,5,2,6,3,7) order inside each 8)
+__device__ __forceinline__ int perm_col(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
+
+enum { LD_A = 0, LD_B = 1, LD_SZ = 2 };
+
+template <class C, int KIND, bool PARTIAL>
+__global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int npp = *a.npp;
+    const int mblocks = npp / C::BM;
+    const int n_out = KIND == GEMM_GATE_UP ? C::BN / 2 : C::BN;
+    const int ntiles = a.N / n_out;
+    const int mn = mblocks * ntiles;
+    const int total = mn * a.split;
+    const int G = gridDim.x;
+    const int nk = a.ksplit / C::BK;
+    const int groups_per_row = a.K / 128;
+
+    for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
+        const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
+        const int s = tc.s, mb = tc.mb, nt = tc.nt;
+        const int e = a.eids[mb];
+        const int row0 = mb * C::BM;
+
+        // B row (of the expert's matrix) that tile row rr of the B slab holds
+        auto b_row = [&](int rr) -> int64_t {
+            if (KIND == GEMM_GATE_UP) {   // rows of wave column w: its gate half, then its up half
+                const int wcol = rr / C::TN, i = rr % C::TN, half = C::TN / 2;
+                const int col = nt * (C::BN / 2) + wcol * half + (i % half);
+                return i < half ? col : a.I + col;
+            }
+            return (int64_t)nt * C::BN + rr;
+        };
+
+        // per load instruction q of this wave: kind, the lane's global source at the split's
+        // first K, the bytes it advances per K step, and the wave's LDS offset in a stage
+        const char *src[C::LPW];
+        int dst[C::LPW], kind[C::LPW], step[C::LPW];
+        bool on[C::LPW];   // lane loads (filler rows of A are skipped, as in gemm_pipe.hip)
+#pragma unroll
+        for (int q = 0; q < C::LPW; q++) {
+            on[q] = true;
+            const int ins = wave + q * C::NW;
+            if (ins < C::A_LOADS) {
+                const int slab = ins / (C::BM / 8), rb = ins % (C::BM / 8) * 8;
+                const int r = rb + (lane >> 3);
+                const int chunk = (lane & 7) ^ swz(r);
+                const int p = a.sorted[row0 + r];
+                const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + r;
+                on[q] = !C::SKIP_FILLER || p < a.pairs || (lane >> 3) == 0;
+                src[q] = (const char *)a.A + (arow * a.lda + (int64_t)s * a.ksplit) * 2 + slab * 128 + chunk * 16;
+                dst[q] = (slab * C::BM + rb) * 128;
+                kind[q] = LD_A;
+                step[q] = C::A_SLABS * 128;
+            } else if (ins < C::A_LOADS + C::B_LOADS) {
+                const int rb = (ins - C::A_LOADS) * 8;
+                const int rr = rb + (lane >> 3);
+                const int chunk = (lane & 7) ^ swz(rr);
+                src[q] = (const char *)a.B + (int64_t)e * a.b_expert_stride + b_row(rr) * a.ldb +
+                         (int64_t)s * a.ksplit / 2 + chunk * 16;
+                dst[q] = C::A_STAGE + rb * 128;
+                kind[q] = LD_B;
+                step[q] = 128;
+            } else {   // 64 rows' scale (or zero) pairs: 4 bytes per lane
+                const int j = ins - C::A_LOADS - C::B_LOADS;
+                const int which = j / (C::BN / 64), r0 = j % (C::BN / 64) * 64;
+                const uint16_t *base = which ? a.bz : a.bs;
+                src[q] = (const char *)(base + (int64_t)e * a.sz_expert_stride + b_row(r0 + lane) * groups_per_row +
+                                        (int64_t)s * a.ksplit / 128);
+                dst[q] = C::A_STAGE + C::B_STAGE + which * C::SZ + r0 * 4;
+                kind[q] = LD_SZ;
+                step[q] = 4;
+            }
+        }
+        // weight streaming: each tile starts its K walk at its own step (see gemm_pipe.hip)
+        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
+        auto issue = [&](int kstep) {
+            const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
+            const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
+#pragma unroll
+            for (int q = 0; q < C::LPW; q++) {
+                const char *g = src[q] + (int64_t)kr * step[q];
+                if (kind[q] == LD_SZ)
+                    lds_dma<4>(g, st + dst[q]);
+                else if (on[q])
+                    lds_dma<16>(g, st + dst[q]);
+            }
+        };
+
+        f32x4 acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; i++)
+#pragma unroll
+            for (int j = 0; j < C::FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        block_barrier();   // every wave is done with the previous tile's buffers
+#pragma unroll
+        for (int p = 0; p < C::ST - 1; p++)
+            if (p < nk) issue(p);
+
+        const int g = lane >> 4;
+        for (int kt = 0; kt < nk; kt++) {
+            wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nk - 1 - kt));
+            block_barrier();
+            if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
+            const char *sa = smem + (kt % C::ST) * C::STAGE;
+            const char *sb = sa + C::A_STAGE, *ss = sb + C::B_STAGE, *sz = ss + C::SZ;
+
+            uint4 braw[2][C::FN];
+            uint32_t sw[C::FN], zw[C::FN];
+#pragma unroll
+            for (int fn = 0; fn < C::FN; fn++) {
+                const int r = wn * C::TN + fn * 16 + (lane & 15);
+                braw[0][fn] = *(const uint4 *)(sb + r * 128 + ((g ^ swz(r)) << 4));
+                braw[1][fn] = *(const uint4 *)(sb + r * 128 + (((g + 4) ^ swz(r)) << 4));
+                sw[fn] = *(const uint32_t *)(ss + r * 4);
+                zw[fn] = *(const uint32_t *)(sz + r * 4);
+            }
+            const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+                f32x4 dg[C::FM][C::FN], rs[C::FM];
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    f16x8 bq[C::FN];
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const uint4 v = braw[half][fn];
+                        bq[fn] = raw8(d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w);
+                    }
+                    const int slab = 2 * half + (g >> 1), chunk = 4 * (g & 1) + d;
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; fm++) {
+                        const int r = wm * C::TM + fm * 16 + (lane & 15);
+                        const f16x8 af = *(const f16x8 *)(sa + (slab * C::BM + r) * 128 + ((chunk ^ swz(r)) << 4));
+                        rs[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, ones, d ? rs[fm] : zero, 0, 0, 0);
+#pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++)
+                            dg[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bq[fn], d ? dg[fm][fn] : zero, 0, 0, 0);
+                    }
+                }
+                // the group's scale and zero point: acc += s D - s (1024 + z) R
+#pragma unroll
+                for (int fn = 0; fn < C::FN; fn++) {
+                    const float sv = (float)half_of(sw[fn], half);
+                    const float zv = sv * (1024.0f + (float)half_of(zw[fn], half));
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            acc[fm][fn][i] = __builtin_fmaf(-zv, rs[fm][i], __builtin_fmaf(sv, dg[fm][fn][i], acc[fm][fn][i]));
+                }
+            }
+        }
+
+        // ---- epilogue: accumulator value i of fragment (fm, fn) is row frag_row(lane, i),
+        //      column lane % 16 of that fragment ----
+        const int lcol = lane & 15;
+        if constexpr (KIND == GEMM_GATE_UP) {
+            // h = SiLU(gate) * up in fp16, columns in the permuted order GEMM2's A expects
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int row = row0 + wm * C::TM + fm * 16 + frag_row<16>(lane, i);
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const float hv = silu(acc[fm][f][i]) * acc[fm][f + C::FN / 2][i];
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + lcol;
+                        ((_Float16 *)a.C)[(int64_t)row * a.ldc + perm_col(col)] = (_Float16)hv;
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int row = row0 + wm * C::TM + fm * 16 + frag_row<16>(lane, i);
+                    const int p = a.sorted[row];
+                    if (p >= a.pairs) continue;   // filler row: never read back
+                    const float w = a.topk_w[p];
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const int col = nt * C::BN + wn * C::TN + fn * 16 + lcol;
+                        const float v = acc[fm][fn][i] * w;
+                        if constexpr (PARTIAL)
+                            ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
+                        else
+                            ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(v);
+                    }
+                }
+        }
+    }
+}
+
+// ---- tile table (ids continue gemm.hip's register-staged int4 tiles) ----------------------
+//        id  BM   BN  ST WM WN
+#define I4_TILES(X)             \
+    X(4, 16, 128, 4, 1, 4)      \
+    X(5, 16, 256, 3, 1, 4)      \
+    X(6, 32, 128, 4, 1, 4)      \
+    X(7, 64, 128, 3, 2, 2)      \
+    X(8, 16, 64, 4, 1, 2)       \
+    X(9, 32, 256, 3, 1, 4)      \
+    X(10, 16, 128, 3, 1, 4)     \
+    X(11, 16, 256, 3, 1, 8)     \
+    X(12, 32, 256, 3, 1, 8)     \
+    X(13, 32, 128, 2, 1, 4)     \
+    X(14, 64, 256, 2, 1, 8)
+
+template <class C, int KIND, bool PARTIAL>
+hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
+    static int occ_cache[64] = {0};   // per device; benign race (same value computed)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int occ = dev < 64 ? __atomic_load_n(&occ_cache[dev], __ATOMIC_RELAXED) : 0;
+    if (occ == 0) {
+        hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemm_i4<C, KIND, PARTIAL>, C::NT, 0);
+        if (err != hipSuccess) return err;
+        if (occ < 1) occ = 1;
+        if (dev < 64) __atomic_store_n(&occ_cache[dev], occ, __ATOMIC_RELAXED);
+    }
+    int64_t grid = (int64_t)device_cu_count() * occ;
+    if (max_tiles < grid) grid = max_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid < 1) grid = 1;
+    GemmArgs b = a;
+    b.group_m = 1;
+    while (b.group_m * b.group_m * 4 <= grid / 8 && b.group_m < 16) b.group_m *= 2;
+    hipLaunchKernelGGL((k_gemm_i4<C, KIND, PARTIAL>), dim3((unsigned)grid), dim3(C::NT), 0, s, b);
+    return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_kind(GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
+    if (kind == GEMM_GATE_UP) return launch_one<C, GEMM_GATE_UP, false>(a, max_tiles, s);
+    if (partial) return launch_one<C, GEMM_DOWN, true>(a, max_tiles, s);
+    return launch_one<C, GEMM_DOWN, false>(a, max_tiles, s);
+}
+
+}  // namespace
+
+bool i4_tile_info(int tile, TileInfo *info) {
+#define I4INFO(id, bm, bn, st, wm, wn)                     \
+    if (tile == id) {                                      \
+        *info = TileInfo{bm, bn, 256, wm, wn, st, 16};     \
+        return true;                                       \
+    }
+    I4_TILES(I4INFO)
+#undef I4INFO
+    return false;
+}
+
+hipError_t launch_gemm_i4(int tile, GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles,
+                          hipStream_t s) {
+#define I4LAUNCH(id, bm, bn, st, wm, wn) \
+    if (tile == id) return launch_kind<ICfg<bm, bn, st, wm, wn>>(kind, partial, a, max_tiles, s);
+    I4_TILES(I4LAUNCH)
+#undef I4LAUNCH
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

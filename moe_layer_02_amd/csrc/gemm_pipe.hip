@@ -1,4 +1,5 @@
-// gemm_pipe.hip -- the grouped GEMMs with a multi-stage direct-to-LDS pipeline (bf16, fp8).
+// gemm_pipe.hip -- the grouped GEMMs with a multi-stage direct-to-LDS pipeline (bf16, fp8;
+// int4 in gemm_i4.hip).
 //
 // Same tiles, tile order and epilogues as gemm.hip, but the operands never pass through
 // VGPRs: gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from HBM/L2 straight into
@@ -21,13 +22,12 @@
 // load at each step.
 #include "common.h"
 #include "kernels.h"
+#include "pipe.h"
 
 namespace moe {
 namespace {
 
-enum { WT_BF16 = 0, WT_FP8 = 2 };
-
-typedef __attribute__((address_space(3))) void *lds_ptr;
+enum { WT_BF16 = 0, WT_FP8 = 2, WT_INT4 = 3 };
 
 template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_>
 struct PCfg {
@@ -44,49 +44,10 @@ struct PCfg {
     static_assert(BM % (MS * WM) == 0 && BN % (MS * WN) == 0 && BM % 8 == 0, "tile / wave grid mismatch");
     static_assert(MS == 16 || (MS == 32 && WT == WT_BF16), "32x32 MFMA tiles are bf16 only");
     static_assert((ST - 2) * LPW <= 63, "vmcnt range");
+    // skip loading A's filler rows: worth it where a block is mostly padding (small blocks,
+    // small T); large tiles keep the registers the per-load flags would take
+    static constexpr bool SKIP_FILLER = BM <= 32;
 };
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// wait until at most n (a multiple of LPW, n <= (ST-2)*LPW) of this wave's loads are pending
-template <int LPW, int MAXS>
-__device__ __forceinline__ void wait_stages(int later) {
-    if constexpr (MAXS >= 3) {
-        if (later >= 3) { wait_vmcnt<3 * LPW>(); return; }
-    }
-    if constexpr (MAXS >= 2) {
-        if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
-    }
-    if constexpr (MAXS >= 1) {
-        if (later >= 1) { wait_vmcnt<LPW>(); return; }
-    }
-    wait_vmcnt<0>();
-}
-
-__device__ __forceinline__ void block_barrier() {
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
-// LDS position of 16-byte chunk c of tile row r (see the file comment)
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-template <int MS> struct AccOf { typedef f32x4 type; };
-template <> struct AccOf<32> { typedef f32x16 type; };
-
-// Row of a 16x16 (32x32) MFMA output fragment held in accumulator value r of this lane;
-// its column is lane % 16 (lane % 32).
-template <int MS>
-__device__ __forceinline__ int frag_row(int lane, int r) {
-    if constexpr (MS == 32) return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    return 4 * (lane >> 4) + r;
-}
 
 template <class C, int WT, int KIND, bool PARTIAL>
 __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
@@ -101,18 +62,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     const int mn = mblocks * ntiles;
     const int total = mn * a.split;
     const int G = gridDim.x;
-    const int j0 = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int nk = a.ksplit / C::BK;
     const int ebytes = WT == WT_FP8 ? 1 : 2;                  // A and B element bytes
 
-    for (int tile = j0; tile < total; tile += G) {
-        const int s = tile / mn;
-        const int rest = tile - s * mn;
-        const int gm0 = rest / (a.group_m * ntiles) * a.group_m;
-        const int gsz = min(a.group_m, mblocks - gm0);
-        const int local = rest - gm0 * ntiles;
-        const int mb = gm0 + local % gsz;
-        const int nt = local / gsz;
+    for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
+        const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
+        const int s = tc.s, mb = tc.mb, nt = tc.nt;
         const int e = a.eids[mb];
         const int row0 = mb * C::BM;
         const int64_t kb = (int64_t)s * a.ksplit * ebytes;     // byte offset of this split's K
@@ -121,21 +76,22 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         // split) and the wave's LDS destination offset inside a stage
         const char *src[C::LPW];
         int dst[C::LPW];
+        bool on[C::LPW];   // lane loads (filler rows of A are skipped, see below)
 #pragma unroll
         for (int q = 0; q < C::LPW; q++) {
+            on[q] = true;
             const int ins = wave + q * C::NW;
             const int r_in = lane >> 3;
             if (ins < C::A_LOADS) {
                 const int slab = ins / (C::BM / 8), rb = ins % (C::BM / 8) * 8;
                 const int r = rb + r_in;
                 const int chunk = (lane & 7) ^ swz(r);
-                int64_t arow;
-                if (KIND == GEMM_GATE_UP) {
-                    const int p = a.sorted[row0 + r];
-                    arow = p < a.pairs ? p / a.top_k : 0;     // filler rows read token 0 (never used)
-                } else {
-                    arow = row0 + r;
-                }
+                const int p = a.sorted[row0 + r];
+                const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + r;
+                // a filler row's products are never read back, so its LDS row may keep stale
+                // data; the lanes of the instruction's first row always load, so every load
+                // instruction runs with a non-empty mask and counts in vmcnt
+                on[q] = !C::SKIP_FILLER || p < a.pairs || (lane >> 3) == 0;
                 src[q] = (const char *)a.A + arow * a.lda * ebytes + kb + slab * 128 + chunk * 16;
                 dst[q] = (slab * C::BM + rb) * 128;
             } else {
@@ -162,12 +118,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         // order is fixed per tile, so results stay reproducible.
         const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
         auto issue = [&](int kstep) {
-            char *st = smem + (kstep % C::ST) * C::STAGE;
+            const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
             const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
             const int64_t koff = (int64_t)kr * C::KS * 128;
 #pragma unroll
             for (int q = 0; q < C::LPW; q++)
-                __builtin_amdgcn_global_load_lds((const void *)(src[q] + koff), (lds_ptr)(st + dst[q]), 16, 0, 0);
+                if (on[q])
+                    lds_dma<16>(src[q] + koff, st + dst[q]);
         };
 
         using Acc = typename AccOf<C::MS>::type;
@@ -414,6 +371,7 @@ bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
 #define PI_FP8(id, bm, bn, ks, st, wm, wn, ms) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms)
     if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) }
     if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) }
+    if (wdtype == WT_INT4) return i4_tile_info(tile, info);
     return false;
 }
 
@@ -425,6 +383,7 @@ hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, c
 #define PL_FP8(id, bm, bn, ks, st, wm, wn, ms) PLAUNCH(WT_FP8, id, bm, bn, ks, st, wm, wn, ms)
     if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) }
     if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) }
+    if (wdtype == WT_INT4) return launch_gemm_i4(tile, kind, partial, a, max_tiles, s);
     return hipErrorInvalidValue;
 }
 

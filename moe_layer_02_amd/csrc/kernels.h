@@ -75,6 +75,11 @@ hipError_t launch_gemm(int wdtype, int tile, GemmKind kind, bool partial, const 
 bool pipe_tile_info(int wdtype, int tile, TileInfo *info);
 hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
                             int64_t max_tiles, hipStream_t s);
+// int4 tiles of the pipelined kind (gemm_i4.hip): A is fp16 in the (0,4,1,5,2,6,3,7) order
+// inside every 8 columns (launch_f16_perm), and GEMM1 writes h as fp16 in the same order
+bool i4_tile_info(int tile, TileInfo *info);
+hipError_t launch_gemm_i4(int tile, GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles,
+                          hipStream_t s);
 
 struct ReduceArgs {
     const void *Y;               // bf16 [cap, H] or fp32 partials [split, cap, H]
@@ -106,6 +111,9 @@ struct QuantArgs {
     int pairs;
 };
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+
+// bf16 [n8 * 8] -> fp16 with each group of 8 reordered (0,4,1,5,2,6,3,7) (int4 GEMM1's A)
+hipError_t launch_f16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream_t s);
 
 int device_cu_count();
 

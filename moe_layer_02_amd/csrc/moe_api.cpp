@@ -77,7 +77,7 @@ moe_status check_layer(const moe_layer *L) {
         break;
     case MOE_DT_INT4_G128:
         if (!L->w13_s || !L->w13_z || !L->w2_s || !L->w2_z) return MOE_ERR_INVALID_ARGUMENT;
-        if (!aligned(L->w13_s, 2) || !aligned(L->w13_z, 2) || !aligned(L->w2_s, 2) || !aligned(L->w2_z, 2))
+        if (!aligned(L->w13_s, 4) || !aligned(L->w13_z, 4) || !aligned(L->w2_s, 4) || !aligned(L->w2_z, 4))
             return MOE_ERR_INVALID_ARGUMENT;
         break;
     default:
@@ -98,6 +98,9 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->block_m != t1->BM || p->block_m != t2->BM) return MOE_ERR_INVALID_ARGUMENT;
     if (p->split_k < 1 || p->split_k > 16) return MOE_ERR_INVALID_ARGUMENT;
+    // int4: the pipelined tiles pass h between the GEMMs as permuted fp16, the
+    // register-staged ones as bf16, so both GEMMs must be of one kind
+    if (wd == MOE_DT_INT4_G128 && (t1->stages > 0) != (t2->stages > 0)) return MOE_ERR_INVALID_ARGUMENT;
     // GEMM1: K = H, output columns I (each tile covers BN/2 gate and BN/2 up rows, and each
     // wave an equal number of gate and up fragments)
     if (L->H % t1->BK || L->I % (t1->BN / 2)) return MOE_ERR_INVALID_ARGUMENT;
@@ -114,6 +117,12 @@ struct Workspace {
 
 // scal words: [0] amax(x) bits, [1] amax(h) bits, [2] s1, [3] s2
 constexpr int kScalarWords = 4;
+
+// int4 with the pipelined tiles: GEMM1 reads the hidden states as permuted fp16
+bool f16_activations(const moe_layer *L, const moe_plan *p) {
+    TileInfo t;
+    return L->weight_dtype == MOE_DT_INT4_G128 && gemm_tile_info(L->weight_dtype, p->gemm1_tile, &t) && t.stages > 0;
+}
 
 Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     Workspace w{};
@@ -135,7 +144,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.inv_pos = take(pairs * 4);
     w.scal = take(kScalarWords * 4);
     const bool fp8 = L->weight_dtype == MOE_DT_FP8_E4M3;
-    w.xq = take(fp8 ? (size_t)T * L->H : 0);
+    w.xq = take(fp8 ? (size_t)T * L->H : f16_activations(L, p) ? (size_t)T * L->H * 2 : 0);
     w.h = take((size_t)w.cap * L->I * (fp8 ? 4 : 2));
     w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
     w.y = take(p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
@@ -226,6 +235,13 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         if ((err = launch_absmax(ab, stream)) != hipSuccess) return fail(err);
         QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs};
         if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
+        a1 = ws + w.xq;
+    } else if (f16_activations(L, &plan)) {
+        // int4: the hidden states as fp16 in the order the kernel dequantises nibbles
+        if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
+        if ((err = launch_f16_perm((const uint16_t *)hidden, (uint16_t *)(ws + w.xq), (int64_t)T * H / 8, stream)) !=
+            hipSuccess)
+            return fail(err);
         a1 = ws + w.xq;
     }
 
@@ -377,7 +393,7 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
                                {96, 128, 22, 22, 2}, {192, 128, 22, 22, 1}, {1e30, 256, 20, 20, 2}};
     static const Row fp8[] = {{1, 16, 9, 1, 1}, {8, 32, 2, 2, 1}, {64, 32, 11, 2, 1}, {256, 128, 5, 13, 1},
                               {1e30, 256, 12, 12, 1}};
-    static const Row int4[] = {{2, 16, 0, 0, 1}, {1e30, 32, 1, 1, 1}};
+    static const Row int4[] = {{8, 16, 11, 11, 1}, {1e30, 32, 12, 12, 1}};
     const Row *rows = bf16;
     int n = sizeof(bf16) / sizeof(Row);
     if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }

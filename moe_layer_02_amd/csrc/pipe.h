@@ -1,0 +1,100 @@
+// pipe.h -- device helpers of the direct-to-LDS pipelined GEMMs (gemm_pipe.hip, gemm_i4.hip).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Byte address of an LDS object in the LDS address space (what M0 holds for a DMA load).
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)p;
+}
+
+// Direct-to-LDS load of 16 (or 4) bytes per lane: lane l's bytes land at LDS address
+// lds + 16 l (4 l).  Issued as inline assembly: the compiler cannot tell which stage buffer
+// such a load fills, and around its own builtin it may insert s_waitcnt vmcnt(0) before
+// LDS reads, draining the stages in flight.  Stage order is kept by the kernels' explicit
+// s_waitcnt vmcnt and s_barrier; the "memory" clobber keeps every memory access in program
+// order around it.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void *g, uint32_t lds) {
+    static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most n (a multiple of LPW, n <= MAXS*LPW) of this wave's loads are pending
+template <int LPW, int MAXS>
+__device__ __forceinline__ void wait_stages(int later) {
+    if constexpr (MAXS >= 3) {
+        if (later >= 3) { wait_vmcnt<3 * LPW>(); return; }
+    }
+    if constexpr (MAXS >= 2) {
+        if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
+    }
+    if constexpr (MAXS >= 1) {
+        if (later >= 1) { wait_vmcnt<LPW>(); return; }
+    }
+    wait_vmcnt<0>();
+}
+
+// s_barrier without the fence of __syncthreads() (which would drain every pending load)
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// LDS position of 16-byte chunk c of tile row r is c ^ swz(r): a pair of rows shares a
+// position in the two halves of the 64 banks, 8 pairs cover the 8 positions, so 16 lanes
+// reading one chunk of 16 consecutive rows hit 64 distinct banks
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+template <int MS> struct AccOf { typedef f32x4 type; };
+template <> struct AccOf<32> { typedef f32x16 type; };
+
+// Row of a 16x16 (32x32) MFMA output fragment held in accumulator value r of this lane;
+// its column is lane % 16 (lane % 32).
+template <int MS>
+__device__ __forceinline__ int frag_row(int lane, int r) {
+    if constexpr (MS == 32) return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    return 4 * (lane >> 4) + r;
+}
+
+// Persistent-grid tile walk shared by the grouped GEMMs: split outermost, then groups of
+// group_m row blocks with the block index fastest inside a group.
+struct TileCoord {
+    int s, mb, nt;
+};
+__device__ __forceinline__ TileCoord tile_coord(int tile, int mn, int mblocks, int ntiles, int group_m) {
+    TileCoord c;
+    c.s = tile / mn;
+    const int rest = tile - c.s * mn;
+    const int gm0 = rest / (group_m * ntiles) * group_m;
+    const int gsz = min(group_m, mblocks - gm0);
+    const int local = rest - gm0 * ntiles;
+    c.mb = gm0 + local % gsz;
+    c.nt = local / gsz;
+    return c;
+}
+
+// workgroup b of a grid of G (a multiple of 8) starts at tile j0: consecutive tiles go to
+// one XCD (workgroups are dealt to the 8 XCDs round-robin)
+__device__ __forceinline__ int xcd_first_tile(int b, int G) {
+    return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+}
+
+}  // namespace moe

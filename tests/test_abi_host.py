@@ -119,6 +119,26 @@ def test_invalid_plans_rejected():
         assert ei.value.status == abi.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_int4_plans_keep_one_intermediate_format():
+    """The pipelined int4 tiles hand h over as permuted fp16 and read the hidden states
+    converted to fp16 (a T*H*2-byte region); the register-staged ones use bf16 h and no
+    conversion: a plan may not mix the two."""
+    cfg = synth.CONFIGS["deepseek"]
+    layer = fake_layer(cfg)
+    T = 8
+    for bad in [abi.Plan(16, 0, 4, 1), abi.Plan(16, 4, 0, 1)]:
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_workspace_bytes(layer, T, bad)
+        assert ei.value.status == abi.MOE_ERR_INVALID_ARGUMENT
+    staged, piped = abi.Plan(16, 0, 0, 1), abi.Plan(16, 4, 4, 1)
+    assert abi.moe_workspace_bytes(layer, T, piped) >= abi.moe_workspace_bytes(layer, T, staged) + T * cfg.H * 2
+    off_s, off_p = abi.moe_workspace_offsets(layer, T, staged), abi.moe_workspace_offsets(layer, T, piped)
+    assert off_s["h"] - off_s["x_q"] == 0 and off_p["h"] - off_p["x_q"] >= T * cfg.H * 2
+    # scales and zero points are read 4 bytes at a time
+    with pytest.raises(abi.MoEError):
+        abi.moe_default_plan(fake_layer(cfg, w13_s=0x10002), T)
+
+
 def test_invalid_layers_rejected():
     cfg = synth.CONFIGS["mixtral"]
     for layer in [fake_layer(cfg.with_shape(H=4000)),                     # H not a multiple of 128

@@ -21,10 +21,10 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 class Case:
     """A config with its device layer and the oracle's view of the same weights."""
 
-    def __init__(self, name, device_for_weights):
-        self.cfg = synth.CONFIGS[name]
+    def __init__(self, name, device_for_weights, cfg=None):
+        self.cfg = cfg or synth.CONFIGS[name]
         say("generating weights", name, "on", device_for_weights)
-        w = weights(name, device_for_weights)
+        w = synth.expert_weights(cfg, device=device_for_weights) if cfg else weights(name, device_for_weights)
         self.bias = synth.correction_bias(self.cfg)
         self.layer = device_layer(self.cfg, w, self.bias)
         self.W = oracle_weights(self.cfg, w)
@@ -230,6 +230,27 @@ def test_deepseek_int4(T):
 
 def test_deepseek_int4_largest_T_sampled():
     check_sampled("deepseek", 512, [0, 511])
+
+
+# DeepSeek-V3's gate and int4 format at a size the oracle runs in well under a second: three
+# K steps of 256 in GEMM1 (a ragged start for the K rotation), two in GEMM2 (split-K 2)
+I4_SMALL = synth.CONFIGS["deepseek"].with_shape(name="i4small", E=16, k=4, n_group=4, topk_group=2, H=768, I=512)
+
+
+@pytest.mark.parametrize("T", [1, 5, 37, 200])
+def test_int4_every_plan(T):
+    if "i4small" not in _cases:
+        _cases["i4small"] = Case("i4small", "cpu", I4_SMALL)
+    c = _cases["i4small"]
+    plans = valid_plans(c.layer, T)
+    tiles = {p.gemm1_tile for p in plans}
+    assert {0, 4, 5, 6, 7, 8, 9, 10} <= tiles, tiles       # staged and pipelined tiles both run
+    ref, _, _ = c.oracle(T)
+    for p in plans:
+        out, ws = c.gpu(T, p)
+        err = rel_l2(bf16_to_f64(out), ref)
+        assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+    check_intermediates(c, T, plans[-1], ws)
 
 
 # ---- properties ------------------------------------------------------------------------
