@@ -55,6 +55,7 @@ struct GemmArgs {
     uint32_t *amax_out;          // fp8 gate/up: |h| max as float bits (atomicMax), may be null
     int group_m;                 // tile order: blocks per group (set by the launcher)
     int rotate_k;                // 1: each tile starts its K walk at its own offset
+    int out_by_pair;             // down, no split: write row p = sorted[row] of C (top-1: the token's output row)
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };

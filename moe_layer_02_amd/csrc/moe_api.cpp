@@ -124,6 +124,10 @@ bool f16_activations(const moe_layer *L, const moe_plan *p) {
     return L->weight_dtype == MOE_DT_INT4_G128 && gemm_tile_info(L->weight_dtype, p->gemm1_tile, &t) && t.stages > 0;
 }
 
+// top-1 routing without a K split: each token owns one row of the down projection, which
+// GEMM2 writes straight into the output (no unpermute-and-reduce pass)
+bool direct_output(const moe_layer *L, const moe_plan *p) { return L->route.top_k == 1 && p->split_k == 1; }
+
 Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     Workspace w{};
     const int k = L->route.top_k, E = L->E;
@@ -147,7 +151,8 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.xq = take(fp8 ? (size_t)T * L->H : f16_activations(L, p) ? (size_t)T * L->H * 2 : 0);
     w.h = take((size_t)w.cap * L->I * (fp8 ? 4 : 2));
     w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
-    w.y = take(p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
+    w.y = take(direct_output(L, p) ? 0
+               : p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
     w.align_scratch = take((size_t)align_scratch_bytes(pairs, E));
     w.total = o;
     return w;
@@ -303,8 +308,10 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     d.bs = L->w2_s;
     d.bz = L->w2_z;
     d.sz_expert_stride = (int64_t)H * (I / 128);
-    d.C = ws + w.y;
+    const bool direct = direct_output(L, &plan);
+    d.C = direct ? out : (void *)(ws + w.y);
     d.ldc = H;
+    d.out_by_pair = direct;
     d.partial_stride = w.cap * (int64_t)H;
     d.K = I;
     d.N = H;
@@ -317,10 +324,13 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
                            mblocks_max * (H / t2.BN) * plan.split_k, stream)) != hipSuccess)
         return fail(err);
 
-    // 7. unpermute and reduce
-    if ((err = mark(MOE_STAGE_REDUCE)) != hipSuccess) return MOE_ERR_HIP;
-    ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out, T, k, H};
-    if ((err = launch_reduce(r, stream)) != hipSuccess) return fail(err);
+    // 7. unpermute and reduce (top-1 without a split: GEMM2 wrote the output already)
+    if (!direct) {
+        if ((err = mark(MOE_STAGE_REDUCE)) != hipSuccess) return MOE_ERR_HIP;
+        ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out,
+                     T, k, H};
+        if ((err = launch_reduce(r, stream)) != hipSuccess) return fail(err);
+    }
     if (events) {
         if (hipEventRecord((hipEvent_t)events[nst], stream) != hipSuccess) return MOE_ERR_HIP;
         *n_stages = nst;

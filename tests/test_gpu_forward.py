@@ -114,6 +114,33 @@ def test_tiny_every_plan(T):
     check_intermediates(c, T, plans[-1], ws)
 
 
+TINY_TOP1 = synth.CONFIGS["tiny"].with_shape(name="tiny_top1", k=1, route_kind=abi.ROUTE_SIGMOID, renormalize=False)
+
+
+@pytest.mark.parametrize("T", [1, 37])
+def test_tiny_top1_every_plan(T):
+    """Top-1 routing: plans without a K split write GEMM2's rows straight into the output
+    (no reduce pass), split plans go through the reduce; both match the oracle."""
+    if "tiny_top1" not in _cases:
+        _cases["tiny_top1"] = Case("tiny_top1", "cpu", TINY_TOP1)
+    c = _cases["tiny_top1"]
+    plans = valid_plans(c.layer, T)
+    assert any(p.split_k == 1 for p in plans) and any(p.split_k > 1 for p in plans)
+    ref, _, _ = c.oracle(T)
+    x, lg = c.inputs(T)
+    for p in plans:
+        out, ws = c.gpu(T, p)
+        err = rel_l2(bf16_to_f64(out), ref)
+        assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+        if p.gemm1_tile == plans[0].gemm1_tile and p.block_m == plans[0].block_m:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
+            o2 = torch.empty_like(out)
+            stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), o2, ws, ev, p)
+            torch.cuda.synchronize()
+            assert ("reduce" in stages) == (p.split_k > 1), (p.as_tuple(), stages)
+            assert torch.equal(o2.view(torch.int16), out.view(torch.int16))
+
+
 def test_tiny_zero_tokens():
     c = case("tiny")
     out = torch.empty((0, c.cfg.H), dtype=torch.bfloat16, device="cuda")
