@@ -1,10 +1,12 @@
 """Benchmark of the fused-MoE layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config mixtral] [--tokens 4096] [--no-sweep]
+    python bench.py [--steps K] [--warmup W] [--config mixtral] [--tokens 4096] [--sweep 1,32,256]
 
 A step is one moe_forward (route, align, [fp8 quantisation], GEMM1, GEMM2, reduce) over one
 batch of T tokens of seeded synthetic inputs already resident in HBM; steps are replayed
-from a captured hipGraph.  Prints one JSON line: whole-layer tokens/s (the headline),
+from a captured hipGraph.  Prints one JSON line: whole-layer tokens/s (the headline, K
+replays back to back), the same step with cold caches (a 512 MiB buffer read before each
+replay, outside the timed region; median, p10, p90),
 TFLOP/s and HBM GB/s with their fractions of the MI355X peaks, the dominant kernel's
 roofline (its duration from HIP events recorded on the launch stream around each step of
 the forward), the CPU oracle's throughput on a bounded sample of the same workload, and a
@@ -30,6 +32,7 @@ from moe_layer_02_amd import abi, synth  # noqa: E402
 
 METRIC = "fused-MoE layer tokens/s + TFLOP/s & HBM GB/s (% of roofline) vs T, 1 GPU"
 PEAK_HBM = 8.0e12                                  # B/s, MI355X HBM3E
+FLUSH_BYTES = 512 << 20                            # > 256 MB last-level cache + 8 x 4 MB L2
 PEAK_MFMA = {synth.WDT_BF16: 2.5e15, synth.WDT_FP8: 5.0e15, synth.WDT_INT4: 2.5e15}   # dense, fp16 for int4
 DTYPE_NAME = {synth.WDT_BF16: "bf16", synth.WDT_FP8: "fp8-e4m3 w8a8", synth.WDT_INT4: "int4-g128 w / fp16 mfma"}
 WORKLOAD = {
@@ -82,6 +85,8 @@ class Bench:
             routed_scaling=cfg.routed_scaling, w13_scale=d.get("w13_scale"), w2_scale=d.get("w2_scale"),
             w13_s=d.get("w13_s"), w13_z=d.get("w13_z"), w2_s=d.get("w2_s"), w2_z=d.get("w2_z"),
             correction_bias=None if self.bias is None else self.bias.cuda())
+        self.flush = torch.ones((FLUSH_BYTES // 4096, 1024), dtype=torch.float32, device="cuda")
+        self.flush_out = torch.empty(1024, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
         print("[bench] %s weights generated on the GPU in %.1f s" % (cfg.name, time.time() - t0),
               file=sys.stderr, flush=True)
@@ -120,8 +125,19 @@ class Bench:
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / steps
+        # cold caches: before each timed replay, read a buffer larger than the 256 MB
+        # last-level cache and the L2s together, outside the timed region (a read leaves
+        # clean lines; a write would leave dirty ones whose write-back lands in the replay)
+        cold = []
+        for _ in range(max(steps, 10)):
+            torch.amax(self.flush, dim=0, out=self.flush_out)
+            t0.record()
+            g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            cold.append(t0.elapsed_time(t1))
         active = self.active_experts(T, plan, ws)
-        return ms, active, plan, (x, lg, ws, out)
+        return ms, np.array(cold), active, plan, (x, lg, ws, out)
 
     def time_stages(self, T, plan, bufs, steps):
         """Average duration of each step of the forward, from HIP events recorded on the
@@ -142,14 +158,17 @@ class Bench:
 
 def measure(b: Bench, T, steps, warmup, stage_steps):
     cfg = b.cfg
-    ms, active, plan, bufs = b.time_graph(T, steps, warmup)
+    ms, cold, active, plan, bufs = b.time_graph(T, steps, warmup)
     stages = b.time_stages(T, plan, bufs, stage_steps)
     sec = ms / 1e3
     flops, mbytes = layer_flops(cfg, T), layer_min_bytes(cfg, T, active)
     t_hbm, t_mfma = mbytes / PEAK_HBM, flops / PEAK_MFMA[cfg.wdtype]
+    c50, c10, c90 = (float(np.percentile(cold, q)) for q in (50, 10, 90))
     return dict(T=T, ms_per_step=ms, tokens_per_s=T / sec, tflops=flops / sec / 1e12, hbm_gbps=mbytes / sec / 1e9,
                 frac_hbm=mbytes / sec / PEAK_HBM, frac_mfma=flops / sec / PEAK_MFMA[cfg.wdtype],
                 roofline_frac=max(t_hbm, t_mfma) / sec, bound="hbm" if t_hbm >= t_mfma else "mfma",
+                cold_ms={"median": round(c50, 4), "p10": round(c10, 4), "p90": round(c90, 4), "n": len(cold)},
+                cold_tokens_per_s=T / (c50 / 1e3), cold_roofline_frac=max(t_hbm, t_mfma) / (c50 / 1e3),
                 active_experts=active, plan=abi.moe_plan_describe(b.layer.struct, T, plan),
                 stages_us={k: round(v, 2) for k, v in stages.items()})
 
@@ -289,6 +308,8 @@ def main():
         "tflops": round(head["tflops"], 3), "hbm_gbps": round(head["hbm_gbps"], 2),
         "frac_mfma": round(head["frac_mfma"], 4), "frac_hbm": round(head["frac_hbm"], 4),
         "layer_roofline_frac": round(head["roofline_frac"], 4), "layer_bound": head["bound"],
+        "cold_ms": head["cold_ms"], "cold_tokens_per_s": round(head["cold_tokens_per_s"], 2),
+        "cold_layer_roofline_frac": round(head["cold_roofline_frac"], 4),
         "stages_us": head["stages_us"], "roofline": roof, "cpu_baseline": cpu, "sweep": sweep,
     }
     print(json.dumps(line), flush=True)

@@ -29,20 +29,23 @@ namespace {
 
 enum { WT_BF16 = 0, WT_FP8 = 2, WT_INT4 = 3 };
 
-template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_>
+template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_>
 struct PCfg {
     static constexpr int BM = BM_, BN = BN_, KS = KS_, ST = ST_, WM = WM_, WN = WN_;
     static constexpr int MS = MS_;                            // MFMA output tile: 16x16 or 32x32
+    static constexpr int SB = SB_;                            // bytes of K per row and slab: 128 or 64
     static constexpr int NW = WM * WN, NT = NW * kWave;
-    static constexpr int SLAB_K = WT == WT_FP8 ? 128 : 64;   // elements in a 128-byte slab row
+    static constexpr int SLAB_K = WT == WT_FP8 ? SB : SB / 2; // K elements in a slab row
     static constexpr int BK = KS * SLAB_K;
     static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MS, FN = TN / MS;
-    static constexpr int A_STAGE = KS * BM * 128, STAGE = KS * (BM + BN) * 128;
-    static constexpr int A_LOADS = KS * BM / 8, LOADS = KS * (BM + BN) / 8;   // wave instructions per stage
+    static constexpr int RPI = 1024 / SB;                     // rows one DMA instruction fills
+    static constexpr int A_STAGE = KS * BM * SB, STAGE = KS * (BM + BN) * SB;
+    static constexpr int A_LOADS = KS * BM / RPI, LOADS = KS * (BM + BN) / RPI;   // wave instructions per stage
     static constexpr int LPW = LOADS / NW;
     static_assert(LOADS % NW == 0, "stage loads must split evenly over the waves");
-    static_assert(BM % (MS * WM) == 0 && BN % (MS * WN) == 0 && BM % 8 == 0, "tile / wave grid mismatch");
+    static_assert(BM % (MS * WM) == 0 && BN % (MS * WN) == 0 && BM % RPI == 0, "tile / wave grid mismatch");
     static_assert(MS == 16 || (MS == 32 && WT == WT_BF16), "32x32 MFMA tiles are bf16 only");
+    static_assert(SB == 128 || (SB == 64 && WT == WT_BF16), "64-byte slabs hold whole MFMA K steps for bf16 only");
     static_assert((ST - 2) * LPW <= 63, "vmcnt range");
     // skip loading A's filler rows: worth it where a block is mostly padding (small blocks,
     // small T); large tiles keep the registers the per-load flags would take
@@ -81,24 +84,23 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         for (int q = 0; q < C::LPW; q++) {
             on[q] = true;
             const int ins = wave + q * C::NW;
-            const int r_in = lane >> 3;
             if (ins < C::A_LOADS) {
-                const int slab = ins / (C::BM / 8), rb = ins % (C::BM / 8) * 8;
-                const int r = rb + r_in;
-                const int chunk = (lane & 7) ^ swz(r);
+                const int slab = ins / (C::BM / C::RPI), rb = ins % (C::BM / C::RPI) * C::RPI;
+                int r, chunk;
+                dma_lane<C::SB>(lane, rb, r, chunk);
                 const int p = a.sorted[row0 + r];
                 const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + r;
                 // a filler row's products are never read back, so its LDS row may keep stale
                 // data; the lanes of the instruction's first row always load, so every load
                 // instruction runs with a non-empty mask and counts in vmcnt
                 on[q] = !C::SKIP_FILLER || p < a.pairs || (lane >> 3) == 0;
-                src[q] = (const char *)a.A + arow * a.lda * ebytes + kb + slab * 128 + chunk * 16;
-                dst[q] = (slab * C::BM + rb) * 128;
+                src[q] = (const char *)a.A + arow * a.lda * ebytes + kb + slab * C::SB + chunk * 16;
+                dst[q] = (slab * C::BM + rb) * C::SB;
             } else {
                 const int j = ins - C::A_LOADS;
-                const int slab = j / (C::BN / 8), rb = j % (C::BN / 8) * 8;
-                const int rr = rb + r_in;
-                const int chunk = (lane & 7) ^ swz(rr);
+                const int slab = j / (C::BN / C::RPI), rb = j % (C::BN / C::RPI) * C::RPI;
+                int rr, chunk;
+                dma_lane<C::SB>(lane, rb, rr, chunk);
                 int64_t grow;
                 if (KIND == GEMM_GATE_UP) {   // LDS rows of wave column w: its gate half, then its up half
                     const int wcol = rr / C::TN, i = rr % C::TN, half = C::TN / 2;
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 } else {
                     grow = (int64_t)nt * C::BN + rr;
                 }
-                src[q] = (const char *)a.B + (int64_t)e * a.b_expert_stride + grow * a.ldb + kb + slab * 128 + chunk * 16;
-                dst[q] = C::A_STAGE + (slab * C::BN + rb) * 128;
+                src[q] = (const char *)a.B + (int64_t)e * a.b_expert_stride + grow * a.ldb + kb + slab * C::SB + chunk * 16;
+                dst[q] = C::A_STAGE + (slab * C::BN + rb) * C::SB;
             }
         }
         // with rotate_k (weight streaming: no two tiles share operands) each tile walks its K
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         auto issue = [&](int kstep) {
             const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
             const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
-            const int64_t koff = (int64_t)kr * C::KS * 128;
+            const int64_t koff = (int64_t)kr * C::KS * C::SB;
 #pragma unroll
             for (int q = 0; q < C::LPW; q++)
                 if (on[q])
@@ -153,19 +155,20 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step.
                 // Double-buffered: the reads of step k + 1 are issued before the MFMAs of
                 // step k (scheduling barriers keep that order).
-                constexpr int NK = C::KS * 4;
+                constexpr int KPS = C::SB / 32;                 // 16-K steps per slab
+                constexpr int NK = C::KS * KPS;
                 bf16x8 af[2][C::FM], bfr[2][C::FN];
                 auto load = [&](int k, int buf) {
-                    const int sl = k / 4, ci = (k % 4) * 2 + (lane >> 5);
+                    const int sl = k / KPS, ci = (k % KPS) * 2 + (lane >> 5);
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++) {
                         const int r = wm * C::TM + fm * 32 + (lane & 31);
-                        af[buf][fm] = *(const bf16x8 *)(sa + (sl * C::BM + r) * 128 + ((ci ^ swz(r)) << 4));
+                        af[buf][fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
                     }
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const int r = wn * C::TN + fn * 32 + (lane & 31);
-                        bfr[buf][fn] = *(const bf16x8 *)(sb + (sl * C::BN + r) * 128 + ((ci ^ swz(r)) << 4));
+                        bfr[buf][fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
                     }
                 };
                 load(0, 0);
@@ -185,19 +188,19 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
 #pragma unroll
                 for (int sl = 0; sl < C::KS; sl++)
 #pragma unroll
-                    for (int kk = 0; kk < 2; kk++) {
+                    for (int kk = 0; kk < C::SB / 64; kk++) {
                         // 16x16x32: lane l holds row l%16, K elements 8*(l/16) .. +7 of the step
                         const int ci = kk * 4 + (lane >> 4);
                         bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
                         for (int fm = 0; fm < C::FM; fm++) {
                             const int r = wm * C::TM + fm * 16 + (lane & 15);
-                            af[fm] = *(const bf16x8 *)(sa + (sl * C::BM + r) * 128 + ((ci ^ swz(r)) << 4));
+                            af[fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
                         }
 #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++) {
                             const int r = wn * C::TN + fn * 16 + (lane & 15);
-                            bfr[fn] = *(const bf16x8 *)(sb + (sl * C::BN + r) * 128 + ((ci ^ swz(r)) << 4));
+                            bfr[fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
                         }
 #pragma unroll
                         for (int fm = 0; fm < C::FM; fm++)
@@ -212,18 +215,18 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++) {
                         const int r = wm * C::TM + fm * 16 + (lane & 15);
-                        const char *row = sa + (sl * C::BM + r) * 128;
-                        const uint4 lo = *(const uint4 *)(row + ((c0 ^ swz(r)) << 4));
-                        const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ swz(r)) << 4));
+                        const char *slab = sa + sl * C::BM * 128;
+                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
                         af[buf][fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     }
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const int r = wn * C::TN + fn * 16 + (lane & 15);
-                        const char *row = sb + (sl * C::BN + r) * 128;
-                        const uint4 lo = *(const uint4 *)(row + ((c0 ^ swz(r)) << 4));
-                        const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ swz(r)) << 4));
+                        const char *slab = sb + sl * C::BN * 128;
+                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
                         bfr[buf][fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     }
@@ -297,36 +300,46 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
 }
 
 // ---- tile tables (ids continue gemm.hip's per weight type) --------------------------------
-//        id  BM   BN  KS ST WM WN MS
+//        id  BM   BN  KS ST WM WN MS  SB
 #define PIPE_BF16_TILES(X)              \
-    X(7, 128, 256, 1, 3, 2, 2, 16)      \
-    X(8, 128, 128, 1, 4, 2, 2, 16)      \
-    X(9, 16, 128, 2, 4, 1, 4, 16)       \
-    X(10, 16, 64, 4, 3, 1, 2, 16)       \
-    X(11, 64, 128, 1, 4, 2, 2, 16)      \
-    X(12, 32, 128, 2, 3, 1, 4, 16)      \
-    X(13, 128, 256, 1, 3, 2, 2, 32)     \
-    X(14, 128, 128, 1, 4, 2, 2, 32)     \
-    X(15, 64, 128, 1, 4, 2, 2, 32)      \
-    X(16, 256, 128, 1, 3, 2, 2, 32)     \
-    X(18, 64, 256, 1, 4, 1, 4, 32)      \
-    X(19, 32, 256, 1, 4, 1, 4, 32)      \
-    X(20, 256, 256, 1, 2, 2, 4, 16)     \
-    X(21, 256, 256, 1, 2, 2, 4, 32)     \
-    X(22, 128, 256, 1, 3, 2, 4, 16)     \
-    X(23, 256, 128, 1, 3, 4, 2, 16)     \
-    X(24, 256, 256, 1, 2, 4, 4, 32)     \
-    X(25, 256, 256, 1, 2, 4, 4, 16)     \
-    X(26, 128, 256, 1, 3, 4, 4, 32)
+    X(7, 128, 256, 1, 3, 2, 2, 16, 128)      \
+    X(8, 128, 128, 1, 4, 2, 2, 16, 128)      \
+    X(9, 16, 128, 2, 4, 1, 4, 16, 128)       \
+    X(10, 16, 64, 4, 3, 1, 2, 16, 128)       \
+    X(11, 64, 128, 1, 4, 2, 2, 16, 128)      \
+    X(12, 32, 128, 2, 3, 1, 4, 16, 128)      \
+    X(13, 128, 256, 1, 3, 2, 2, 32, 128)     \
+    X(14, 128, 128, 1, 4, 2, 2, 32, 128)     \
+    X(15, 64, 128, 1, 4, 2, 2, 32, 128)      \
+    X(16, 256, 128, 1, 3, 2, 2, 32, 128)     \
+    X(18, 64, 256, 1, 4, 1, 4, 32, 128)      \
+    X(19, 32, 256, 1, 4, 1, 4, 32, 128)      \
+    X(20, 256, 256, 1, 2, 2, 4, 16, 128)     \
+    X(21, 256, 256, 1, 2, 2, 4, 32, 128)     \
+    X(22, 128, 256, 1, 3, 2, 4, 16, 128)     \
+    X(23, 256, 128, 1, 3, 4, 2, 16, 128)     \
+    X(24, 256, 256, 1, 2, 4, 4, 32, 128)     \
+    X(25, 256, 256, 1, 2, 4, 4, 16, 128)     \
+    X(26, 128, 256, 1, 3, 4, 4, 32, 128)     \
+    X(27, 256, 128, 1, 3, 4, 2, 32, 128)     \
+    X(28, 128, 256, 1, 3, 2, 4, 32, 128)     \
+    X(29, 256, 128, 1, 3, 4, 2, 16, 128) \
+    X(30, 256, 256, 1, 4, 4, 4, 16, 64)  \
+    X(31, 256, 256, 1, 4, 2, 4, 32, 64)  \
+    X(32, 256, 256, 1, 4, 2, 4, 16, 64)  \
+    X(33, 256, 256, 1, 5, 4, 4, 16, 64)  \
+    X(34, 256, 256, 1, 5, 2, 4, 32, 64)  \
+    X(35, 256, 128, 1, 5, 4, 2, 32, 64)  \
+    X(36, 128, 256, 1, 5, 2, 4, 32, 64)
 #define PIPE_FP8_TILES(X)               \
-    X(7, 128, 256, 1, 3, 2, 2, 16)      \
-    X(8, 128, 128, 1, 4, 2, 2, 16)      \
-    X(9, 16, 128, 2, 4, 1, 4, 16)       \
-    X(10, 64, 128, 1, 4, 2, 2, 16)      \
-    X(11, 32, 128, 2, 3, 1, 4, 16)      \
-    X(12, 256, 256, 1, 2, 2, 4, 16)     \
-    X(13, 128, 256, 1, 3, 2, 4, 16)     \
-    X(14, 256, 256, 1, 2, 4, 4, 16)
+    X(7, 128, 256, 1, 3, 2, 2, 16, 128)      \
+    X(8, 128, 128, 1, 4, 2, 2, 16, 128)      \
+    X(9, 16, 128, 2, 4, 1, 4, 16, 128)       \
+    X(10, 64, 128, 1, 4, 2, 2, 16, 128)      \
+    X(11, 32, 128, 2, 3, 1, 4, 16, 128)      \
+    X(12, 256, 256, 1, 2, 2, 4, 16, 128)     \
+    X(13, 128, 256, 1, 3, 2, 4, 16, 128)     \
+    X(14, 256, 256, 1, 2, 4, 4, 16, 128)
 
 template <class C, int WT, int KIND, bool PARTIAL>
 hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
@@ -362,13 +375,13 @@ hipError_t launch_kind(GemmKind kind, bool partial, const GemmArgs &a, int64_t m
 }  // namespace
 
 bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
-#define PINFO(WT, id, bm, bn, ks, st, wm, wn, ms)                                          \
+#define PINFO(WT, id, bm, bn, ks, st, wm, wn, ms, sb)                                      \
     if (tile == id) {                                                                      \
-        *info = TileInfo{bm, bn, ks * (WT == WT_FP8 ? 128 : 64), wm, wn, st, ms};          \
+        *info = TileInfo{bm, bn, ks * (WT == WT_FP8 ? sb : sb / 2), wm, wn, st, ms};       \
         return true;                                                                       \
     }
-#define PI_BF16(id, bm, bn, ks, st, wm, wn, ms) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms)
-#define PI_FP8(id, bm, bn, ks, st, wm, wn, ms) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms)
+#define PI_BF16(id, bm, bn, ks, st, wm, wn, ms, sb) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
+#define PI_FP8(id, bm, bn, ks, st, wm, wn, ms, sb) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
     if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) }
     if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) }
     if (wdtype == WT_INT4) return i4_tile_info(tile, info);
@@ -377,10 +390,10 @@ bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
 
 hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
                             int64_t max_tiles, hipStream_t s) {
-#define PLAUNCH(WT, id, bm, bn, ks, st, wm, wn, ms) \
-    if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms>, WT>(kind, partial, a, max_tiles, s);
-#define PL_BF16(id, bm, bn, ks, st, wm, wn, ms) PLAUNCH(WT_BF16, id, bm, bn, ks, st, wm, wn, ms)
-#define PL_FP8(id, bm, bn, ks, st, wm, wn, ms) PLAUNCH(WT_FP8, id, bm, bn, ks, st, wm, wn, ms)
+#define PLAUNCH(WT, id, bm, bn, ks, st, wm, wn, ms, sb) \
+    if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms, sb>, WT>(kind, partial, a, max_tiles, s);
+#define PL_BF16(id, bm, bn, ks, st, wm, wn, ms, sb) PLAUNCH(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
+#define PL_FP8(id, bm, bn, ks, st, wm, wn, ms, sb) PLAUNCH(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
     if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) }
     if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) }
     if (wdtype == WT_INT4) return launch_gemm_i4(tile, kind, partial, a, max_tiles, s);

@@ -395,15 +395,17 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     if (st != MOE_OK) return st;
     if (T < 0 || !plan) return MOE_ERR_INVALID_ARGUMENT;
     // Plans by rows per expert r = T*k/E, from timing every valid plan of the Mixtral,
-    // Qwen2, Llama-4-Scout and DeepSeek-V3 shapes on MI355X (each pick within ~10% of the
-    // fastest plan at every measured T).  Small r streams weights (16-row blocks, narrow
-    // tiles, pipelined direct-to-LDS loads); large r is MFMA work (256x256 tiles, 8 waves).
+    // Llama-4-Scout, Qwen2 and DeepSeek-V3 shapes on MI355X (graph replays): each row is the
+    // plan with the smallest worst-case slowdown over the measured points of its range
+    // (within 4% of the fastest plan at every point).  Small r streams weights (16-row
+    // blocks, narrow tiles, split-K for GEMM2); large r is MFMA work (256x256 tiles of 16
+    // waves).
     struct Row { double r_max; int bm, g1, g2, split; };
-    static const Row bf16[] = {{1, 16, 10, 10, 2},   {12, 16, 1, 9, 1},     {48, 64, 18, 11, 1},
-                               {96, 128, 22, 22, 2}, {192, 128, 22, 22, 1}, {1e30, 256, 20, 20, 2}};
-    static const Row fp8[] = {{1, 16, 9, 1, 1}, {8, 32, 2, 2, 1}, {64, 32, 11, 2, 1}, {256, 128, 5, 13, 1},
-                              {1e30, 256, 12, 12, 1}};
-    static const Row int4[] = {{8, 16, 11, 11, 1}, {1e30, 32, 12, 12, 1}};
+    static const Row bf16[] = {{1.5, 16, 9, 9, 4},     {8, 32, 19, 12, 1},    {24, 64, 18, 11, 1},
+                               {96, 128, 22, 22, 2},   {384, 256, 25, 25, 1}, {768, 256, 25, 25, 2},
+                               {1e30, 256, 25, 25, 1}};
+    static const Row fp8[] = {{8, 16, 9, 1, 1}, {48, 32, 11, 2, 1}, {192, 128, 7, 13, 1}, {1e30, 256, 12, 14, 1}};
+    static const Row int4[] = {{8, 16, 10, 11, 1}, {1e30, 32, 12, 12, 1}};
     const Row *rows = bf16;
     int n = sizeof(bf16) / sizeof(Row);
     if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }
@@ -427,7 +429,7 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     }
     // any valid plan (tiny or unusual shapes)
     for (int bm : {16, 32, 64, 128, 256})
-        for (int g = 0; g < 32; g++) {
+        for (int g = 0; g < 40; g++) {
             moe_plan p{bm, g, g, 1};
             if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
                 *plan = p;

@@ -20,6 +20,11 @@ __device__ __forceinline__ uint32_t lds_addr(T *p) {
 // LDS reads, draining the stages in flight.  Stage order is kept by the kernels' explicit
 // s_waitcnt vmcnt and s_barrier; the "memory" clobber keeps every memory access in program
 // order around it.
+// M0 is a register the compiler reserves (it warns that a clobber of it may not be
+// preserved): the statement writes M0 itself, right before the load that reads it, and
+// the kernels using it keep no other value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(const void *g, uint32_t lds) {
     static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
@@ -29,6 +34,7 @@ __device__ __forceinline__ void lds_dma(const void *g, uint32_t lds) {
     else
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -62,6 +68,34 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // position in the two halves of the 64 banks, 8 pairs cover the 8 positions, so 16 lanes
 // reading one chunk of 16 consecutive rows hit 64 distinct banks
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Slabs of SB = 64-byte rows (32 bf16 of K) pack two rows into each 128-byte line: row r
+// is line r / 2, half r % 2, and its chunk c (0..3) sits at position (4 (r % 2) + c) ^ s
+// with s = (line / 2) % 4.  16 lanes reading one chunk of 16 consecutive rows touch 8
+// lines; lines alternate between the two halves of the banks, and within a half the four
+// lines have four different s, so the 16 positions are all distinct: conflict-free like
+// the 128-byte layout.
+template <int SB>
+__device__ __forceinline__ int slab_off(int r, int c) {
+    if constexpr (SB == 128) return r * 128 + ((c ^ swz(r)) << 4);
+    else return (r >> 1) * 128 + (((((r & 1) << 2) | c) ^ ((r >> 2) & 3)) << 4);
+}
+
+// The row and chunk that lane `lane` of a DMA instruction filling the 1024 LDS bytes of
+// rows rb .. rb + 1024 / SB - 1 (rb a multiple of that count) must load: lane l writes
+// LDS bytes 16 l .. 16 l + 15 of the instruction's range, i.e. slab_off(row, chunk).
+template <int SB>
+__device__ __forceinline__ void dma_lane(int lane, int rb, int &row, int &chunk) {
+    if constexpr (SB == 128) {
+        row = rb + (lane >> 3);
+        chunk = (lane & 7) ^ swz(row);
+    } else {
+        const int line = (rb >> 1) + (lane >> 3);
+        const int v = (lane & 7) ^ ((line >> 1) & 3);
+        row = 2 * line + (v >> 2);
+        chunk = v & 3;
+    }
+}
 
 template <int MS> struct AccOf { typedef f32x4 type; };
 template <> struct AccOf<32> { typedef f32x16 type; };

@@ -19,11 +19,11 @@ import torch
 from moe_layer_02_amd import abi, synth
 
 
-def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 32):
+def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64, 128, 256), tiles=None):
     out = []
-    for bm in (16, 32, 64, 128, 256):
-        for g1 in range(max_tile):
-            for g2 in range(max_tile):
+    for bm in bms:
+        for g1 in (tiles if tiles is not None else range(max_tile)):
+            for g2 in (tiles if tiles is not None else range(max_tile)):
                 for sk in (1, 2, 4, 8):
                     p = abi.Plan(bm, g1, g2, sk)
                     try:
@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--config", default="mixtral", choices=sorted(synth.CONFIGS))
     ap.add_argument("--tokens", default="1,32,256,4096")
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--bm", default="16,32,64,128,256", help="block heights to try")
+    ap.add_argument("--tiles", default=None, help="tile ids to try for both GEMMs (default: all)")
     args = ap.parse_args()
     cfg = synth.CONFIGS[args.config]
     w = synth.expert_weights(cfg, device="cuda")
@@ -79,13 +81,17 @@ def main():
         x = synth.hidden_states(cfg, T).cuda()
         lg = synth.router_logits(cfg, T).cuda()
         res = []
-        for p in valid_plans(layer, T):
+        bms = tuple(int(b) for b in args.bm.split(","))
+        tiles = None if args.tiles is None else [int(t) for t in args.tiles.split(",")]
+        for p in valid_plans(layer, T, bms=bms, tiles=tiles):
             us = time_plan(layer, x, lg, T, p, args.reps)
             res.append((us, p.as_tuple()))
             print("[tune] %s T=%d plan=%s %.1f us" % (cfg.name, T, p.as_tuple(), us), file=sys.stderr, flush=True)
         res.sort()
         default = layer.plan(T).as_tuple()
-        dus = next(u for u, p in res if p == default)
+        dus = next((u for u, p in res if p == default), None)
+        if dus is None:
+            dus = time_plan(layer, x, lg, T, layer.plan(T), args.reps)
         print(json.dumps({"config": cfg.name, "T": T, "best": res[0][1], "best_us": round(res[0][0], 2),
                           "default": default, "default_us": round(dus, 2),
                           "all": [[round(u, 2), p] for u, p in res]}), flush=True)

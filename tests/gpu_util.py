@@ -81,7 +81,7 @@ def workspace_view(layer, T, plan, ws, region, dtype, count):
 
 def valid_plans(layer, T):
     """Every (block_m, tile1, tile2, split) the library accepts for this layer."""
-    n = 32
+    n = 40
     out = []
     for g1 in range(n):
         for g2 in range(n):
