@@ -34,7 +34,8 @@
  *  - Tensors are dense and row-major.  bf16 is the bit pattern of IEEE binary32's upper
  *    half; fp8 is OCP E4M3FN (bias 7, max 448, no infinities); int4 weights are unsigned
  *    nibbles, column c of a row in byte c/2 (low nibble when c is even), dequantised as
- *    (q - z) * s with fp16 scale s and fp16 zero point z per group of 128 columns.
+ *    (q - z) * s with fp16 scale s and fp16 zero point z per group of 128 columns; z must
+ *    hold an integer in [0, 15] (as GPTQ/AWQ packing produces).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -65,7 +66,9 @@ typedef enum {
     MOE_DT_FP32 = 1,
     MOE_DT_FP8_E4M3 = 2,    /* w8a8: per-expert per-tensor weight scales, dynamic
                                per-tensor activation scales */
-    MOE_DT_INT4_G128 = 3    /* weights only; activations stay bf16 */
+    MOE_DT_INT4_G128 = 3    /* weights only: the hidden states stay bf16 at the boundary
+                               (the kernels multiply in fp16, exact for bf16 values in
+                               fp16's normal range) */
 } moe_dtype;
 
 /*
