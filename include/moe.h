@@ -199,6 +199,8 @@ moe_status moe_workspace_bytes(const moe_layer *layer, int32_t T, const moe_plan
  *  workspace  [device] at least moe_workspace_bytes(layer, T, plan) bytes, 256-byte aligned;
  *             scratch only, its contents on return are unspecified.
  *  plan       [host] or NULL for moe_default_plan.
+ * MOE_ERR_UNSUPPORTED when T*k > 2^24, or when T*H*2 or capacity*I*2 bytes exceed 2^32 - 1
+ * (the GEMMs address activation rows with 32-bit offsets).
  */
 moe_status moe_forward(const moe_layer *layer, int32_t T, const void *hidden, const void *logits,
                        void *out, void *workspace, size_t workspace_bytes, const moe_plan *plan,

@@ -69,7 +69,7 @@ __device__ __forceinline__ _Float16 half_of(uint32_t w, int hi) {
 // column c of h is stored at this position (the (0,4,1,5,2,6,3,7) order inside each 8)
 __device__ __forceinline__ int perm_col(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
 
-enum { LD_A = 0, LD_B = 1, LD_SZ = 2 };
+enum { LD_A = 0, LD_B = 1, LD_S = 2, LD_Z = 3 };
 
 template <class C, int KIND, bool PARTIAL>
 __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
         const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
         const int s = tc.s, mb = tc.mb, nt = tc.nt;
-        const int e = a.eids[mb];
+        const int e = __builtin_amdgcn_readfirstlane(a.eids[mb]);
         const int row0 = mb * C::BM;
 
         // B row (of the expert's matrix) that tile row rr of the B slab holds
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
 
         // per load instruction q of this wave: kind, the lane's global source at the split's
         // first K, the bytes it advances per K step, and the wave's LDS offset in a stage
-        const char *src[C::LPW];
-        int dst[C::LPW], kind[C::LPW], step[C::LPW];
+        uint32_t voff[C::LPW];
+        int dst[C::LPW], kind[C::LPW];
         bool on[C::LPW];   // lane loads (filler rows of A are skipped, as in gemm_pipe.hip)
 #pragma unroll
         for (int q = 0; q < C::LPW; q++) {
@@ -119,42 +119,49 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                 const int p = a.sorted[row0 + r];
                 const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + r;
                 on[q] = !C::SKIP_FILLER || p < a.pairs || (lane >> 3) == 0;
-                src[q] = (const char *)a.A + (arow * a.lda + (int64_t)s * a.ksplit) * 2 + slab * 128 + chunk * 16;
+                voff[q] = (uint32_t)(arow * a.lda * 2 + slab * 128 + chunk * 16);
                 dst[q] = (slab * C::BM + rb) * 128;
                 kind[q] = LD_A;
-                step[q] = C::A_SLABS * 128;
             } else if (ins < C::A_LOADS + C::B_LOADS) {
                 const int rb = (ins - C::A_LOADS) * 8;
                 const int rr = rb + (lane >> 3);
                 const int chunk = (lane & 7) ^ swz(rr);
-                src[q] = (const char *)a.B + (int64_t)e * a.b_expert_stride + b_row(rr) * a.ldb +
-                         (int64_t)s * a.ksplit / 2 + chunk * 16;
+                voff[q] = (uint32_t)(b_row(rr) * a.ldb + chunk * 16);
                 dst[q] = C::A_STAGE + rb * 128;
                 kind[q] = LD_B;
-                step[q] = 128;
             } else {   // 64 rows' scale (or zero) pairs: 4 bytes per lane
                 const int j = ins - C::A_LOADS - C::B_LOADS;
                 const int which = j / (C::BN / 64), r0 = j % (C::BN / 64) * 64;
-                const uint16_t *base = which ? a.bz : a.bs;
-                src[q] = (const char *)(base + (int64_t)e * a.sz_expert_stride + b_row(r0 + lane) * groups_per_row +
-                                        (int64_t)s * a.ksplit / 128);
+                voff[q] = (uint32_t)(b_row(r0 + lane) * groups_per_row * 2);
                 dst[q] = C::A_STAGE + C::B_STAGE + which * C::SZ + r0 * 4;
-                kind[q] = LD_SZ;
-                step[q] = 4;
+                kind[q] = which ? LD_Z : LD_S;
             }
         }
         // weight streaming: each tile starts its K walk at its own step (see gemm_pipe.hip)
         const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
+        // operand bases at the split's first K (wave-uniform); a K step advances A by 512
+        // bytes (256 fp16), B by 128 (256 nibbles), scales and zeros by 4 (two groups)
+        const char *base_a = uniform_ptr((const char *)a.A + (int64_t)s * a.ksplit * 2);
+        const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + (int64_t)s * a.ksplit / 2);
+        const char *base_s = uniform_ptr((const char *)(a.bs + (int64_t)e * a.sz_expert_stride + (int64_t)s * a.ksplit / 128));
+        const char *base_z = uniform_ptr((const char *)(a.bz + (int64_t)e * a.sz_expert_stride + (int64_t)s * a.ksplit / 128));
+        const char *qbase[C::LPW];
+        int qstep[C::LPW];
+#pragma unroll
+        for (int q = 0; q < C::LPW; q++) {
+            qbase[q] = kind[q] == LD_A ? base_a : kind[q] == LD_B ? base_b : kind[q] == LD_S ? base_s : base_z;
+            qstep[q] = kind[q] == LD_A ? C::A_SLABS * 128 : kind[q] == LD_B ? 128 : 4;
+        }
         auto issue = [&](int kstep) {
             const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
-            const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
+            const int kr = __builtin_amdgcn_readfirstlane(kstep + krot < nk ? kstep + krot : kstep + krot - nk);
 #pragma unroll
             for (int q = 0; q < C::LPW; q++) {
-                const char *g = src[q] + (int64_t)kr * step[q];
-                if (kind[q] == LD_SZ)
-                    lds_dma<4>(g, st + dst[q]);
+                const char *g = qbase[q] + (int64_t)kr * qstep[q];
+                if (kind[q] >= LD_S)
+                    lds_dma_off<4>(g, voff[q], st + dst[q]);
                 else if (on[q])
-                    lds_dma<16>(g, st + dst[q]);
+                    lds_dma_off<16>(g, voff[q], st + dst[q]);
             }
         };
 

@@ -71,19 +71,21 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
         const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
         const int s = tc.s, mb = tc.mb, nt = tc.nt;
-        const int e = a.eids[mb];
+        const int e = __builtin_amdgcn_readfirstlane(a.eids[mb]);
         const int row0 = mb * C::BM;
         const int64_t kb = (int64_t)s * a.ksplit * ebytes;     // byte offset of this split's K
 
-        // per load instruction q of this wave: the lane's global source (at K = 0 of the
-        // split) and the wave's LDS destination offset inside a stage
-        const char *src[C::LPW];
+        // per load instruction q of this wave: operand (A or B), the lane's byte offset from
+        // the operand's base at the split's first K, and the wave's LDS offset in a stage
+        uint32_t voff[C::LPW];
         int dst[C::LPW];
+        bool is_a[C::LPW];
         bool on[C::LPW];   // lane loads (filler rows of A are skipped, see below)
 #pragma unroll
         for (int q = 0; q < C::LPW; q++) {
             on[q] = true;
             const int ins = wave + q * C::NW;
+            is_a[q] = ins < C::A_LOADS;
             if (ins < C::A_LOADS) {
                 const int slab = ins / (C::BM / C::RPI), rb = ins % (C::BM / C::RPI) * C::RPI;
                 int r, chunk;
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 // data; the lanes of the instruction's first row always load, so every load
                 // instruction runs with a non-empty mask and counts in vmcnt
                 on[q] = !C::SKIP_FILLER || p < a.pairs || (lane >> 3) == 0;
-                src[q] = (const char *)a.A + arow * a.lda * ebytes + kb + slab * C::SB + chunk * 16;
+                voff[q] = (uint32_t)(arow * a.lda * ebytes + slab * C::SB + chunk * 16);
                 dst[q] = (slab * C::BM + rb) * C::SB;
             } else {
                 const int j = ins - C::A_LOADS;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 } else {
                     grow = (int64_t)nt * C::BN + rr;
                 }
-                src[q] = (const char *)a.B + (int64_t)e * a.b_expert_stride + grow * a.ldb + kb + slab * C::SB + chunk * 16;
+                voff[q] = (uint32_t)(grow * a.ldb + slab * C::SB + chunk * 16);
                 dst[q] = C::A_STAGE + (slab * C::BN + rb) * C::SB;
             }
         }
@@ -119,14 +121,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         // address bits; tiles that share A or B rows keep K in step for L2 reuse.  The
         // order is fixed per tile, so results stay reproducible.
         const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
+        const char *base_a = uniform_ptr((const char *)a.A + kb);
+        const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + kb);
         auto issue = [&](int kstep) {
             const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
-            const int kr = kstep + krot < nk ? kstep + krot : kstep + krot - nk;
+            const int kr = __builtin_amdgcn_readfirstlane(kstep + krot < nk ? kstep + krot : kstep + krot - nk);
             const int64_t koff = (int64_t)kr * C::KS * C::SB;
 #pragma unroll
             for (int q = 0; q < C::LPW; q++)
                 if (on[q])
-                    lds_dma<16>(src[q] + koff, st + dst[q]);
+                    lds_dma_off<16>((is_a[q] ? base_a : base_b) + koff, voff[q], st + dst[q]);
         };
 
         using Acc = typename AccOf<C::MS>::type;
@@ -330,7 +334,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     X(33, 256, 256, 1, 5, 4, 4, 16, 64)  \
     X(34, 256, 256, 1, 5, 2, 4, 32, 64)  \
     X(35, 256, 128, 1, 5, 4, 2, 32, 64)  \
-    X(36, 128, 256, 1, 5, 2, 4, 32, 64)
+    X(36, 128, 256, 1, 5, 2, 4, 32, 64)  \
+    X(37, 256, 128, 1, 3, 4, 4, 16, 128)
 #define PIPE_FP8_TILES(X)               \
     X(7, 128, 256, 1, 3, 2, 2, 16, 128)      \
     X(8, 128, 128, 1, 4, 2, 2, 16, 128)      \

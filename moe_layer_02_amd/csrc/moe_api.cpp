@@ -200,6 +200,9 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     if (!aligned(logits, L->route.logits_dtype == MOE_DT_BF16 ? 2 : 4)) return MOE_ERR_INVALID_ARGUMENT;
     const Workspace w = layout(L, T, &plan);
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    // the GEMMs address A rows with 32-bit byte offsets from the operand's base
+    if ((int64_t)T * L->H * 2 > (int64_t)UINT32_MAX || w.cap * (int64_t)L->I * 2 > (int64_t)UINT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
 
     char *ws = (char *)workspace;
     int32_t *ids = (int32_t *)(ws + w.ids), *sorted = (int32_t *)(ws + w.sorted);

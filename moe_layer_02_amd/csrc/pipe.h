@@ -34,6 +34,27 @@ __device__ __forceinline__ void lds_dma(const void *g, uint32_t lds) {
     else
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
+
+// A wave-uniform pointer as the compiler's uniform (SGPR) value.
+template <class T>
+__device__ __forceinline__ const T *uniform_ptr(const T *p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return (const T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The same load with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane byte offset:
+// one VGPR per load instead of a 64-bit address, and advancing the base is scalar work.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma_off(const void *base, uint32_t voff, uint32_t lds) {
+    static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+    const void *sb = uniform_ptr((const char *)base);
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb), "s"(m) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <int N>
