@@ -142,7 +142,9 @@ typedef struct {
 /* Steps of moe_forward, for moe_forward_profiled. */
 typedef enum {
     MOE_STAGE_ROUTE = 0, MOE_STAGE_ALIGN = 1, MOE_STAGE_ACT_QUANT = 2, MOE_STAGE_GEMM1 = 3,
-    MOE_STAGE_H_QUANT = 4, MOE_STAGE_GEMM2 = 5, MOE_STAGE_REDUCE = 6, MOE_STAGE_COUNT = 7
+    MOE_STAGE_H_QUANT = 4, MOE_STAGE_GEMM2 = 5, MOE_STAGE_REDUCE = 6,
+    MOE_STAGE_PROLOGUE = 7,   /* T <= 16: route, align and the activation pass in one launch */
+    MOE_STAGE_COUNT = 8
 } moe_stage;
 
 /* Static text for a status code [host]. */

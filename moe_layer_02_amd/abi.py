@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 ROUTE_SOFTMAX, ROUTE_SIGMOID, ROUTE_GROUPED_SIGMOID_BIAS = 0, 1, 2
 DT_BF16, DT_FP32, DT_FP8_E4M3, DT_INT4_G128 = 0, 1, 2, 3
-STAGES = ("route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce")
+STAGES = ("route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce", "prologue")
 STAGE_COUNT = len(STAGES)
 WS_REGIONS = ("topk_ids", "topk_weights", "sorted_ids", "expert_ids", "num_post_pad", "expert_counts",
               "inv_pos", "scalars", "x_q", "h", "h_q", "y", "align_scratch")

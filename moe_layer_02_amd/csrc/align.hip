@@ -13,8 +13,7 @@
 // histograms every chunk in parallel, k_align_scan (one workgroup) turns the histograms
 // into per-chunk write offsets, and k_align_scatter ranks and writes every chunk in
 // parallel -- the same stable order, so both paths produce identical outputs.
-#include "common.h"
-#include "kernels.h"
+#include "align_dev.h"
 
 namespace moe {
 
@@ -22,146 +21,9 @@ constexpr int64_t kOneGroupPairs = 4096;   // up to this many pairs: the one-wor
 
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kMaxE = 256;
+using namespace align_dev;
 
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(v, off, kWave);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
-
-// Lanes of the wave holding the same expert as this lane (only lanes with valid set).
-__device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; b++) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bal = __ballot(valid && bit);
-        same &= bit ? bal : ~bal;
-    }
-    return same;
-}
-
-// Count the pairs [beg, end) per expert into hist (LDS): per 64-pair piece, the lowest lane
-// of each group of equal experts adds the group's size (no atomic contention per expert).
-__device__ __forceinline__ void count_range(const int32_t *ids, int beg, int end, int E, int nbits, int *hist) {
-    const int lane = lane_id();
-    for (int base = beg; base < end; base += kWave) {
-        const int i = base + lane;
-        int e = i < end ? ids[i] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;   // other ids are dropped
-        if (!valid) e = 0;
-        const uint64_t same = match_mask(e, valid, nbits);
-        if (valid && (same & lanemask_lt()) == 0) atomicAdd(&hist[e], __popcll(same));
-    }
-}
-
-// Scatter the pairs [beg, end) in order; cursor[e] (LDS) is the next row of expert e for
-// this wave and advances by each piece's group sizes.
-__device__ __forceinline__ void scatter_range(const int32_t *ids, int beg, int end, int E, int nbits,
-                                              volatile int *cursor, int32_t *sorted, int32_t *inv_pos) {
-    const int lane = lane_id();
-    for (int base = beg; base < end; base += kWave) {
-        const int i = base + lane;
-        int e = i < end ? ids[i] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;
-        if (!valid) {
-            if (i < end) inv_pos[i] = -1;
-            e = 0;
-        }
-        const uint64_t same = match_mask(e, valid, nbits);
-        if (valid) {
-            const int rank = __popcll(same & lanemask_lt());
-            const int cnt = __popcll(same);
-            const int pos = cursor[e] + rank;
-            sorted[pos] = i;
-            inv_pos[i] = pos;
-            if (rank == cnt - 1) cursor[e] = pos + 1;
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
-// Exclusive scan of off_s[0..E) (padded counts) by wave 0; off_s[kMaxE] = total.
-__device__ __forceinline__ void scan_experts(int *off_s, int E) {
-    if (threadIdx.x >= kWave) return;
-    const int lane = lane_id();
-    int v[4], sum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const int e = lane * 4 + q;
-        v[q] = e < E ? off_s[e] : 0;
-        sum += v[q];
-    }
-    const int incl = wave_inclusive_scan(sum);
-    int run = incl - sum;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const int e = lane * 4 + q;
-        if (e < E) off_s[e] = run;
-        run += v[q];
-    }
-    if (lane == kWave - 1) off_s[kMaxE] = incl;
-}
-
-// expert_ids for every block: the last expert whose first row is at or before the block's
-// first row owns it (experts with no rows share their successor's offset).
-__device__ __forceinline__ void write_block_experts(const int *off_s, int E, int BM, int64_t cap, int total,
-                                                    int32_t *eids) {
-    for (int64_t b = threadIdx.x; b < cap / BM; b += blockDim.x) {
-        const int64_t r = b * BM;
-        int e = -1;
-        if (r < total) {
-            int lo = 0, hi = E - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off_s[mid] <= r) lo = mid; else hi = mid - 1;
-            }
-            e = lo;
-        }
-        eids[b] = e;
-    }
-}
-
-__global__ __launch_bounds__(1024) void k_align(AlignArgs a) {
-    __shared__ int hist[kWaves][kMaxE];   // per-wave counts, then per-wave write cursors
-    __shared__ int off_s[kMaxE + 1];
-    const int tid = threadIdx.x, w = tid >> 6;
-    const int P = a.T * a.k, E = a.E, BM = a.BM;
-
-    for (int i = tid; i < kWaves * kMaxE; i += 1024) hist[i / kMaxE][i % kMaxE] = 0;
-    for (int64_t r = tid; r < a.cap; r += 1024) a.sorted[r] = P;
-    __syncthreads();
-    // each wave owns a contiguous segment of pairs, a multiple of 64 long
-    const int seg = (P + kWaves * kWave - 1) / (kWaves * kWave) * kWave;
-    const int beg = min(P, w * seg), end = min(P, beg + seg);
-    count_range(a.ids, beg, end, E, a.nbits, hist[w]);
-    __syncthreads();
-    if (tid < E) {
-        int run = 0;
-        for (int ww = 0; ww < kWaves; ww++) {
-            const int c = hist[ww][tid];
-            hist[ww][tid] = run;   // pairs of this expert in earlier waves
-            run += c;
-        }
-        a.counts[tid] = run;
-        off_s[tid] = (run + BM - 1) / BM * BM;
-    }
-    __syncthreads();
-    scan_experts(off_s, E);
-    __syncthreads();
-    const int total = off_s[kMaxE];
-    if (tid == 0) *a.npp = total;
-    if (tid < E)
-        for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += off_s[tid];
-    write_block_experts(off_s, E, BM, a.cap, total, a.eids);
-    __syncthreads();
-    scatter_range(a.ids, beg, end, E, a.nbits, hist[w], a.sorted, a.inv_pos);
-}
+__global__ __launch_bounds__(1024) void k_align(AlignArgs a) { align_group(a); }
 
 // ---- the multi-workgroup path -------------------------------------------------------------
 

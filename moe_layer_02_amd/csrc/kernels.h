@@ -116,6 +116,25 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 // bf16 [n8 * 8] -> fp16 with each group of 8 reordered (0,4,1,5,2,6,3,7) (int4 GEMM1's A)
 hipError_t launch_f16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream_t s);
 
+// Route + align (+ the activation pass) of a batch of at most kPrologueMaxT tokens in one
+// launch (prologue.hip); results identical to launch_route, launch_align and the fp8 /
+// fp16 activation kernels.
+constexpr int kPrologueMaxT = 16;
+enum { PROLOGUE_ACT_NONE = 0, PROLOGUE_ACT_FP8 = 1, PROLOGUE_ACT_F16_PERM = 2 };
+struct PrologueArgs {
+    RouteArgs route;             // zero_ptr unused
+    AlignArgs align;             // ids = route.ids
+    int act;                     // PROLOGUE_ACT_*
+    const uint16_t *x;           // bf16 hidden [n]
+    int64_t n;                   // T * H
+    uint8_t *xq;                 // fp8: codes [n]
+    uint16_t *x16;               // int4: fp16 [n] in the packed-nibble order
+    uint32_t *x_amax;            // fp8: |x| max as float bits
+    float *x_scale;              // fp8: amax / 448 (1 when amax is 0)
+    uint32_t *h_amax;            // cleared to 0 (GEMM1's |h| maximum), may be null
+};
+hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s);
+
 int device_cu_count();
 
 }  // namespace moe

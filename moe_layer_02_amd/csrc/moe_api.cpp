@@ -222,35 +222,53 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     auto fail = [&](hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; };
     hipError_t err;
 
-    // 1. route (its first workgroup also clears the scratch words)
-    if ((err = mark(MOE_STAGE_ROUTE)) != hipSuccess) return MOE_ERR_HIP;
     RouteArgs ra = route_args(&L->route, T, logits, L->correction_bias, ids, topk_w);
-    ra.zero_ptr = scal;
-    ra.zero_n = kScalarWords;
-    if ((err = launch_route(ra, stream)) != hipSuccess) return fail(err);
-
-    // 2. align
-    if ((err = mark(MOE_STAGE_ALIGN)) != hipSuccess) return MOE_ERR_HIP;
     AlignArgs aa{T, k, E, plan.block_m, nbits_for(E), w.cap, ids, sorted, eids, npp, counts, inv_pos};
-    int32_t *align_scratch = align_scratch_bytes(pairs, E) ? (int32_t *)(ws + w.align_scratch) : nullptr;
-    if ((err = launch_align(aa, align_scratch, stream)) != hipSuccess) return fail(err);
-
-    // 3. fp8: quantise the hidden states with one dynamic scale
     const void *a1 = hidden;
-    if (fp8) {
-        if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-        AbsmaxArgs ab{(const uint16_t *)hidden, (int64_t)T * H, &scal[0]};
-        if ((err = launch_absmax(ab, stream)) != hipSuccess) return fail(err);
-        QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs};
-        if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
-        a1 = ws + w.xq;
-    } else if (f16_activations(L, &plan)) {
-        // int4: the hidden states as fp16 in the order the kernel dequantises nibbles
-        if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-        if ((err = launch_f16_perm((const uint16_t *)hidden, (uint16_t *)(ws + w.xq), (int64_t)T * H / 8, stream)) !=
-            hipSuccess)
-            return fail(err);
-        a1 = ws + w.xq;
+    if (T <= kPrologueMaxT) {
+        // 1-3 in one launch for a small batch
+        if ((err = mark(MOE_STAGE_PROLOGUE)) != hipSuccess) return MOE_ERR_HIP;
+        PrologueArgs pa{};
+        pa.route = ra;
+        pa.align = aa;
+        pa.act = fp8 ? PROLOGUE_ACT_FP8 : f16_activations(L, &plan) ? PROLOGUE_ACT_F16_PERM : PROLOGUE_ACT_NONE;
+        pa.x = (const uint16_t *)hidden;
+        pa.n = (int64_t)T * H;
+        pa.xq = (uint8_t *)(ws + w.xq);
+        pa.x16 = (uint16_t *)(ws + w.xq);
+        pa.x_amax = &scal[0];
+        pa.x_scale = (float *)&scal[2];
+        pa.h_amax = &scal[1];
+        if ((err = launch_prologue(pa, stream)) != hipSuccess) return fail(err);
+        if (pa.act != PROLOGUE_ACT_NONE) a1 = ws + w.xq;
+    } else {
+        // 1. route (its first workgroup also clears the scratch words)
+        if ((err = mark(MOE_STAGE_ROUTE)) != hipSuccess) return MOE_ERR_HIP;
+        ra.zero_ptr = scal;
+        ra.zero_n = kScalarWords;
+        if ((err = launch_route(ra, stream)) != hipSuccess) return fail(err);
+
+        // 2. align
+        if ((err = mark(MOE_STAGE_ALIGN)) != hipSuccess) return MOE_ERR_HIP;
+        int32_t *align_scratch = align_scratch_bytes(pairs, E) ? (int32_t *)(ws + w.align_scratch) : nullptr;
+        if ((err = launch_align(aa, align_scratch, stream)) != hipSuccess) return fail(err);
+
+        // 3. fp8: quantise the hidden states with one dynamic scale
+        if (fp8) {
+            if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
+            AbsmaxArgs ab{(const uint16_t *)hidden, (int64_t)T * H, &scal[0]};
+            if ((err = launch_absmax(ab, stream)) != hipSuccess) return fail(err);
+            QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs};
+            if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
+            a1 = ws + w.xq;
+        } else if (f16_activations(L, &plan)) {
+            // int4: the hidden states as fp16 in the order the kernel dequantises nibbles
+            if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
+            if ((err = launch_f16_perm((const uint16_t *)hidden, (uint16_t *)(ws + w.xq), (int64_t)T * H / 8, stream)) !=
+                hipSuccess)
+                return fail(err);
+            a1 = ws + w.xq;
+        }
     }
 
     // 4. GEMM1: gate/up with SiLU * up

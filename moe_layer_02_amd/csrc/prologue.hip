@@ -1,0 +1,86 @@
+// prologue.hip -- route, align and the activation pass of a small batch in one launch.
+//
+// With a handful of tokens each of these steps is a few microseconds of launch and memory
+// latency, comparable to the whole weight-streaming time of a small layer.  One launch of
+// up to two 1024-thread workgroups does them all, with the same results as the separate
+// kernels:
+//   workgroup 0: wave w routes token w (route_dev.h), a barrier makes the pairs visible,
+//                then the one-workgroup align (align_dev.h) lays them out;
+//   workgroup 1: the activation pass, independent of the routing --
+//                fp8: the largest |x| over the batch (reduced inside the workgroup, no
+//                atomics), then every code with that scale (quant_dev.h), and the scale;
+//                int4: the hidden states to fp16 in the packed-nibble order.
+#include "align_dev.h"
+#include "kernels.h"
+#include "quant_dev.h"
+#include "route_dev.h"
+
+namespace moe {
+namespace {
+
+template <int EPL>
+__global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0 && p.h_amax) *p.h_amax = 0u;   // GEMM1's |h| maximum starts at 0
+        const int w = threadIdx.x >> 6;
+        if (w < p.route.T) route_dev::route_token<EPL>(p.route, w);
+        __syncthreads();
+        align_dev::align_group(p.align);
+        return;
+    }
+    const int64_t n8 = p.n / 8;
+    const int tid = threadIdx.x;
+    if (p.act == PROLOGUE_ACT_F16_PERM) {
+        for (int64_t i = tid; i < n8; i += 1024) ((uint4 *)p.x16)[i] = bf16x8_to_f16x8_perm(((const uint4 *)p.x)[i]);
+        return;
+    }
+    // fp8: amax over the batch
+    float m = 0.0f;
+    for (int64_t i = tid; i < n8; i += 1024) {
+        const uint4 v = ((const uint4 *)p.x)[i];
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            m = fmaxf(m, fabsf(__uint_as_float(wv[q] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(wv[q] & 0xFFFF0000u)));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    __shared__ float wmax[16];
+    if (lane_id() == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, wmax[i]);
+    float scale, inv;
+    quant_dev::scales_from_amax(__float_as_uint(amax), &scale, &inv);
+    if (tid == 0) {
+        *p.x_amax = __float_as_uint(amax);
+        *p.x_scale = scale;
+    }
+    for (int64_t i = tid; i < n8; i += 1024) {
+        const uint4 v = ((const uint4 *)p.x)[i];
+        uint2 out;
+        out.x = quant_dev::e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u), inv);
+        out.y = quant_dev::e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                                  __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u), inv);
+        ((uint2 *)p.xq)[i] = out;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s) {
+    const dim3 grid(p.act == PROLOGUE_ACT_NONE ? 1 : 2), block(1024);
+    if (p.route.E <= 64)
+        hipLaunchKernelGGL(k_prologue<1>, grid, block, 0, s, p);
+    else if (p.route.E <= 128)
+        hipLaunchKernelGGL(k_prologue<2>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(k_prologue<4>, grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -10,9 +10,12 @@
 //           block 0 publishes scale = amax / 448 (1 when amax is 0) for the GEMM epilogue.
 #include "common.h"
 #include "kernels.h"
+#include "quant_dev.h"
 
 namespace moe {
 namespace {
+
+using namespace quant_dev;
 
 __global__ __launch_bounds__(256) void k_absmax(AbsmaxArgs a) {
     float m = 0.0f;
@@ -34,27 +37,6 @@ __global__ __launch_bounds__(256) void k_absmax(AbsmaxArgs a) {
     __syncthreads();
     if (threadIdx.x == 0)
         atomicMax(a.amax, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
-}
-
-__device__ __forceinline__ void scales_from_amax(uint32_t bits, float *scale, float *inv) {
-    const float amax = __uint_as_float(bits);
-    if (amax == 0.0f) {
-        *scale = 1.0f;
-        *inv = 1.0f;
-    } else {
-        *scale = amax / 448.0f;   // IEEE division: the same rounding on every side
-        *inv = 448.0f / amax;
-    }
-}
-
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float inv) {
-    const float lim = 448.0f;
-    a = fminf(fmaxf(a * inv, -lim), lim);
-    b = fminf(fmaxf(b * inv, -lim), lim);
-    c = fminf(fmaxf(c * inv, -lim), lim);
-    d = fminf(fmaxf(d * inv, -lim), lim);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // 8 elements (bf16 or fp32) per thread -> 8 codes (one 8-byte store)

@@ -202,10 +202,11 @@ def test_qwen2_fp8(T):
     check_full("qwen2", T)
 
 
-def test_qwen2_fp8_activation_codes_exact():
-    """The hidden states' E4M3 codes are decided in fp32 on both sides: bit-exact."""
+@pytest.mark.parametrize("T", [16, 40])
+def test_qwen2_fp8_activation_codes_exact(T):
+    """The hidden states' E4M3 codes are decided in fp32 on both sides: bit-exact (T=16:
+    the one-launch prologue; T=40: the separate absmax and quantisation kernels)."""
     c = case("qwen2")
-    T = 16
     out, ws = c.gpu(T)
     plan = c.layer.plan(T)
     x, _ = c.inputs(T)
@@ -323,6 +324,29 @@ def test_graph_replay_matches_eager(name, T):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "replay %d" % i
+
+
+@pytest.mark.parametrize("name,T,expect", [
+    ("qwen2", 1, ["prologue", "gemm1", "h_quant", "gemm2", "reduce"]),
+    ("qwen2", 16, ["prologue", "gemm1", "h_quant", "gemm2", "reduce"]),
+    ("qwen2", 17, ["route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce"]),
+    ("deepseek", 3, ["prologue", "gemm1", "gemm2", "reduce"])])
+def test_small_batch_prologue(name, T, expect):
+    """Up to 16 tokens, route, align and the activation pass run as one launch; the
+    forward's routing and align results stay bit-exact and the output within tolerance."""
+    c = case(name)
+    x, lg = c.inputs(T)
+    plan = c.layer.plan(T)
+    ws = c.layer.workspace(T, plan)
+    out = torch.empty((T, c.cfg.H), dtype=torch.bfloat16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
+    say("profiled forward", name, "T=%d" % T)
+    stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), out, ws, ev, plan)
+    torch.cuda.synchronize()
+    assert stages == expect
+    ref, _, _ = c.oracle(T)
+    assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype]
+    check_intermediates(c, T, plan, ws)
 
 
 def test_profiled_forward_records_every_stage():
