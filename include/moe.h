@@ -129,14 +129,18 @@ typedef struct {
  * align block height and the GEMM tile height; gemm1_tile / gemm2_tile index the tile
  * shapes compiled for the layer's weight type (moe_plan_describe lists them); split_k
  * splits GEMM2's reduction into that many fp32 partial sums, combined in a fixed order by
- * the reduce step.  moe_default_plan picks one per T; any valid plan gives results equal
- * within rounding (and bitwise reproducible for a fixed plan).
+ * the reduce step; split_k1 (0 or 1: none) splits GEMM1's likewise -- fp32 partial sums of
+ * the gate and up projections that a finishing pass adds in a fixed order before SiLU * up
+ * (tiles with block_m <= 32 only: the small-T case, where it multiplies the number of
+ * workgroups streaming weights).  moe_default_plan picks one per T; any valid plan gives
+ * results equal within rounding (and bitwise reproducible for a fixed plan).
  */
 typedef struct {
     int32_t block_m;
     int32_t gemm1_tile;
     int32_t gemm2_tile;
     int32_t split_k;
+    int32_t split_k1;
 } moe_plan;
 
 /* Steps of moe_forward, for moe_forward_profiled. */
@@ -144,7 +148,8 @@ typedef enum {
     MOE_STAGE_ROUTE = 0, MOE_STAGE_ALIGN = 1, MOE_STAGE_ACT_QUANT = 2, MOE_STAGE_GEMM1 = 3,
     MOE_STAGE_H_QUANT = 4, MOE_STAGE_GEMM2 = 5, MOE_STAGE_REDUCE = 6,
     MOE_STAGE_PROLOGUE = 7,   /* T <= 16: route, align and the activation pass in one launch */
-    MOE_STAGE_COUNT = 8
+    MOE_STAGE_GEMM1_FINISH = 8, /* split_k1 > 1: sum of GEMM1's partials, SiLU * up      */
+    MOE_STAGE_COUNT = 9
 } moe_stage;
 
 /* Static text for a status code [host]. */
@@ -245,7 +250,9 @@ typedef enum {
                                  fp32 [split_k, capacity, H] partial sums             */
     MOE_WS_ALIGN_SCRATCH = 12, /* int32 per-chunk expert histograms of the chunked align
                                   (T*k > 4096 only)                                   */
-    MOE_WS_COUNT = 13
+    MOE_WS_GEMM1_PARTIALS = 13, /* split_k1 > 1: fp32 [split_k1, capacity, 2I] gate (columns
+                                   [0, I)) and up ([I, 2I)) partial sums              */
+    MOE_WS_COUNT = 14
 } moe_ws_region;
 
 /* Byte offset of each moe_ws_region in the workspace of moe_forward(layer, T, plan) into

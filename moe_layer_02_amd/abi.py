@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 ROUTE_SOFTMAX, ROUTE_SIGMOID, ROUTE_GROUPED_SIGMOID_BIAS = 0, 1, 2
 DT_BF16, DT_FP32, DT_FP8_E4M3, DT_INT4_G128 = 0, 1, 2, 3
-STAGES = ("route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce", "prologue")
+STAGES = ("route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce", "prologue", "gemm1_finish")
 STAGE_COUNT = len(STAGES)
 WS_REGIONS = ("topk_ids", "topk_weights", "sorted_ids", "expert_ids", "num_post_pad", "expert_counts",
-              "inv_pos", "scalars", "x_q", "h", "h_q", "y", "align_scratch")
+              "inv_pos", "scalars", "x_q", "h", "h_q", "y", "align_scratch", "gemm1_partials")
 
 # every function include/moe.h declares (checked against the header by the tests)
 EXPORTS = ("moe_status_str", "moe_align_capacity", "moe_route", "moe_align", "moe_default_plan",
@@ -53,10 +53,11 @@ class Layer(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("gemm1_tile", ctypes.c_int32), ("gemm2_tile", ctypes.c_int32),
-                ("split_k", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("split_k1", ctypes.c_int32)]
 
     def as_tuple(self):
-        return (self.block_m, self.gemm1_tile, self.gemm2_tile, self.split_k)
+        t = (self.block_m, self.gemm1_tile, self.gemm2_tile, self.split_k)
+        return t + (self.split_k1,) if self.split_k1 > 1 else t
 
 
 _lib = None

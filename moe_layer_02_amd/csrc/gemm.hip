@@ -301,7 +301,24 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
         // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 fragment ----
         float scale = 1.0f;
         if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
-        if constexpr (KIND == GEMM_GATE_UP) {
+        if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
+            // split K: this split's gate and up sums in fp32 (the finishing pass adds the
+            // splits in order and applies SiLU * up); filler rows are left out
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int row = row0 + wm * C::TM + fm * 16 + 4 * (lane >> 4) + i;
+                    if (a.sorted[row] >= a.pairs) continue;
+                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
+                        P[col] = acc[fm][f][i] * scale;
+                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
+                    }
+                }
+        } else if constexpr (KIND == GEMM_GATE_UP) {
             float amax = 0.0f;
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
                         if constexpr (WT == WT_FP8) {   // fp32: its E4M3 code is decided in fp32
                             ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
-                            amax = fmaxf(amax, fabsf(hv));
+                            if (a.sorted[row] < a.pairs) amax = fmaxf(amax, fabsf(hv));   // valid rows only
                         } else {
                             ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
                         }
@@ -400,7 +417,11 @@ hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
 
 template <class C, int WT>
 hipError_t launch_kind(GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
-    if (kind == GEMM_GATE_UP) return launch_one<C, WT, GEMM_GATE_UP, false>(a, max_tiles, s);
+    if (kind == GEMM_GATE_UP) {
+        if (!partial) return launch_one<C, WT, GEMM_GATE_UP, false>(a, max_tiles, s);
+        if constexpr (C::BM <= 32) return launch_one<C, WT, GEMM_GATE_UP, true>(a, max_tiles, s);
+        return hipErrorInvalidValue;   // GEMM1 split-K is built for the small-T tiles only
+    }
     if (partial) return launch_one<C, WT, GEMM_DOWN, true>(a, max_tiles, s);
     return launch_one<C, WT, GEMM_DOWN, false>(a, max_tiles, s);
 }

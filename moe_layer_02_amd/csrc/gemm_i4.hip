@@ -235,7 +235,25 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
         // ---- epilogue: accumulator value i of fragment (fm, fn) is row frag_row(lane, i),
         //      column lane % 16 of that fragment ----
         const int lcol = lane & 15;
-        if constexpr (KIND == GEMM_GATE_UP) {
+        if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
+            // split K: this split's gate and up sums in fp32, natural column order (the
+            // finishing pass adds the splits, applies SiLU * up and permutes); filler rows
+            // are left out
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int row = row0 + wm * C::TM + fm * 16 + frag_row<16>(lane, i);
+                    if (a.sorted[row] >= a.pairs) continue;
+                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + lcol;
+                        P[col] = acc[fm][f][i];
+                        P[a.I + col] = acc[fm][f + C::FN / 2][i];
+                    }
+                }
+        } else if constexpr (KIND == GEMM_GATE_UP) {
             // h = SiLU(gate) * up in fp16, columns in the permuted order GEMM2's A expects
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
@@ -312,7 +330,11 @@ hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
 
 template <class C>
 hipError_t launch_kind(GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
-    if (kind == GEMM_GATE_UP) return launch_one<C, GEMM_GATE_UP, false>(a, max_tiles, s);
+    if (kind == GEMM_GATE_UP) {
+        if (!partial) return launch_one<C, GEMM_GATE_UP, false>(a, max_tiles, s);
+        if constexpr (C::BM <= 32) return launch_one<C, GEMM_GATE_UP, true>(a, max_tiles, s);
+        return hipErrorInvalidValue;   // GEMM1 split-K is built for the small-T tiles only
+    }
     if (partial) return launch_one<C, GEMM_DOWN, true>(a, max_tiles, s);
     return launch_one<C, GEMM_DOWN, false>(a, max_tiles, s);
 }

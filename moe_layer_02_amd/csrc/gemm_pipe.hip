@@ -254,7 +254,24 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         float scale = 1.0f;
         if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
         const int lcol = lane & (C::MS - 1);
-        if constexpr (KIND == GEMM_GATE_UP) {
+        if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
+            // split K: this split's gate and up sums in fp32 (the finishing pass adds the
+            // splits in order and applies SiLU * up); filler rows are left out
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
+                    if (a.sorted[row] >= a.pairs) continue;
+                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
+                        P[col] = acc[fm][f][i] * scale;
+                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
+                    }
+                }
+        } else if constexpr (KIND == GEMM_GATE_UP) {
             float amax = 0.0f;
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
@@ -372,7 +389,11 @@ hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
 
 template <class C, int WT>
 hipError_t launch_kind(GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
-    if (kind == GEMM_GATE_UP) return launch_one<C, WT, GEMM_GATE_UP, false>(a, max_tiles, s);
+    if (kind == GEMM_GATE_UP) {
+        if (!partial) return launch_one<C, WT, GEMM_GATE_UP, false>(a, max_tiles, s);
+        if constexpr (C::BM <= 32) return launch_one<C, WT, GEMM_GATE_UP, true>(a, max_tiles, s);
+        return hipErrorInvalidValue;   // GEMM1 split-K is built for the small-T tiles only
+    }
     if (partial) return launch_one<C, WT, GEMM_DOWN, true>(a, max_tiles, s);
     return launch_one<C, WT, GEMM_DOWN, false>(a, max_tiles, s);
 }

@@ -92,6 +92,20 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
+// GEMM1 split-K finish: h from the split planes of gate/up sums (fp32 [split, cap, 2I]).
+enum { GATE_UP_H_BF16 = 0, GATE_UP_H_F32 = 1, GATE_UP_H_F16_PERM = 2 };
+struct GateUpFinishArgs {
+    const float *P;
+    int64_t plane;               // elements between split planes
+    int split, I;
+    const int32_t *sorted, *npp;
+    int pairs;
+    void *h;                     // [cap, I] in h_kind's format
+    int h_kind;                  // GATE_UP_H_*
+    uint32_t *amax;              // fp32 h: |h| max as float bits (atomicMax), may be null
+};
+hipError_t launch_gate_up_finish(const GateUpFinishArgs &a, int64_t max_rows, hipStream_t s);
+
 // fp8 activation quantisation
 struct AbsmaxArgs {
     const uint16_t *x;           // bf16

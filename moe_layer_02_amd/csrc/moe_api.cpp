@@ -88,6 +88,9 @@ moe_status check_layer(const moe_layer *L) {
     return MOE_OK;
 }
 
+// GEMM1's K splits (0 and 1 both mean none)
+int split1(const moe_plan *p) { return p->split_k1 > 1 ? p->split_k1 : 1; }
+
 // A plan is valid when both tiles exist for the weight type, share the block height, and
 // tile the layer's dimensions exactly.
 moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileInfo *t2) {
@@ -98,6 +101,10 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->block_m != t1->BM || p->block_m != t2->BM) return MOE_ERR_INVALID_ARGUMENT;
     if (p->split_k < 1 || p->split_k > 16) return MOE_ERR_INVALID_ARGUMENT;
+    const int s1 = split1(p);
+    if (p->split_k1 < 0 || s1 > 16) return MOE_ERR_INVALID_ARGUMENT;
+    // GEMM1 split K: the small-T tiles only, each split a whole number of K steps
+    if (s1 > 1 && (t1->BM > 32 || L->H % (t1->BK * s1))) return MOE_ERR_INVALID_ARGUMENT;
     // int4: the pipelined tiles pass h between the GEMMs as permuted fp16, the
     // register-staged ones as bf16, so both GEMMs must be of one kind
     if (wd == MOE_DT_INT4_G128 && (t1->stages > 0) != (t2->stages > 0)) return MOE_ERR_INVALID_ARGUMENT;
@@ -111,7 +118,7 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
 }
 
 struct Workspace {
-    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, total;
+    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, total;
     int64_t cap;
 };
 
@@ -154,6 +161,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.y = take(direct_output(L, p) ? 0
                : p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
     w.align_scratch = take((size_t)align_scratch_bytes(pairs, E));
+    w.g1p = take(split1(p) > 1 ? (size_t)split1(p) * w.cap * 2 * L->I * 4 : 0);
     w.total = o;
     return w;
 }
@@ -305,9 +313,25 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     // so stagger their K walks across DRAM channels
     g.rotate_k = (int64_t)pairs <= (int64_t)E * plan.block_m;
     const int64_t mblocks_max = w.cap / plan.block_m;
-    if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, false, g,
-                           mblocks_max * (I / (t1.BN / 2)), stream)) != hipSuccess)
+    const int s1 = split1(&plan);
+    if (s1 > 1) {   // fp32 partial planes of gate and up, finished below
+        g.C = ws + w.g1p;
+        g.ldc = 2 * (int64_t)I;
+        g.partial_stride = w.cap * 2 * (int64_t)I;
+        g.split = s1;
+        g.ksplit = H / s1;
+        g.amax_out = nullptr;
+    }
+    if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, s1 > 1, g, mblocks_max * (I / (t1.BN / 2)) * s1,
+                           stream)) != hipSuccess)
         return fail(err);
+    if (s1 > 1) {
+        if ((err = mark(MOE_STAGE_GEMM1_FINISH)) != hipSuccess) return MOE_ERR_HIP;
+        GateUpFinishArgs f{(const float *)(ws + w.g1p), w.cap * 2 * (int64_t)I, s1, I, sorted, npp, pairs, ws + w.h,
+                           fp8 ? GATE_UP_H_F32 : f16_activations(L, &plan) ? GATE_UP_H_F16_PERM : GATE_UP_H_BF16,
+                           fp8 ? &scal[1] : nullptr};
+        if ((err = launch_gate_up_finish(f, w.cap, stream)) != hipSuccess) return fail(err);
+    }
 
     // 5. fp8: quantise h with its dynamic scale
     const void *a2 = ws + w.h;
@@ -418,15 +442,17 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     // Plans by rows per expert r = T*k/E, from timing every valid plan of the Mixtral,
     // Llama-4-Scout, Qwen2 and DeepSeek-V3 shapes on MI355X (graph replays): each row is the
     // plan with the smallest worst-case slowdown over the measured points of its range
-    // (within 4% of the fastest plan at every point).  Small r streams weights (16-row
-    // blocks, narrow tiles, split-K for GEMM2); large r is MFMA work (256x256 tiles of 16
-    // waves).
-    struct Row { double r_max; int bm, g1, g2, split; };
-    static const Row bf16[] = {{1.5, 16, 9, 9, 4},     {8, 32, 19, 12, 1},    {24, 64, 18, 11, 1},
-                               {96, 128, 22, 22, 2},   {384, 256, 25, 25, 1}, {768, 256, 25, 25, 2},
-                               {1e30, 256, 25, 25, 1}};
-    static const Row fp8[] = {{8, 16, 9, 1, 1}, {48, 32, 11, 2, 1}, {192, 128, 7, 13, 1}, {1e30, 256, 12, 14, 1}};
-    static const Row int4[] = {{8, 16, 10, 11, 1}, {1e30, 32, 12, 12, 1}};
+    // (within 6% of the fastest plan at every point).  Small r streams weights (16-row
+    // blocks, narrow tiles, split-K for GEMM2, and for GEMM1 where an expert's I is small
+    // next to the GPU); large r is MFMA work (256x256 tiles of 16 waves).
+    struct Row { double r_max; int bm, g1, g2, split, split1; };
+    static const Row bf16[] = {{0.1, 16, 9, 9, 4, 1},      {0.3, 16, 10, 9, 4, 1},    {1.5, 16, 9, 9, 4, 1},
+                               {3, 16, 10, 9, 1, 1},       {8, 32, 19, 12, 1, 1},     {24, 64, 18, 11, 1, 1},
+                               {96, 128, 22, 22, 2, 1},    {384, 256, 25, 25, 1, 1},  {768, 256, 25, 25, 2, 1},
+                               {1e30, 256, 25, 25, 1, 1}};
+    static const Row fp8[] = {{0.25, 16, 9, 1, 1, 2},  {8, 16, 1, 1, 1, 2},        {48, 32, 11, 2, 1, 1},
+                              {192, 128, 7, 13, 1, 1}, {1e30, 256, 12, 14, 1, 1}};
+    static const Row int4[] = {{0.05, 16, 11, 11, 1, 2}, {8, 16, 11, 10, 1, 1}, {1e30, 32, 12, 12, 1, 1}};
     const Row *rows = bf16;
     int n = sizeof(bf16) / sizeof(Row);
     if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }
@@ -441,7 +467,8 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
         const int i = d % 2 == 0 ? first + d / 2 : first - (d + 1) / 2;
         if (i < 0 || i >= n) continue;
         for (int sk = rows[i].split; sk >= 1; sk /= 2) {
-            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk};
+            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk, rows[i].split1};
+            if (check_plan(layer, &p, &t1, &t2) != MOE_OK) p.split_k1 = 1;   // H not split that way
             if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
                 *plan = p;
                 return MOE_OK;
@@ -451,7 +478,7 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     // any valid plan (tiny or unusual shapes)
     for (int bm : {16, 32, 64, 128, 256})
         for (int g = 0; g < 40; g++) {
-            moe_plan p{bm, g, g, 1};
+            moe_plan p{bm, g, g, 1, 1};
             if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
                 *plan = p;
                 return MOE_OK;
@@ -496,9 +523,9 @@ moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *
     if ((st = check_plan(layer, plan, &t1, &t2)) != MOE_OK) return st;
     std::snprintf(buf, len,
                   "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d stages%d mfma%d] gemm2=%d[BM%d BN%d BK%d "
-                  "waves%dx%d stages%d mfma%d] split_k=%d",
+                  "waves%dx%d stages%d mfma%d] split_k=%d split_k1=%d",
                   plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, t1.stages, t1.mfma,
-                  plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k);
+                  plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k, split1(plan));
     return MOE_OK;
 }
 
@@ -513,7 +540,7 @@ moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_pl
     if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
     const Workspace w = layout(layer, T, &p);
     const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos,
-                                    w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch};
+                                    w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p};
     for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
     return MOE_OK;
 }

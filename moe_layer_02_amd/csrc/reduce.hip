@@ -6,7 +6,9 @@
 // owns 8 consecutive columns of one token and adds, for j = 0..k-1 and then split s =
 // 0..S-1, the row inv_pos[t*k + j] -- the same order on every run, so the result is bitwise
 // reproducible; SGLang PR #2333 ("[kernel] introduce fused_moe_triton_splitk", Background)
-// shows what an unordered atomic_add of the same partial sums did to the output.
+// shows what an unordered atomic_add of the same partial sums did to the output.  The same
+// file finishes a K-split GEMM1: its split planes of gate and up sums are added in a fixed
+// order before SiLU * up.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,7 +49,73 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     *(uint4 *)(a.out + t * a.H + col) = o;
 }
 
+// GEMM1 split K: h[r, c] = SiLU(sum_s G_s[r, c]) * sum_s U_s[r, c] over the split planes in
+// order s = 0, 1, ... (the same SiLU as the unsplit epilogue), 8 columns per thread, valid
+// rows only; fp32 h also folds its |h| maximum (one atomic per workgroup, max is exact).
+__global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
+    const int64_t c8 = a.I / 8;
+    const int64_t rows = *a.npp;
+    float m = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * c8; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / c8;
+        const int c = (int)(i % c8) * 8;
+        if (a.sorted[r] >= a.pairs) continue;
+        float g[8], u[8];
+        for (int s = 0; s < a.split; s++) {
+            const float *p = a.P + s * a.plane + r * 2 * (int64_t)a.I;
+            const float4 g0 = *(const float4 *)(p + c), g1 = *(const float4 *)(p + c + 4);
+            const float4 u0 = *(const float4 *)(p + a.I + c), u1 = *(const float4 *)(p + a.I + c + 4);
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                g[j] = s ? g[j] + gv[j] : gv[j];
+                u[j] = s ? u[j] + uv[j] : uv[j];
+            }
+        }
+        float h[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) h[j] = g[j] / (1.0f + __expf(-g[j])) * u[j];
+        if (a.h_kind == GATE_UP_H_F32) {
+            float *o = (float *)a.h + r * a.I + c;
+            *(float4 *)o = make_float4(h[0], h[1], h[2], h[3]);
+            *(float4 *)(o + 4) = make_float4(h[4], h[5], h[6], h[7]);
+#pragma unroll
+            for (int j = 0; j < 8; j++) m = fmaxf(m, fabsf(h[j]));
+        } else if (a.h_kind == GATE_UP_H_F16_PERM) {   // fp16, order (0,4,1,5,2,6,3,7) in the 8
+            const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h[perm[2 * q]]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h[perm[2 * q + 1]]) << 16);
+            *(uint4 *)((uint16_t *)a.h + r * a.I + c) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            *(uint4 *)((uint16_t *)a.h + r * a.I + c) =
+                make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                           pack_bf16x2(h[6], h[7]));
+        }
+    }
+    if (a.h_kind == GATE_UP_H_F32 && a.amax) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+        __shared__ float wmax[4];
+        if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) atomicMax(a.amax, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gate_up_finish(const GateUpFinishArgs &a, int64_t max_rows, hipStream_t s) {
+    int64_t blocks = (max_rows * (a.I / 8) + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_gate_up_finish, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s) {
     const int64_t threads = (int64_t)a.T * (a.H / 8);

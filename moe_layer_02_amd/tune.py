@@ -19,18 +19,20 @@ import torch
 from moe_layer_02_amd import abi, synth
 
 
-def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64, 128, 256), tiles=None):
+def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64, 128, 256), tiles=None,
+                split1=(1,)):
     out = []
     for bm in bms:
         for g1 in (tiles if tiles is not None else range(max_tile)):
             for g2 in (tiles if tiles is not None else range(max_tile)):
                 for sk in (1, 2, 4, 8):
-                    p = abi.Plan(bm, g1, g2, sk)
-                    try:
-                        abi.moe_workspace_bytes(layer.struct, T, p)
-                    except abi.MoEError:
-                        continue
-                    out.append(p)
+                    for s1 in split1:
+                        p = abi.Plan(bm, g1, g2, sk, s1)
+                        try:
+                            abi.moe_workspace_bytes(layer.struct, T, p)
+                        except abi.MoEError:
+                            continue
+                        out.append(p)
     return out
 
 
@@ -66,6 +68,7 @@ def main():
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--bm", default="16,32,64,128,256", help="block heights to try")
     ap.add_argument("--tiles", default=None, help="tile ids to try for both GEMMs (default: all)")
+    ap.add_argument("--split1", default="1", help="GEMM1 K splits to try (small-T tiles only)")
     args = ap.parse_args()
     cfg = synth.CONFIGS[args.config]
     w = synth.expert_weights(cfg, device="cuda")
@@ -83,7 +86,8 @@ def main():
         res = []
         bms = tuple(int(b) for b in args.bm.split(","))
         tiles = None if args.tiles is None else [int(t) for t in args.tiles.split(",")]
-        for p in valid_plans(layer, T, bms=bms, tiles=tiles):
+        split1 = tuple(int(v) for v in args.split1.split(","))
+        for p in valid_plans(layer, T, bms=bms, tiles=tiles, split1=split1):
             us = time_plan(layer, x, lg, T, p, args.reps)
             res.append((us, p.as_tuple()))
             print("[tune] %s T=%d plan=%s %.1f us" % (cfg.name, T, p.as_tuple(), us), file=sys.stderr, flush=True)

@@ -79,18 +79,19 @@ def workspace_view(layer, T, plan, ws, region, dtype, count):
     return ws[off:off + count * torch.tensor([], dtype=dtype).element_size()].view(dtype)
 
 
-def valid_plans(layer, T):
-    """Every (block_m, tile1, tile2, split) the library accepts for this layer."""
+def valid_plans(layer, T, split1=(1, 2, 4)):
+    """Every (block_m, tile1, tile2, split, split1) the library accepts for this layer."""
     n = 40
     out = []
     for g1 in range(n):
         for g2 in range(n):
             for sk in (1, 2, 4, 8):
-                for bm in (16, 32, 64, 128, 256):
-                    p = abi.Plan(bm, g1, g2, sk)
-                    try:
-                        abi.moe_workspace_bytes(layer.struct, T, p)
-                    except abi.MoEError:
-                        continue
-                    out.append(p)
+                for s1 in split1:
+                    for bm in (16, 32, 64, 128, 256):
+                        p = abi.Plan(bm, g1, g2, sk, s1)
+                        try:
+                            abi.moe_workspace_bytes(layer.struct, T, p)
+                        except abi.MoEError:
+                            continue
+                        out.append(p)
     return out

@@ -139,6 +139,27 @@ def test_int4_plans_keep_one_intermediate_format():
         abi.moe_default_plan(fake_layer(cfg, w13_s=0x10002), T)
 
 
+def test_gemm1_split_rules():
+    """GEMM1 K splits: 0 and 1 mean none; small-T tiles (block_m <= 32) only; each split a
+    whole number of K steps; the partial planes get their own workspace region."""
+    cfg = synth.CONFIGS["mixtral"]
+    layer = fake_layer(cfg)
+    T = 4
+    base = abi.moe_workspace_bytes(layer, T, abi.Plan(16, 9, 9, 1, 0))
+    assert base == abi.moe_workspace_bytes(layer, T, abi.Plan(16, 9, 9, 1, 1))
+    cap = abi.moe_align_capacity(T, cfg.k, cfg.E, 16)
+    assert abi.moe_workspace_bytes(layer, T, abi.Plan(16, 9, 9, 1, 4)) >= base + 4 * cap * 2 * cfg.I * 4
+    off = abi.moe_workspace_offsets(layer, T, abi.Plan(16, 9, 9, 1, 4))
+    assert off["gemm1_partials"] >= off["align_scratch"]
+    assert "split_k1=4" in abi.moe_plan_describe(layer, T, abi.Plan(16, 9, 9, 1, 4))
+    for bad in [abi.Plan(256, 25, 25, 1, 2),      # large tile
+                abi.Plan(16, 9, 9, 1, 3),         # 4096 / 3 is not a whole number of K steps
+                abi.Plan(16, 9, 9, 1, -1), abi.Plan(16, 9, 9, 1, 32)]:
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_workspace_bytes(layer, T, bad)
+        assert ei.value.status == abi.MOE_ERR_INVALID_ARGUMENT
+
+
 def test_invalid_layers_rejected():
     cfg = synth.CONFIGS["mixtral"]
     for layer in [fake_layer(cfg.with_shape(H=4000)),                     # H not a multiple of 128

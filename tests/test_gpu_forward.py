@@ -283,6 +283,27 @@ def test_int4_every_plan(T):
 
 # ---- properties ------------------------------------------------------------------------
 
+@pytest.mark.parametrize("name,T", [("mixtral", 1), ("qwen2", 3), ("deepseek", 2), ("scout", 5)])
+def test_gemm1_split_k(name, T):
+    """GEMM1 split into 2 and 4 K ranges (fp32 partial planes of gate and up, added in order
+    by the finishing pass) on the full-size layers: output within tolerance, routing and
+    align bit-exact, and the same output for a repeated call."""
+    c = case(name)
+    base = c.layer.plan(T)
+    ran = 0
+    for s1 in (2, 4, 7):
+        p = abi.Plan(base.block_m, base.gemm1_tile, base.gemm2_tile, base.split_k, s1)
+        try:
+            abi.moe_workspace_bytes(c.layer.struct, T, p)
+        except abi.MoEError:
+            continue                  # H is not a multiple of s1 K steps for this tile
+        out = check_full(name, T, p)
+        again, _ = c.gpu(T, p)
+        assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+        ran += 1
+    assert ran >= 2
+
+
 def test_deterministic_bitwise():
     c = case("mixtral")
     a, ws = c.gpu(64)
@@ -343,6 +364,8 @@ def test_small_batch_prologue(name, T, expect):
     say("profiled forward", name, "T=%d" % T)
     stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), out, ws, ev, plan)
     torch.cuda.synchronize()
+    if plan.split_k1 > 1:   # a K-split GEMM1 is followed by its finishing pass
+        expect = expect[:expect.index("gemm1") + 1] + ["gemm1_finish"] + expect[expect.index("gemm1") + 1:]
     assert stages == expect
     ref, _, _ = c.oracle(T)
     assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype]
@@ -358,7 +381,10 @@ def test_profiled_forward_records_every_stage():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
     stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), out, ws, ev)
     torch.cuda.synchronize()
-    assert stages == ["route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce"]
+    expect = ["route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce"]
+    if c.layer.plan(T).split_k1 > 1:
+        expect.insert(4, "gemm1_finish")
+    assert stages == expect
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(stages))]
     assert all(t >= 0 for t in times)
     ref, _, _ = c.oracle(T)
