@@ -24,30 +24,89 @@ __device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib)
     return ka > kb || (ka == kb && ia < ib);
 }
 
-// Butterfly arg-max over the wave; every lane ends with the winner and its payload.
-__device__ __forceinline__ void wave_argmax(float &key, int &idx, float &val) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ok = __shfl_xor(key, off, kWave);
-        const int oi = __shfl_xor(idx, off, kWave);
-        const float ov = __shfl_xor(val, off, kWave);
-        if (ranks_before(ok, oi, key, idx)) {
-            key = ok;
-            idx = oi;
-            val = ov;
-        }
+// Lane exchanges without LDS: step S pairs every lane with one partner so that steps
+// 0..g-1 combine all lanes of each aligned group of 2^g (g <= 6).  Steps 0-3 are DPP moves
+// (xor 1, xor 2, mirror within 8, mirror within 16); steps 4 and 5 are gfx950's
+// v_permlane16_swap / v_permlane32_swap, whose two results hold, for each lane, its own
+// value and its partner's (lane l and l ^ 16, resp. l ^ 32); which of the two is the
+// partner depends on the lane's half.
+template <int S>
+__device__ __forceinline__ int partner(int x) {
+    if constexpr (S == 0) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+    if constexpr (S == 1) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);    // quad_perm [2,3,0,1]
+    if constexpr (S == 2) return __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);   // row_half_mirror
+    if constexpr (S == 3) return __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false);   // row_mirror
+    if constexpr (S == 4) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane_id() & 16) ? p[0] : p[1];
+    }
+    if constexpr (S == 5) {
+        const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane_id() & 32) ? p[0] : p[1];
+    }
+    return x;
+}
+template <int S>
+__device__ __forceinline__ float partner(float x) { return __int_as_float(partner<S>(__float_as_int(x))); }
+template <int S>
+__device__ __forceinline__ double partner(double x) {
+    const int64_t b = __double_as_longlong(x);
+    const int lo = partner<S>((int)b), hi = partner<S>((int)(b >> 32));
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+// One arg-max step over (key descending, index ascending); the order is total, so both
+// lanes of a pair keep the same winner.
+template <int S>
+__device__ __forceinline__ void argmax_step(float &key, int &idx, float &val) {
+    const float ok = partner<S>(key), ov = partner<S>(val);
+    const int oi = partner<S>(idx);
+    if (ranks_before(ok, oi, key, idx)) {
+        key = ok;
+        idx = oi;
+        val = ov;
     }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+// Arg-max over each aligned group of 2^g lanes (g <= 6, wave-uniform); every lane of a
+// group ends with the group's winner and its payload.
+__device__ __forceinline__ void group_argmax(float &key, int &idx, float &val, int g) {
+    if (g > 0) argmax_step<0>(key, idx, val);
+    if (g > 1) argmax_step<1>(key, idx, val);
+    if (g > 2) argmax_step<2>(key, idx, val);
+    if (g > 3) argmax_step<3>(key, idx, val);
+    if (g > 4) argmax_step<4>(key, idx, val);
+    if (g > 5) argmax_step<5>(key, idx, val);
 }
 
+__device__ __forceinline__ void wave_argmax(float &key, int &idx, float &val) {
+    argmax_step<0>(key, idx, val);
+    argmax_step<1>(key, idx, val);
+    argmax_step<2>(key, idx, val);
+    argmax_step<3>(key, idx, val);
+    argmax_step<4>(key, idx, val);
+    argmax_step<5>(key, idx, val);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, partner<0>(v));
+    v = fmaxf(v, partner<1>(v));
+    v = fmaxf(v, partner<2>(v));
+    v = fmaxf(v, partner<3>(v));
+    v = fmaxf(v, partner<4>(v));
+    return fmaxf(v, partner<5>(v));
+}
+
+// Sum over the wave in a fixed tree (lane pairs add in the same order on both sides, so
+// every lane ends with the same value).
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    double o;
+    o = partner<0>(v); v = (lane_id() & 1) ? o + v : v + o;
+    o = partner<1>(v); v = (lane_id() & 2) ? o + v : v + o;
+    o = partner<2>(v); v = (lane_id() & 4) ? o + v : v + o;
+    o = partner<3>(v); v = (lane_id() & 8) ? o + v : v + o;
+    o = partner<4>(v); v = (lane_id() & 16) ? o + v : v + o;
+    o = partner<5>(v); v = (lane_id() & 32) ? o + v : v + o;
     return v;
 }
 
@@ -96,28 +155,21 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
     }
 
     if (a.kind == GROUPED && (E / a.n_group) <= kWave && ((E / a.n_group) & (E / a.n_group - 1)) == 0) {
-        // Groups of G = 2^s <= 64 consecutive experts lie inside one slot on G consecutive
-        // lanes, so every group's two largest keys come from segmented butterflies (xor
-        // offsets < G) over all slots at once.
+        // Groups of G = 2^g <= 64 consecutive experts lie inside one slot on G consecutive
+        // lanes, so every group's two largest keys come from arg-max steps confined to
+        // aligned groups of G lanes, for all slots at once.
         const int G = E / a.n_group;
+        const int gbits = __builtin_ctz(G);
         float score[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
             const int e = lane + kWave * i;
-            float k1 = live[i] ? key[i] : -INFINITY;
+            float k1 = live[i] ? key[i] : -INFINITY, unused = 0.0f;
             int i1 = live[i] ? e : INT32_MAX;
-            for (int off = G >> 1; off >= 1; off >>= 1) {
-                const float ok = __shfl_xor(k1, off, kWave);
-                const int oi = __shfl_xor(i1, off, kWave);
-                if (ranks_before(ok, oi, k1, i1)) { k1 = ok; i1 = oi; }
-            }
+            group_argmax(k1, i1, unused, gbits);
             float k2 = (live[i] && e != i1) ? key[i] : -INFINITY;
             int i2 = (live[i] && e != i1) ? e : INT32_MAX;
-            for (int off = G >> 1; off >= 1; off >>= 1) {
-                const float ok = __shfl_xor(k2, off, kWave);
-                const int oi = __shfl_xor(i2, off, kWave);
-                if (ranks_before(ok, oi, k2, i2)) { k2 = ok; i2 = oi; }
-            }
+            group_argmax(k2, i2, unused, gbits);
             score[i] = G >= 2 ? k1 + k2 : k1;
         }
         // keep the topk_group best groups; the first lane of each segment stands for its group
