@@ -212,6 +212,35 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                             for (int fn = 0; fn < C::FN; fn++)
                                 acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
                     }
+            } else if constexpr (C::NW >= 16) {
+                // fp8 with 16 waves (128 registers a lane): all A fragments of the slab, then
+                // one B fragment at a time, so that fragments take 8 (FM + 1) registers
+                const int c0 = 2 * (lane >> 4);
+#pragma unroll
+                for (int sl = 0; sl < C::KS; sl++) {
+                    i32x8 af[C::FM];
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; fm++) {
+                        const int r = wm * C::TM + fm * 16 + (lane & 15);
+                        const char *slab = sa + sl * C::BM * 128;
+                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                        af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    }
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const int r = wn * C::TN + fn * 16 + (lane & 15);
+                        const char *slab = sb + sl * C::BN * 128;
+                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                        const i32x8 b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++)
+                            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], b, acc[fm][fn], 0, 0, 0,
+                                                                                        127, 0, 127);
+                        __builtin_amdgcn_sched_barrier(0);   // keep the B loads from being hoisted together
+                    }
+                }
             } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
                 const int c0 = 2 * (lane >> 4);
                 i32x8 af[2][C::FM], bfr[2][C::FN];
@@ -361,7 +390,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     X(11, 32, 128, 2, 3, 1, 4, 16, 128)      \
     X(12, 256, 256, 1, 2, 2, 4, 16, 128)     \
     X(13, 128, 256, 1, 3, 2, 4, 16, 128)     \
-    X(14, 256, 256, 1, 2, 4, 4, 16, 128)
+    X(14, 256, 256, 1, 2, 4, 4, 16, 128) \
+    X(15, 256, 128, 1, 3, 4, 4, 16, 128) \
+    X(16, 128, 256, 1, 3, 4, 4, 16, 128)
 
 template <class C, int WT, int KIND, bool PARTIAL>
 hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {

@@ -450,8 +450,8 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
                                {3, 16, 10, 9, 1, 1},       {8, 32, 19, 12, 1, 1},     {24, 64, 18, 11, 1, 1},
                                {96, 128, 22, 22, 2, 1},    {384, 256, 25, 25, 1, 1},  {768, 256, 25, 25, 2, 1},
                                {1e30, 256, 25, 25, 1, 1}};
-    static const Row fp8[] = {{0.25, 16, 9, 1, 1, 2},  {8, 16, 1, 1, 1, 2},        {48, 32, 11, 2, 1, 1},
-                              {192, 128, 7, 13, 1, 1}, {1e30, 256, 12, 14, 1, 1}};
+    static const Row fp8[] = {{0.25, 16, 9, 1, 1, 2},  {8, 16, 1, 1, 1, 2},         {48, 32, 11, 2, 1, 1},
+                              {192, 128, 7, 16, 1, 1}, {384, 128, 13, 16, 1, 1}, {1e30, 256, 12, 14, 1, 1}};
     static const Row int4[] = {{0.05, 16, 11, 11, 1, 2}, {8, 16, 11, 10, 1, 1}, {1e30, 32, 12, 12, 1, 1}};
     const Row *rows = bf16;
     int n = sizeof(bf16) / sizeof(Row);

@@ -260,6 +260,27 @@ def test_deepseek_int4_largest_T_sampled():
     check_sampled("deepseek", 512, [0, 511])
 
 
+# Qwen2's w8a8 fp8 format at a size where every fp8 tile runs (four K steps of 128 in GEMM1,
+# two in GEMM2): every plan against the oracle
+FP8_SMALL = synth.CONFIGS["qwen2"].with_shape(name="fp8small", E=16, k=4, H=512, I=256)
+
+
+@pytest.mark.parametrize("T", [1, 6, 40, 300])
+def test_fp8_every_plan(T):
+    if "fp8small" not in _cases:
+        _cases["fp8small"] = Case("fp8small", "cpu", FP8_SMALL)
+    c = _cases["fp8small"]
+    plans = valid_plans(c.layer, T)
+    tiles = {p.gemm1_tile for p in plans}
+    assert {0, 1, 2, 7, 9, 12, 14} <= tiles, tiles       # staged and pipelined, 8 and 16 waves
+    ref, _, _ = c.oracle(T)
+    for p in plans:
+        out, ws = c.gpu(T, p)
+        err = rel_l2(bf16_to_f64(out), ref)
+        assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+    check_intermediates(c, T, plans[-1], ws)
+
+
 # DeepSeek-V3's gate and int4 format at a size the oracle runs in well under a second: three
 # K steps of 256 in GEMM1 (a ragged start for the K rotation), two in GEMM2 (split-K 2)
 I4_SMALL = synth.CONFIGS["deepseek"].with_shape(name="i4small", E=16, k=4, n_group=4, topk_group=2, H=768, I=512)
