@@ -105,6 +105,10 @@ struct GateUpFinishArgs {
     uint32_t *amax;              // fp32 h: |h| max as float bits (atomicMax), may be null
 };
 hipError_t launch_gate_up_finish(const GateUpFinishArgs &a, int64_t max_rows, hipStream_t s);
+// fp32 h (GATE_UP_H_F32) of a small batch, finished and quantised to E4M3 in one workgroup:
+// the pairs' rows through inv_pos; writes |h| max bits to a.amax and amax / 448 to scale_out
+hipError_t launch_gate_up_finish_quant(const GateUpFinishArgs &a, const int32_t *inv_pos, uint8_t *hq, float *scale_out,
+                                       hipStream_t s);
 
 // fp8 activation quantisation
 struct AbsmaxArgs {

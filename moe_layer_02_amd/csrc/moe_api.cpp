@@ -325,17 +325,24 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, s1 > 1, g, mblocks_max * (I / (t1.BN / 2)) * s1,
                            stream)) != hipSuccess)
         return fail(err);
+    // a tiny fp8 batch finishes a split GEMM1 and quantises h in one launch (one workgroup:
+    // worth it while the partial sums it reads are a few tens of KB)
+    const bool finish_quant = fp8 && s1 > 1 && (int64_t)pairs * I * s1 <= 32768;
     if (s1 > 1) {
         if ((err = mark(MOE_STAGE_GEMM1_FINISH)) != hipSuccess) return MOE_ERR_HIP;
         GateUpFinishArgs f{(const float *)(ws + w.g1p), w.cap * 2 * (int64_t)I, s1, I, sorted, npp, pairs, ws + w.h,
                            fp8 ? GATE_UP_H_F32 : f16_activations(L, &plan) ? GATE_UP_H_F16_PERM : GATE_UP_H_BF16,
                            fp8 ? &scal[1] : nullptr};
-        if ((err = launch_gate_up_finish(f, w.cap, stream)) != hipSuccess) return fail(err);
+        err = finish_quant ? launch_gate_up_finish_quant(f, inv_pos, (uint8_t *)(ws + w.hq), (float *)&scal[3], stream)
+                           : launch_gate_up_finish(f, w.cap, stream);
+        if (err != hipSuccess) return fail(err);
     }
 
     // 5. fp8: quantise h with its dynamic scale
     const void *a2 = ws + w.h;
-    if (fp8) {
+    if (fp8 && finish_quant) {
+        a2 = ws + w.hq;
+    } else if (fp8) {
         if ((err = mark(MOE_STAGE_H_QUANT)) != hipSuccess) return MOE_ERR_HIP;
         QuantArgs q{ws + w.h, 1, (uint8_t *)(ws + w.hq), w.cap, I, &scal[1], (float *)&scal[3], sorted, npp, pairs};
         if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
@@ -450,7 +457,7 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
                                {3, 16, 10, 9, 1, 1},       {8, 32, 19, 12, 1, 1},     {24, 64, 18, 11, 1, 1},
                                {96, 128, 22, 22, 2, 1},    {384, 256, 25, 25, 1, 1},  {768, 256, 25, 25, 2, 1},
                                {1e30, 256, 25, 25, 1, 1}};
-    static const Row fp8[] = {{0.25, 16, 9, 1, 1, 2},  {8, 16, 1, 1, 1, 2},         {48, 32, 11, 2, 1, 1},
+    static const Row fp8[] = {{0.125, 16, 9, 1, 1, 2}, {8, 16, 1, 1, 1, 2},         {48, 32, 11, 2, 1, 1},
                               {192, 128, 7, 16, 1, 1}, {384, 128, 13, 16, 1, 1}, {1e30, 256, 12, 14, 1, 1}};
     static const Row int4[] = {{0.05, 16, 11, 11, 1, 2}, {8, 16, 11, 10, 1, 1}, {1e30, 32, 12, 12, 1, 1}};
     const Row *rows = bf16;

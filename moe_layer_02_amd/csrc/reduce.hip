@@ -11,6 +11,7 @@
 // order before SiLU * up.
 #include "common.h"
 #include "kernels.h"
+#include "quant_dev.h"
 
 namespace moe {
 namespace {
@@ -106,7 +107,74 @@ __global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
     }
 }
 
+// A small fp8 batch: the finish above and the quantisation of h (quant.hip) in one
+// workgroup -- every valid pair's h row (through inv_pos) in fp32 with |h| folded, then
+// after a barrier the same rows as E4M3 codes with the scale of that maximum.  Codes,
+// scale and h are those of the two separate kernels.
+__global__ __launch_bounds__(1024) void k_gate_up_finish_quant(GateUpFinishArgs a, const int32_t *inv_pos,
+                                                                uint8_t *hq, float *scale_out) {
+    const int c8 = a.I / 8;
+    const int items = a.pairs * c8;
+    float m = 0.0f;
+    for (int it = threadIdx.x; it < items; it += 1024) {
+        const int64_t r = inv_pos[it / c8];
+        const int c = (it % c8) * 8;
+        float g[8], u[8];
+        for (int s = 0; s < a.split; s++) {
+            const float *p = a.P + s * a.plane + r * 2 * (int64_t)a.I;
+            const float4 g0 = *(const float4 *)(p + c), g1 = *(const float4 *)(p + c + 4);
+            const float4 u0 = *(const float4 *)(p + a.I + c), u1 = *(const float4 *)(p + a.I + c + 4);
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                g[j] = s ? g[j] + gv[j] : gv[j];
+                u[j] = s ? u[j] + uv[j] : uv[j];
+            }
+        }
+        float h[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            h[j] = g[j] / (1.0f + __expf(-g[j])) * u[j];
+            m = fmaxf(m, fabsf(h[j]));
+        }
+        float *o = (float *)a.h + r * a.I + c;
+        *(float4 *)o = make_float4(h[0], h[1], h[2], h[3]);
+        *(float4 *)(o + 4) = make_float4(h[4], h[5], h[6], h[7]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    __shared__ float wmax[16];
+    if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, wmax[i]);
+    float scale, inv;
+    quant_dev::scales_from_amax(__float_as_uint(amax), &scale, &inv);
+    if (threadIdx.x == 0) {
+        *a.amax = __float_as_uint(amax);
+        *scale_out = scale;
+    }
+    for (int it = threadIdx.x; it < items; it += 1024) {
+        const int64_t r = inv_pos[it / c8];
+        const int c = (it % c8) * 8;
+        const float *o = (const float *)a.h + r * a.I + c;
+        const float4 lo = *(const float4 *)o, hi = *(const float4 *)(o + 4);
+        uint2 q;
+        q.x = quant_dev::e4m3x4(lo.x, lo.y, lo.z, lo.w, inv);
+        q.y = quant_dev::e4m3x4(hi.x, hi.y, hi.z, hi.w, inv);
+        *(uint2 *)(hq + r * a.I + c) = q;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gate_up_finish_quant(const GateUpFinishArgs &a, const int32_t *inv_pos, uint8_t *hq, float *scale_out,
+                                       hipStream_t s) {
+    hipLaunchKernelGGL(k_gate_up_finish_quant, dim3(1), dim3(1024), 0, s, a, inv_pos, hq, scale_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_gate_up_finish(const GateUpFinishArgs &a, int64_t max_rows, hipStream_t s) {
     int64_t blocks = (max_rows * (a.I / 8) + 255) / 256;

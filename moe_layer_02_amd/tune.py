@@ -25,7 +25,7 @@ def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64
     for bm in bms:
         for g1 in (tiles if tiles is not None else range(max_tile)):
             for g2 in (tiles if tiles is not None else range(max_tile)):
-                for sk in (1, 2, 4, 8):
+                for sk in (1, 2, 3, 4, 5, 6, 7, 8):
                     for s1 in split1:
                         p = abi.Plan(bm, g1, g2, sk, s1)
                         try:

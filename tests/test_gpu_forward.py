@@ -387,6 +387,8 @@ def test_small_batch_prologue(name, T, expect):
     torch.cuda.synchronize()
     if plan.split_k1 > 1:   # a K-split GEMM1 is followed by its finishing pass
         expect = expect[:expect.index("gemm1") + 1] + ["gemm1_finish"] + expect[expect.index("gemm1") + 1:]
+        if c.cfg.wdtype == synth.WDT_FP8 and T * c.cfg.k * c.cfg.I * plan.split_k1 <= 32768:
+            expect.remove("h_quant")   # which also quantises h in a tiny batch
     assert stages == expect
     ref, _, _ = c.oracle(T)
     assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype]
