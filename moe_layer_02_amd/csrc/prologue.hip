@@ -18,12 +18,12 @@
 namespace moe {
 namespace {
 
-template <int EPL>
+template <int EPL, int V>
 __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
     if (blockIdx.x == 0) {
         if (threadIdx.x == 0 && p.h_amax) *p.h_amax = 0u;   // GEMM1's |h| maximum starts at 0
         const int w = threadIdx.x >> 6;
-        if (w < p.route.T) route_dev::route_token<EPL>(p.route, w);
+        if (w < p.route.T) route_dev::route_token<EPL, V>(p.route, w);
         __syncthreads();
         align_dev::align_group(p.align);
         return;
@@ -70,16 +70,26 @@ __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
     }
 }
 
+template <int EPL>
+void launch_epl(const PrologueArgs &p, dim3 grid, dim3 block, hipStream_t s) {
+    switch (route_dev::route_variant(p.route.kind, p.route.E, p.route.n_group)) {
+    case route_dev::V_SOFTMAX: hipLaunchKernelGGL((k_prologue<EPL, route_dev::V_SOFTMAX>), grid, block, 0, s, p); break;
+    case route_dev::V_SIGMOID: hipLaunchKernelGGL((k_prologue<EPL, route_dev::V_SIGMOID>), grid, block, 0, s, p); break;
+    case route_dev::V_GROUPED_POW2: hipLaunchKernelGGL((k_prologue<EPL, route_dev::V_GROUPED_POW2>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((k_prologue<EPL, route_dev::V_GROUPED_ANY>), grid, block, 0, s, p); break;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s) {
     const dim3 grid(p.act == PROLOGUE_ACT_NONE ? 1 : 2), block(1024);
     if (p.route.E <= 64)
-        hipLaunchKernelGGL(k_prologue<1>, grid, block, 0, s, p);
+        launch_epl<1>(p, grid, block, s);
     else if (p.route.E <= 128)
-        hipLaunchKernelGGL(k_prologue<2>, grid, block, 0, s, p);
+        launch_epl<2>(p, grid, block, s);
     else
-        hipLaunchKernelGGL(k_prologue<4>, grid, block, 0, s, p);
+        launch_epl<4>(p, grid, block, s);
     return hipGetLastError();
 }
 

@@ -19,6 +19,16 @@ namespace moe {
 namespace route_dev {
 
 enum { SOFTMAX = 0, SIGMOID = 1, GROUPED = 2 };
+// compiled variants: the routing mode, with the grouped gate split by its group size
+enum { V_SOFTMAX = 0, V_SIGMOID = 1, V_GROUPED_POW2 = 2, V_GROUPED_ANY = 3 };
+
+// The variant that routes cfg: the grouped gate's fast path needs groups of 2^g <= 64 experts.
+__host__ __device__ inline int route_variant(int kind, int E, int n_group) {
+    if (kind == SOFTMAX) return V_SOFTMAX;
+    if (kind == SIGMOID) return V_SIGMOID;
+    const int G = E / n_group;
+    return (G <= 64 && (G & (G - 1)) == 0) ? V_GROUPED_POW2 : V_GROUPED_ANY;
+}
 
 __device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib) {
     return ka > kb || (ka == kb && ia < ib);
@@ -114,9 +124,11 @@ __device__ __forceinline__ float sigmoid_f64_rounded(float x) {
     return (float)(1.0 / (1.0 + exp(-(double)x)));
 }
 
-// Route token t with the calling wavefront (every lane of the wave must call).
-template <int EPL>
+// Route token t with the calling wavefront (every lane of the wave must call); V is
+// route_variant(a.kind, a.E, a.n_group).
+template <int EPL, int V>
 __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
+    constexpr bool softmax = V == V_SOFTMAX;
     const int lane = lane_id();
     const int E = a.E;
 
@@ -132,7 +144,7 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
             x = a.logits_bf16 ? bf16_bits_to_f32(((const uint16_t *)a.logits)[(int64_t)t * E + e])
                               : ((const float *)a.logits)[(int64_t)t * E + e];
         }
-        if (a.kind == SOFTMAX) {
+        if constexpr (softmax) {
             key[i] = live[i] ? x : -INFINITY;
             val[i] = x;
             if (live[i]) xmax = fmaxf(xmax, x);
@@ -145,7 +157,7 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
 
     // softmax normaliser in fp64: p_e = exp(x_e - max) / sum_all exp(x_e' - max)
     double m = 0.0, z = 1.0;
-    if (a.kind == SOFTMAX) {
+    if constexpr (softmax) {
         m = (double)wave_max(xmax);
         double part = 0.0;
 #pragma unroll
@@ -154,7 +166,7 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         z = wave_sum(part);
     }
 
-    if (a.kind == GROUPED && (E / a.n_group) <= kWave && ((E / a.n_group) & (E / a.n_group - 1)) == 0) {
+    if constexpr (V == V_GROUPED_POW2) {
         // Groups of G = 2^g <= 64 consecutive experts lie inside one slot on G consecutive
         // lanes, so every group's two largest keys come from arg-max steps confined to
         // aligned groups of G lanes, for all slots at once.
@@ -193,7 +205,7 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
             const int e = lane + kWave * i;
             if (live[i] && !((kept >> (e / G)) & 1ull)) live[i] = false;
         }
-    } else if (a.kind == GROUPED) {
+    } else if constexpr (V == V_GROUPED_ANY) {
         // general group size: group score = sum of the group's two largest keys, from two
         // wave-wide arg-max rounds per group; lane g keeps group g's score
         const int G = E / a.n_group;
@@ -264,7 +276,7 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
 #pragma unroll
         for (int i = 0; i < EPL; i++)
             if (lane + kWave * i == bi) live[i] = false;
-        const double v = a.kind == SOFTMAX ? exp((double)bv - m) / z : (double)bv;
+        const double v = softmax ? exp((double)bv - m) / z : (double)bv;
         norm += v;
         if (lane == j) {
             my_id = bi;
