@@ -132,8 +132,18 @@ typedef struct {
  * the reduce step; split_k1 (0 or 1: none) splits GEMM1's likewise -- fp32 partial sums of
  * the gate and up projections that a finishing pass adds in a fixed order before SiLU * up
  * (tiles with block_m <= 32 only: the small-T case, where it multiplies the number of
- * workgroups streaming weights).  moe_default_plan picks one per T; any valid plan gives
- * results equal within rounding (and bitwise reproducible for a fixed plan).
+ * workgroups streaming weights).
+ * split_tail (0 or 1: off; 2..16 with split_k = 1 and a pipelined bf16 or fp8 GEMM2 tile):
+ * GEMM2 runs as a persistent grid, one tile per workgroup per round; when its last round
+ * would be at most half full, the row blocks of that round are computed instead as
+ * S = min(split_tail, grid / their tiles) K splits -- fp32 partial sums that the reduce
+ * step adds in a fixed order -- so that the round's work spreads over the whole grid.  The
+ * grid size and the number of row blocks are known on the device only; GEMM2 records the
+ * split it took.
+ * max_workgroups (0: the whole device) caps the persistent grids of both GEMMs, e.g. to
+ * leave compute units to concurrent work.
+ * moe_default_plan picks a plan per T; any valid plan gives results equal within rounding
+ * (and bitwise reproducible for a fixed plan on a fixed device).
  */
 typedef struct {
     int32_t block_m;
@@ -141,6 +151,8 @@ typedef struct {
     int32_t gemm2_tile;
     int32_t split_k;
     int32_t split_k1;
+    int32_t split_tail;
+    int32_t max_workgroups;
 } moe_plan;
 
 /* Steps of moe_forward, for moe_forward_profiled. */
@@ -252,7 +264,10 @@ typedef enum {
                                   (T*k > 4096 only)                                   */
     MOE_WS_GEMM1_PARTIALS = 13, /* split_k1 > 1: fp32 [split_k1, capacity, 2I] gate (columns
                                    [0, I)) and up ([I, 2I)) partial sums              */
-    MOE_WS_COUNT = 14
+    MOE_WS_GEMM2_TAIL = 14,   /* split_tail > 1: int32 [4] = first sorted row of the split
+                                 row blocks, S (0: none split), elements per plane, 0;
+                                 then at byte 256 fp32 [S, rows, H] partial sums        */
+    MOE_WS_COUNT = 15
 } moe_ws_region;
 
 /* Byte offset of each moe_ws_region in the workspace of moe_forward(layer, T, plan) into

@@ -63,17 +63,52 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     const int n_out = KIND == GEMM_GATE_UP ? C::BN / 2 : C::BN;
     const int ntiles = a.N / n_out;
     const int mn = mblocks * ntiles;
-    const int total = mn * a.split;
     const int G = gridDim.x;
     const int nk = a.ksplit / C::BK;
     const int ebytes = WT == WT_FP8 ? 1 : 2;                  // A and B element bytes
 
+    // Split tail (GEMM2 without a K split): with one tile per workgroup and round, a last
+    // round of rem = mn % G tiles leaves G - rem workgroups idle.  When the row blocks
+    // holding those tiles make at most half a round, they are computed as S K splits
+    // instead (fp32 planes, added in order by the reduce step): after the whole rounds of
+    // the other blocks, S x their tiles units of 1/S of the work fill the grid.
+    constexpr bool TAIL = KIND == GEMM_DOWN && !PARTIAL;
+    int mb_dp = mblocks, tail_s = 0, tail_tiles = 0;
+    if constexpr (TAIL) {
+        if (a.tail_split >= 2) {
+            const int rem = mn % G;
+            if (rem > 0) {
+                const int tmb = (rem + ntiles - 1) / ntiles, tt = tmb * ntiles;
+                const int sk = min(min(a.tail_split, G / tt), min(a.tail_cap / tt, nk));
+                if (sk >= 2) {
+                    mb_dp = mblocks - tmb;
+                    tail_s = sk;
+                    tail_tiles = tt;
+                }
+            }
+            if (blockIdx.x == 0 && tid == 0) {
+                a.tail_info[0] = mb_dp * C::BM;
+                a.tail_info[1] = tail_s;
+                a.tail_info[2] = (mblocks - mb_dp) * C::BM * (int)a.ldc;
+                a.tail_info[3] = 0;
+            }
+        }
+    }
+    const int mn_dp = mb_dp * ntiles;
+    const int total = TAIL ? mn_dp + tail_tiles * tail_s : mn * a.split;
+    const int64_t tail_plane = (int64_t)(mblocks - mb_dp) * C::BM * a.ldc;
+
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
-        const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
-        const int s = tc.s, mb = tc.mb, nt = tc.nt;
+        // unit: whole-K tile (or one of split_k splits), or one split of a tail tile
+        const bool tail = TAIL && tile >= mn_dp;
+        const TileCoord tc = tail ? tile_coord(tile - mn_dp, tail_tiles, mblocks - mb_dp, ntiles, a.group_m)
+                                  : tile_coord(tile, mn_dp, mb_dp, ntiles, a.group_m);
+        const int s = tc.s, mb = tail ? mb_dp + tc.mb : tc.mb, nt = tc.nt;
+        const int kbeg = tail ? s * nk / tail_s : s * nk;     // first K step and number of steps
+        const int nku = tail ? (s + 1) * nk / tail_s - kbeg : nk;
         const int e = __builtin_amdgcn_readfirstlane(a.eids[mb]);
         const int row0 = mb * C::BM;
-        const int64_t kb = (int64_t)s * a.ksplit * ebytes;     // byte offset of this split's K
+        const int64_t kb = (int64_t)kbeg * C::BK * ebytes;    // byte offset of this unit's K
 
         // per load instruction q of this wave: operand (A or B), the lane's byte offset from
         // the operand's base at the split's first K, and the wave's LDS offset in a stage
@@ -120,12 +155,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         // DRAM channels instead of all reading the same column slice of rows that share
         // address bits; tiles that share A or B rows keep K in step for L2 reuse.  The
         // order is fixed per tile, so results stay reproducible.
-        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
+        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nku : 0;
         const char *base_a = uniform_ptr((const char *)a.A + kb);
         const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + kb);
         auto issue = [&](int kstep) {
             const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
-            const int kr = __builtin_amdgcn_readfirstlane(kstep + krot < nk ? kstep + krot : kstep + krot - nk);
+            const int kr = __builtin_amdgcn_readfirstlane(kstep + krot < nku ? kstep + krot : kstep + krot - nku);
             const int64_t koff = (int64_t)kr * C::KS * C::SB;
 #pragma unroll
             for (int q = 0; q < C::LPW; q++)
@@ -147,12 +182,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         block_barrier();
 #pragma unroll
         for (int p = 0; p < C::ST - 1; p++)
-            if (p < nk) issue(p);
+            if (p < nku) issue(p);
 
-        for (int kt = 0; kt < nk; kt++) {
-            wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nk - 1 - kt));
+        for (int kt = 0; kt < nku; kt++) {
+            wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nku - 1 - kt));
             block_barrier();
-            if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1);
+            if (kt + C::ST - 1 < nku) issue(kt + C::ST - 1);
             const char *sa = smem + (kt % C::ST) * C::STAGE, *sb = sa + C::A_STAGE;
             // Fragments of step k + 1 can be read while the MFMAs of step k run (see DB below).
             if constexpr (WT == WT_BF16 && C::MS == 32) {
@@ -341,6 +376,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         const float v = acc[fm][fn][i] * w;
                         if constexpr (PARTIAL)
                             ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
+                        else if (tail)
+                            a.tail_P[s * tail_plane + (int64_t)(row - mb_dp * C::BM) * a.ldc + col] = v;
                         else
                             ((uint16_t *)a.C)[(a.out_by_pair ? (int64_t)p : row) * a.ldc + col] = f32_to_bf16_bits(v);
                     }

@@ -56,6 +56,12 @@ struct GemmArgs {
     int group_m;                 // tile order: blocks per group (set by the launcher)
     int rotate_k;                // 1: each tile starts its K walk at its own offset
     int out_by_pair;             // down, no split: write row p = sorted[row] of C (top-1: the token's output row)
+    // down, no split, pipelined bf16/fp8 tiles: an at most half-full last round of tiles is
+    // computed as up to tail_split K splits into fp32 planes (tail_split < 2: never)
+    int tail_split;
+    int tail_cap;                // tiles x splits the planes hold (BM x BN fp32 each)
+    float *tail_P;               // fp32 [S, tail rows, ldc]
+    int32_t *tail_info;          // written by workgroup 0: first tail row, S (0: none), plane elements
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
@@ -89,6 +95,12 @@ struct ReduceArgs {
     const int32_t *inv_pos;
     uint16_t *out;               // bf16 [T, H]
     int T, k, H;
+    // GEMM2's split tail (null: none): rows from tail_info[0] on are the sum of tail_info[1]
+    // fp32 planes of tail_info[2] elements at tail_P; with direct, GEMM2 wrote the other
+    // rows' tokens itself (top-1) and only the tail's tokens are written here
+    const int32_t *tail_info;
+    const float *tail_P;
+    int direct;
 };
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 

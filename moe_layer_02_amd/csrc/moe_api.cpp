@@ -114,11 +114,20 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
     if ((t1->BN / t1->WN) % (2 * t1->mfma)) return MOE_ERR_INVALID_ARGUMENT;
     // GEMM2: K = I split split_k ways, output columns H
     if (L->I % (t2->BK * p->split_k) || L->H % t2->BN) return MOE_ERR_INVALID_ARGUMENT;
+    // split tail: the unsplit GEMM2 of the pipelined bf16 / fp8 tiles
+    if (p->split_tail < 0 || p->split_tail > 16 || p->max_workgroups < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->split_tail > 1 && (p->split_k != 1 || t2->stages == 0 || wd == MOE_DT_INT4_G128))
+        return MOE_ERR_INVALID_ARGUMENT;
     return MOE_OK;
 }
 
+// GEMM2's split tail on / the tiles x splits its planes hold
+bool split_tail(const moe_plan *p) { return p->split_tail > 1; }
+constexpr int kTailUnits = 256;
+constexpr size_t kTailInfoBytes = 256;
+
 struct Workspace {
-    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, total;
+    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, tail, total;
     int64_t cap;
 };
 
@@ -162,6 +171,9 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
                : p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
     w.align_scratch = take((size_t)align_scratch_bytes(pairs, E));
     w.g1p = take(split1(p) > 1 ? (size_t)split1(p) * w.cap * 2 * L->I * 4 : 0);
+    TileInfo t2{};
+    gemm_tile_info(L->weight_dtype, p->gemm2_tile, &t2);
+    w.tail = take(split_tail(p) ? kTailInfoBytes + (size_t)kTailUnits * t2.BM * t2.BN * 4 : 0);
     w.total = o;
     return w;
 }
@@ -322,8 +334,12 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         g.ksplit = H / s1;
         g.amax_out = nullptr;
     }
-    if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, s1 > 1, g, mblocks_max * (I / (t1.BN / 2)) * s1,
-                           stream)) != hipSuccess)
+    // persistent grids: at most max_workgroups workgroups when the plan caps them
+    auto grid_cap = [&](int64_t tiles) {
+        return plan.max_workgroups > 0 ? std::min<int64_t>(tiles, plan.max_workgroups) : tiles;
+    };
+    if ((err = launch_gemm(wd, plan.gemm1_tile, GEMM_GATE_UP, s1 > 1, g,
+                           grid_cap(mblocks_max * (I / (t1.BN / 2)) * s1), stream)) != hipSuccess)
         return fail(err);
     // a tiny fp8 batch finishes a split GEMM1 and quantises h in one launch (one workgroup:
     // worth it while the partial sums it reads are a few tens of KB)
@@ -372,15 +388,22 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     d.a_scale = (const float *)&scal[3];
     d.b_scale = L->w2_scale;
     d.amax_out = nullptr;
+    int32_t *tail_info = split_tail(&plan) ? (int32_t *)(ws + w.tail) : nullptr;
+    float *tail_P = split_tail(&plan) ? (float *)(ws + w.tail + kTailInfoBytes) : nullptr;
+    d.tail_split = split_tail(&plan) ? plan.split_tail : 0;
+    d.tail_cap = kTailUnits;
+    d.tail_P = tail_P;
+    d.tail_info = tail_info;
     if ((err = launch_gemm(wd, plan.gemm2_tile, GEMM_DOWN, plan.split_k > 1, d,
-                           mblocks_max * (H / t2.BN) * plan.split_k, stream)) != hipSuccess)
+                           grid_cap(mblocks_max * (H / t2.BN) * plan.split_k), stream)) != hipSuccess)
         return fail(err);
 
-    // 7. unpermute and reduce (top-1 without a split: GEMM2 wrote the output already)
-    if (!direct) {
+    // 7. unpermute and reduce (top-1 without a split: GEMM2 wrote the output already, but
+    //    for the rows of a split tail)
+    if (!direct || split_tail(&plan)) {
         if ((err = mark(MOE_STAGE_REDUCE)) != hipSuccess) return MOE_ERR_HIP;
         ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out,
-                     T, k, H};
+                     T, k, H, tail_info, tail_P, direct ? 1 : 0};
         if ((err = launch_reduce(r, stream)) != hipSuccess) return fail(err);
     }
     if (events) {
@@ -449,17 +472,19 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     // Plans by rows per expert r = T*k/E, from timing every valid plan of the Mixtral,
     // Llama-4-Scout, Qwen2 and DeepSeek-V3 shapes on MI355X (graph replays): each row is the
     // plan with the smallest worst-case slowdown over the measured points of its range
-    // (within 6% of the fastest plan at every point).  Small r streams weights (16-row
-    // blocks, narrow tiles, split-K for GEMM2, and for GEMM1 where an expert's I is small
-    // next to the GPU); large r is MFMA work (256x256 tiles of 16 waves).
-    struct Row { double r_max; int bm, g1, g2, split, split1; };
-    static const Row bf16[] = {{0.1, 16, 9, 9, 4, 1},      {0.3, 16, 10, 9, 4, 1},    {1.5, 16, 9, 9, 4, 1},
-                               {3, 16, 10, 9, 1, 1},       {8, 32, 19, 12, 1, 1},     {24, 64, 18, 11, 1, 1},
-                               {96, 128, 22, 22, 2, 1},    {384, 256, 25, 25, 1, 1},  {768, 256, 25, 25, 2, 1},
-                               {1e30, 256, 25, 25, 1, 1}};
-    static const Row fp8[] = {{0.125, 16, 9, 1, 1, 2}, {8, 16, 1, 1, 1, 2},         {48, 32, 11, 2, 1, 1},
-                              {192, 128, 7, 16, 1, 1}, {384, 128, 13, 16, 1, 1}, {1e30, 256, 12, 14, 1, 1}};
-    static const Row int4[] = {{0.05, 16, 11, 11, 1, 2}, {8, 16, 11, 10, 1, 1}, {1e30, 32, 12, 12, 1, 1}};
+    // (within 6% of the fastest plan at every point but Mixtral T=512, 9%).  Small r
+    // streams weights (16-row blocks, narrow tiles, split-K for GEMM2, and for GEMM1 where
+    // an expert's I is small next to the GPU); large r is MFMA work (128x256 and 256x256
+    // tiles of 16 waves, GEMM2's partial last round split).
+    struct Row { double r_max; int bm, g1, g2, split, split1, tail; };
+    static const Row bf16[] = {{0.1, 16, 9, 9, 4, 1, 0},        {0.3, 16, 10, 9, 4, 1, 0},
+                               {1.5, 16, 9, 9, 4, 1, 0},        {3, 16, 10, 9, 1, 1, 0},
+                               {8, 32, 19, 12, 1, 1, 0},        {24, 64, 18, 11, 1, 1, 0},
+                               {96, 128, 22, 22, 2, 1, 0},      {384, 128, 22, 22, 1, 1, 8},
+                               {1e30, 256, 25, 25, 1, 1, 8}};
+    static const Row fp8[] = {{0.125, 16, 9, 1, 1, 2, 0},  {8, 16, 1, 1, 1, 2, 0},       {48, 32, 11, 2, 1, 1, 0},
+                              {192, 128, 7, 16, 1, 1, 8},  {384, 128, 13, 16, 1, 1, 8},  {1e30, 256, 12, 14, 1, 1, 8}};
+    static const Row int4[] = {{0.05, 16, 11, 11, 1, 2, 0}, {8, 16, 11, 10, 1, 1, 0}, {1e30, 32, 12, 12, 1, 1, 0}};
     const Row *rows = bf16;
     int n = sizeof(bf16) / sizeof(Row);
     if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }
@@ -474,10 +499,11 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
         const int i = d % 2 == 0 ? first + d / 2 : first - (d + 1) / 2;
         if (i < 0 || i >= n) continue;
         // top-1 at large r: no split, so that GEMM2 writes the output rows itself and the
-        // reduce pass is skipped (Llama-4-Scout T=8192: 2.41 ms against 2.48 with split 2)
+        // reduce pass only adds a split tail (Llama-4-Scout T=8192: 2.31 ms against 2.45 with
+        // split 2)
         const int split0 = layer->route.top_k == 1 && r > 96 ? 1 : rows[i].split;
         for (int sk = split0; sk >= 1; sk /= 2) {
-            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk, rows[i].split1};
+            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk, rows[i].split1, sk == 1 ? rows[i].tail : 0, 0};
             if (check_plan(layer, &p, &t1, &t2) != MOE_OK) p.split_k1 = 1;   // H not split that way
             if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
                 *plan = p;
@@ -533,9 +559,10 @@ moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *
     if ((st = check_plan(layer, plan, &t1, &t2)) != MOE_OK) return st;
     std::snprintf(buf, len,
                   "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d stages%d mfma%d] gemm2=%d[BM%d BN%d BK%d "
-                  "waves%dx%d stages%d mfma%d] split_k=%d split_k1=%d",
+                  "waves%dx%d stages%d mfma%d] split_k=%d split_k1=%d split_tail=%d max_workgroups=%d",
                   plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, t1.stages, t1.mfma,
-                  plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k, split1(plan));
+                  plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k, split1(plan),
+                  split_tail(plan) ? plan->split_tail : 0, plan->max_workgroups);
     return MOE_OK;
 }
 
@@ -550,7 +577,7 @@ moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_pl
     if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
     const Workspace w = layout(layer, T, &p);
     const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos,
-                                    w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p};
+                                    w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p, w.tail};
     for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
     return MOE_OK;
 }

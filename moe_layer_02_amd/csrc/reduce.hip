@@ -22,10 +22,26 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     const int64_t t = gid / c8;
     const int col = (int)(gid % c8) * 8;
     if (t >= a.T) return;
+    // GEMM2's split tail: rows from tail_row0 on are tail_s fp32 planes
+    int64_t tail_row0 = INT64_MAX, tail_plane = 0;
+    int tail_s = 0;
+    if (a.tail_info && a.tail_info[1] > 0) {
+        tail_row0 = a.tail_info[0];
+        tail_s = a.tail_info[1];
+        tail_plane = a.tail_info[2];
+    }
+    if (a.direct && a.inv_pos[t] < tail_row0) return;   // top-1: GEMM2 wrote this token
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < a.k; j++) {
         const int64_t row = a.inv_pos[t * a.k + j];
-        if (a.split == 0) {
+        if (row >= tail_row0) {
+            for (int s = 0; s < tail_s; s++) {
+                const float *p = a.tail_P + s * tail_plane + (row - tail_row0) * a.H + col;
+                const float4 lo = *(const float4 *)p, hi = *(const float4 *)(p + 4);
+                acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+                acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+            }
+        } else if (a.split == 0) {
             const uint4 v = *(const uint4 *)((const uint16_t *)a.Y + row * a.H + col);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

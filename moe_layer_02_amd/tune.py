@@ -20,19 +20,20 @@ from moe_layer_02_amd import abi, synth
 
 
 def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64, 128, 256), tiles=None,
-                split1=(1,)):
+                split1=(1,), tails=(0,)):
     out = []
     for bm in bms:
         for g1 in (tiles if tiles is not None else range(max_tile)):
             for g2 in (tiles if tiles is not None else range(max_tile)):
                 for sk in (1, 2, 3, 4, 5, 6, 7, 8):
                     for s1 in split1:
-                        p = abi.Plan(bm, g1, g2, sk, s1)
-                        try:
-                            abi.moe_workspace_bytes(layer.struct, T, p)
-                        except abi.MoEError:
-                            continue
-                        out.append(p)
+                        for st in tails:
+                            p = abi.Plan(bm, g1, g2, sk, s1, st)
+                            try:
+                                abi.moe_workspace_bytes(layer.struct, T, p)
+                            except abi.MoEError:
+                                continue
+                            out.append(p)
     return out
 
 
@@ -69,6 +70,7 @@ def main():
     ap.add_argument("--bm", default="16,32,64,128,256", help="block heights to try")
     ap.add_argument("--tiles", default=None, help="tile ids to try for both GEMMs (default: all)")
     ap.add_argument("--split1", default="1", help="GEMM1 K splits to try (small-T tiles only)")
+    ap.add_argument("--split-tail", default="0", help="GEMM2 split-tail factors to try (0: off)")
     args = ap.parse_args()
     cfg = synth.CONFIGS[args.config]
     w = synth.expert_weights(cfg, device="cuda")
@@ -87,7 +89,11 @@ def main():
         bms = tuple(int(b) for b in args.bm.split(","))
         tiles = None if args.tiles is None else [int(t) for t in args.tiles.split(",")]
         split1 = tuple(int(v) for v in args.split1.split(","))
-        for p in valid_plans(layer, T, bms=bms, tiles=tiles, split1=split1):
+        tails = tuple(int(v) for v in args.split_tail.split(","))
+        plans = valid_plans(layer, T, bms=bms, tiles=tiles, split1=split1, tails=tails)
+        if plans:   # bring the clocks up before the first timed plan
+            time_plan(layer, x, lg, T, plans[0], 5 * args.reps)
+        for p in plans:
             us = time_plan(layer, x, lg, T, p, args.reps)
             res.append((us, p.as_tuple()))
             print("[tune] %s T=%d plan=%s %.1f us" % (cfg.name, T, p.as_tuple(), us), file=sys.stderr, flush=True)

@@ -216,3 +216,37 @@ def test_route_and_align_argument_checks():
 def test_status_strings():
     assert abi.status_str(abi.MOE_OK) == "ok"
     assert abi.status_str(abi.MOE_ERR_WORKSPACE_TOO_SMALL) == "workspace too small"
+
+
+def test_split_tail_rules():
+    """GEMM2's split tail: unsplit GEMM2 with a pipelined bf16 or fp8 tile only, at most 16
+    splits; its planes (256 tiles of fp32) get their own workspace region; max_workgroups
+    is a non-negative cap."""
+    cfg = synth.CONFIGS["mixtral"]
+    layer = fake_layer(cfg)
+    T = 4096
+    off_plain = abi.moe_workspace_offsets(layer, T, abi.Plan(256, 25, 25, 1))
+    base = abi.moe_workspace_bytes(layer, T, abi.Plan(256, 25, 25, 1))
+    assert base == abi.moe_workspace_bytes(layer, T, abi.Plan(256, 25, 25, 1, 0, 1))
+    with_tail = abi.Plan(256, 25, 25, 1, 0, 4)
+    assert abi.moe_workspace_bytes(layer, T, with_tail) >= base + 256 + 256 * 256 * 256 * 4
+    off = abi.moe_workspace_offsets(layer, T, with_tail)
+    assert off["gemm2_tail"] >= off["gemm1_partials"] and off["gemm2_tail"] == off_plain["gemm2_tail"]
+    assert "split_tail=4 max_workgroups=0" in abi.moe_plan_describe(layer, T, with_tail)
+    assert "max_workgroups=64" in abi.moe_plan_describe(layer, T, abi.Plan(256, 25, 25, 1, 0, 0, 64))
+    assert abi.Plan(256, 25, 25, 1, 0, 4).as_tuple() == (256, 25, 25, 1, 0, 4)
+    assert abi.Plan(256, 25, 25, 1, 0, 0, 64).as_tuple() == (256, 25, 25, 1, 0, 0, 64)
+    assert abi.Plan(256, 25, 25, 1).as_tuple() == (256, 25, 25, 1)
+    assert abi.moe_default_plan(layer, T).split_tail > 1
+    for bad in [abi.Plan(256, 25, 25, 2, 0, 4),     # with a K split of every tile
+                abi.Plan(16, 0, 0, 1, 0, 4),        # register-staged GEMM2 tile
+                abi.Plan(256, 25, 25, 1, 0, 17), abi.Plan(256, 25, 25, 1, 0, -1),
+                abi.Plan(256, 25, 25, 1, 0, 0, -1)]:
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_workspace_bytes(layer, T, bad)
+        assert ei.value.status == abi.MOE_ERR_INVALID_ARGUMENT
+    i4 = fake_layer(synth.CONFIGS["deepseek"])
+    with pytest.raises(abi.MoEError):
+        abi.moe_workspace_bytes(i4, 64, abi.Plan(32, 12, 12, 1, 0, 4))
+    assert abi.moe_workspace_bytes(i4, 64, abi.Plan(32, 12, 12, 1)) > 0
+    assert all(abi.moe_default_plan(i4, T).split_tail == 0 for T in (1, 64, 512))

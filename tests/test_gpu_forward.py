@@ -12,8 +12,8 @@ import torch
 
 import oracle
 from moe_layer_02_amd import abi, synth
-from tests.gpu_util import (TOL, bits, bf16_to_f64, device_layer, needs_gpu, oracle_route, oracle_weights,
-                            rel_l2, say, valid_plans, weights, workspace_view)
+from tests.gpu_util import (TOL, bits, bf16_to_f64, device_layer, expected_tail, gemm2_tile, needs_gpu,
+                            oracle_route, oracle_weights, rel_l2, say, valid_plans, weights, workspace_view)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -137,7 +137,7 @@ def test_tiny_top1_every_plan(T):
             o2 = torch.empty_like(out)
             stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), o2, ws, ev, p)
             torch.cuda.synchronize()
-            assert ("reduce" in stages) == (p.split_k > 1), (p.as_tuple(), stages)
+            assert ("reduce" in stages) == (p.split_k > 1 or p.split_tail > 1), (p.as_tuple(), stages)
             assert torch.equal(o2.view(torch.int16), out.view(torch.int16))
 
 
@@ -412,3 +412,92 @@ def test_profiled_forward_records_every_stage():
     assert all(t >= 0 for t in times)
     ref, _, _ = c.oracle(T)
     assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype]
+
+
+# ---- GEMM2 split tail ------------------------------------------------------------------
+
+def tail_taken(c, T, plan, ws):
+    """(first tail row, S) that GEMM2 recorded in the workspace."""
+    info = workspace_view(c.layer, T, plan, ws, "gemm2_tail", torch.int32, 4).cpu().numpy()
+    return int(info[0]), int(info[1])
+
+
+def check_tail_plans(c, T, grids, tails=(2, 8)):
+    """Every split-tail plan on grids of `grids` workgroups against the oracle; GEMM2's
+    recorded tail is the rule's.  Returns how many runs split a tail after whole tiles and
+    how many split everything."""
+    ref, _, _ = c.oracle(T)
+    mixed = whole = 0
+    for g in grids:
+        plans = valid_plans(c.layer, T, split1=(1,), splits=(1,), tails=tails, max_workgroups=g)
+        assert plans, "no split-tail plan"
+        for p in plans:
+            out, ws = c.gpu(T, p)
+            err = rel_l2(bf16_to_f64(out), ref)
+            assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+            npp = int(workspace_view(c.layer, T, p, ws, "num_post_pad", torch.int32, 1).cpu()[0])
+            got = tail_taken(c, T, p, ws)
+            cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, p.block_m)
+            want = expected_tail(npp, cap, c.cfg.H, c.cfg.I, gemm2_tile(c.layer, T, p), g, p.split_tail)
+            assert got == want, (p.as_tuple(), got, want)
+            if got[1]:
+                mixed += got[0] > 0
+                whole += got[0] == 0
+    return mixed, whole
+
+
+# a layer wide enough for several GEMM2 column tiles and K steps in every tile shape
+TAIL_SMALL = synth.CONFIGS["tiny"].with_shape(name="tailsmall", H=512, I=512)
+TAIL_SMALL_TOP1 = TAIL_SMALL.with_shape(name="tailsmall_top1", k=1, route_kind=abi.ROUTE_SIGMOID, renormalize=False)
+
+
+def small_case(cfg):
+    if cfg.name not in _cases:
+        _cases[cfg.name] = Case(cfg.name, "cpu", cfg)
+    return _cases[cfg.name]
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_split_tail_every_plan(T):
+    """GEMM2's last partial round as K splits (fp32 planes the reduce adds in order) on grids
+    of 24 and 48 workgroups, every tile shape: whole tiles, then the split tail."""
+    mixed, _ = check_tail_plans(small_case(TAIL_SMALL), T, (24, 48))
+    assert mixed > 0
+
+
+def test_split_tail_every_plan_fp8():
+    mixed, _ = check_tail_plans(small_case(FP8_SMALL), 300, (8, 24))
+    assert mixed > 0
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_split_tail_top1(T):
+    """Top-1: GEMM2 writes the whole-tile rows' tokens itself and the reduce writes only the
+    tail's tokens."""
+    mixed, _ = check_tail_plans(small_case(TAIL_SMALL_TOP1), T, (24,))
+    assert mixed > 0
+
+
+@pytest.mark.parametrize("grid", [112, 0])
+def test_split_tail_mixtral_sampled(grid):
+    """The full-size Mixtral shard with its large-T tile: tokens whose expert rows lie in
+    the split tail (and two others) against the oracle."""
+    c = case("mixtral")
+    T = 512
+    p = abi.Plan(256, 25, 25, 1, 1, 4, grid)
+    out, ws = c.gpu(T, p)
+    row0, S = tail_taken(c, T, p, ws)
+    if grid:   # with the whole device the grid is the capacity's tile bound: no tail here
+        npp = int(workspace_view(c.layer, T, p, ws, "num_post_pad", torch.int32, 1).cpu()[0])
+        cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, 256)
+        assert (row0, S) == expected_tail(npp, cap, c.cfg.H, c.cfg.I, (256, 256, 64), grid, 4)
+        assert S >= 2 and row0 > 0
+    inv = workspace_view(c.layer, T, p, ws, "inv_pos", torch.int32, T * c.cfg.k).cpu().numpy().reshape(T, c.cfg.k)
+    in_tail = [t for t in range(T) if S and (inv[t] >= row0).any()]
+    tokens = sorted(set(in_tail[:2] + [0, T - 1]))
+    ref, _, _ = c.oracle(T, tokens=tokens)
+    err = rel_l2(bf16_to_f64(out[tokens]), ref)
+    say("  tail rows from %d, S=%d, sampled rel-L2 %.3e" % (row0, S, err))
+    assert err <= TOL[c.cfg.wdtype]
+    again, _ = c.gpu(T, p, ws=ws)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
