@@ -159,7 +159,8 @@ typedef struct {
 typedef enum {
     MOE_STAGE_ROUTE = 0, MOE_STAGE_ALIGN = 1, MOE_STAGE_ACT_QUANT = 2, MOE_STAGE_GEMM1 = 3,
     MOE_STAGE_H_QUANT = 4, MOE_STAGE_GEMM2 = 5, MOE_STAGE_REDUCE = 6,
-    MOE_STAGE_PROLOGUE = 7,   /* T <= 16: route, align and the activation pass in one launch */
+    MOE_STAGE_PROLOGUE = 7,   /* T <= 64 (fp8 or more than 64 experts: 16): route, align
+                                 and the activation pass in one launch                  */
     MOE_STAGE_GEMM1_FINISH = 8, /* split_k1 > 1: sum of GEMM1's partials, SiLU * up      */
     MOE_STAGE_COUNT = 9
 } moe_stage;

@@ -126,6 +126,15 @@ bool split_tail(const moe_plan *p) { return p->split_tail > 1; }
 constexpr int kTailUnits = 256;
 constexpr size_t kTailInfoBytes = 256;
 
+// the one-launch prologue (route, align, activation pass) takes batches up to this size:
+// its 16 waves route the tokens in turn, which pays while a token's routing is short (up
+// to 64 experts: Mixtral T=32 265 against 272 us); the 256-expert grouped gate keeps one
+// wave per token beyond 16 tokens (DeepSeek T=64: 773 against 813 us in the prologue)
+int prologue_max_t(const moe_layer *L) {
+    if (L->weight_dtype == MOE_DT_FP8_E4M3) return kPrologueMaxTFp8;
+    return L->E <= 64 ? kPrologueMaxT : kPrologueMaxTFp8;
+}
+
 struct Workspace {
     size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, tail, total;
     int64_t cap;
@@ -245,7 +254,8 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     RouteArgs ra = route_args(&L->route, T, logits, L->correction_bias, ids, topk_w);
     AlignArgs aa{T, k, E, plan.block_m, nbits_for(E), w.cap, ids, sorted, eids, npp, counts, inv_pos};
     const void *a1 = hidden;
-    if (T <= kPrologueMaxT) {
+    const bool prologue = T <= prologue_max_t(L);
+    if (prologue) {
         // 1-3 in one launch for a small batch
         if ((err = mark(MOE_STAGE_PROLOGUE)) != hipSuccess) return MOE_ERR_HIP;
         PrologueArgs pa{};
@@ -394,6 +404,8 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     d.tail_cap = kTailUnits;
     d.tail_P = tail_P;
     d.tail_info = tail_info;
+    const ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out,
+                       T, k, H, tail_info, tail_P, direct ? 1 : 0};
     if ((err = launch_gemm(wd, plan.gemm2_tile, GEMM_DOWN, plan.split_k > 1, d,
                            grid_cap(mblocks_max * (H / t2.BN) * plan.split_k), stream)) != hipSuccess)
         return fail(err);
@@ -402,8 +414,6 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     //    for the rows of a split tail)
     if (!direct || split_tail(&plan)) {
         if ((err = mark(MOE_STAGE_REDUCE)) != hipSuccess) return MOE_ERR_HIP;
-        ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out,
-                     T, k, H, tail_info, tail_P, direct ? 1 : 0};
         if ((err = launch_reduce(r, stream)) != hipSuccess) return fail(err);
     }
     if (events) {

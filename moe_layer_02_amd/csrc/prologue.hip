@@ -1,15 +1,16 @@
 // prologue.hip -- route, align and the activation pass of a small batch in one launch.
 //
-// With a handful of tokens each of these steps is a few microseconds of launch and memory
+// With a few tokens each of these steps is a few microseconds of launch and memory
 // latency, comparable to the whole weight-streaming time of a small layer.  One launch of
-// up to two 1024-thread workgroups does them all, with the same results as the separate
-// kernels:
-//   workgroup 0: wave w routes token w (route_dev.h), a barrier makes the pairs visible,
-//                then the one-workgroup align (align_dev.h) lays them out;
-//   workgroup 1: the activation pass, independent of the routing --
-//                fp8: the largest |x| over the batch (reduced inside the workgroup, no
-//                atomics), then every code with that scale (quant_dev.h), and the scale;
-//                int4: the hidden states to fp16 in the packed-nibble order.
+// 1024-thread workgroups does them all, with the same results as the separate kernels:
+//   workgroup 0: wave w routes tokens w, w + 16, ... (route_dev.h), a barrier makes the
+//                pairs visible, then the one-workgroup align (align_dev.h) lays them out;
+//   workgroups 1..: the activation pass, independent of the routing --
+//                fp8 (one workgroup): the largest |x| over the batch (reduced inside the
+//                workgroup, no atomics), then every code with that scale (quant_dev.h), and
+//                the scale; int4: the hidden states to fp16 in the packed-nibble order.
+#include <algorithm>
+
 #include "align_dev.h"
 #include "kernels.h"
 #include "quant_dev.h"
@@ -22,16 +23,17 @@ template <int EPL, int V>
 __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
     if (blockIdx.x == 0) {
         if (threadIdx.x == 0 && p.h_amax) *p.h_amax = 0u;   // GEMM1's |h| maximum starts at 0
-        const int w = threadIdx.x >> 6;
-        if (w < p.route.T) route_dev::route_token<EPL, V>(p.route, w);
+        for (int t = threadIdx.x >> 6; t < p.route.T; t += 16) route_dev::route_token<EPL, V>(p.route, t);
         __syncthreads();
         align_dev::align_group(p.align);
         return;
     }
     const int64_t n8 = p.n / 8;
     const int tid = threadIdx.x;
-    if (p.act == PROLOGUE_ACT_F16_PERM) {
-        for (int64_t i = tid; i < n8; i += 1024) ((uint4 *)p.x16)[i] = bf16x8_to_f16x8_perm(((const uint4 *)p.x)[i]);
+    if (p.act == PROLOGUE_ACT_F16_PERM) {   // workgroups 1 .. G-1 share the conversion
+        const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
+        for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + tid; i < n8; i += stride)
+            ((uint4 *)p.x16)[i] = bf16x8_to_f16x8_perm(((const uint4 *)p.x)[i]);
         return;
     }
     // fp8: amax over the batch
@@ -83,7 +85,11 @@ void launch_epl(const PrologueArgs &p, dim3 grid, dim3 block, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s) {
-    const dim3 grid(p.act == PROLOGUE_ACT_NONE ? 1 : 2), block(1024);
+    // fp8: one workgroup for the pass; fp16 conversion: one per 4096 16-byte groups, up to 32
+    int g = 1;
+    if (p.act == PROLOGUE_ACT_FP8) g = 2;
+    if (p.act == PROLOGUE_ACT_F16_PERM) g = 1 + (int)std::min<int64_t>(32, std::max<int64_t>(1, (p.n / 8 + 4095) / 4096));
+    const dim3 grid(g), block(1024);
     if (p.route.E <= 64)
         launch_epl<1>(p, grid, block, s);
     else if (p.route.E <= 128)
