@@ -62,6 +62,7 @@ struct GemmArgs {
     int tail_cap;                // tiles x splits the planes hold (BM x BN fp32 each)
     float *tail_P;               // fp32 [S, tail rows, ldc]
     int32_t *tail_info;          // written by workgroup 0: first tail row, S (0: none), plane elements
+    int expert_groups;           // > 0: tile groups of an expert's row blocks, at most this many (set by the launcher)
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };

@@ -146,6 +146,38 @@ __device__ __forceinline__ TileCoord tile_coord(int tile, int mn, int mblocks, i
     return c;
 }
 
+// The same walk with groups aligned to experts: the row blocks of one expert, at most gmax
+// per group (eids is non-decreasing over the row blocks), so that the tiles in flight on an
+// XCD share the expert's weight tiles instead of straddling two experts.
+__device__ __forceinline__ TileCoord tile_coord_expert(int tile, int mn, int mblocks, int ntiles,
+                                                       const int32_t *eids, int gmax) {
+    TileCoord c;
+    c.s = tile / mn;
+    const int rest = tile - c.s * mn;
+    const int bt = rest / ntiles;                 // a block of rest's group (groups span all column tiles)
+    const int e = eids[bt];
+    int lo = 0, hi = bt;                          // first block of expert e
+    while (lo < hi) {
+        const int m = (lo + hi) / 2;
+        if (eids[m] < e) lo = m + 1;
+        else hi = m;
+    }
+    const int efirst = lo;
+    lo = bt + 1;                                  // one past its last block below mblocks
+    hi = mblocks;
+    while (lo < hi) {
+        const int m = (lo + hi) / 2;
+        if (eids[m] <= e) lo = m + 1;
+        else hi = m;
+    }
+    const int b0 = efirst + (bt - efirst) / gmax * gmax;
+    const int gsz = min(gmax, lo - b0);
+    const int local = rest - b0 * ntiles;
+    c.mb = b0 + local % gsz;
+    c.nt = local / gsz;
+    return c;
+}
+
 // workgroup b of a grid of G (a multiple of 8) starts at tile j0: consecutive tiles go to
 // one XCD (workgroups are dealt to the 8 XCDs round-robin)
 __device__ __forceinline__ int xcd_first_tile(int b, int G) {
