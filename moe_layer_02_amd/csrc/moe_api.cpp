@@ -494,7 +494,7 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
                                {1e30, 256, 25, 25, 1, 1, 8}};
     static const Row fp8[] = {{0.125, 16, 9, 1, 1, 2, 0},  {8, 16, 1, 1, 1, 2, 0},       {48, 32, 11, 2, 1, 1, 0},
                               {192, 128, 7, 16, 1, 1, 8},  {384, 128, 13, 16, 1, 1, 8},  {1e30, 256, 12, 14, 1, 1, 8}};
-    static const Row int4[] = {{0.05, 16, 11, 11, 1, 2, 0}, {8, 16, 11, 10, 1, 1, 0}, {1e30, 32, 12, 12, 1, 1, 0}};
+    static const Row int4[] = {{0.05, 16, 11, 11, 1, 2, 0}, {8, 16, 11, 11, 1, 1, 0}, {1e30, 32, 12, 12, 1, 1, 0}};
     const Row *rows = bf16;
     int n = sizeof(bf16) / sizeof(Row);
     if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }
