@@ -80,6 +80,8 @@ def lib():
         L.orc_forward.restype = I
         L.orc_fp8_intermediate.argtypes = [ctypes.POINTER(_Weights), I, I, P, P, P, P, P]
         L.orc_fp8_intermediate.restype = I
+        L.orc_grouped_gemm.argtypes = [I, I, I, I, I, P, F, P, P, P, P]
+        L.orc_grouped_gemm.restype = I
         _lib = L
     return _lib
 
@@ -226,3 +228,20 @@ def fp8_intermediate(W: Weights, hidden_bits, ids):
 def to_bf16(out64):
     """Round the fp64 layer output to the layer's bf16 output (via fp32, RNE)."""
     return f32_to_bf16(np.asarray(out64, np.float64).astype(np.float32))
+
+
+def grouped_gemm(dtype, E, N, K, x, w, m_sizes, x_scale=1.0, w_scale=None, M=None):
+    """EP-MoE grouped GEMM over contiguous segments: y [M, N] fp64 (rows past the last
+    segment are zero).  dtype BF16 (x, w as bf16 bits) or FP8_E4M3 (E4M3 codes, per-tensor
+    x_scale and per-expert w_scale)."""
+    x = _c(x, np.uint16 if dtype == BF16 else np.uint8)
+    w = _c(w, np.uint16 if dtype == BF16 else np.uint8)
+    m_sizes = _c(m_sizes, np.int32)
+    M = x.shape[0] if M is None else M
+    assert x.shape == (M, K) and w.shape == (E, N, K) and m_sizes.shape == (E,)
+    y = np.zeros((M, N), np.float64)
+    rc = lib().orc_grouped_gemm(E, N, K, dtype, M, _ptr(x), float(x_scale), _ptr(w), _ptr(_c(w_scale, np.float32)),
+                                _ptr(m_sizes), _ptr(y))
+    if rc != 0:
+        raise ValueError("orc_grouped_gemm: invalid arguments")
+    return y

@@ -476,3 +476,44 @@ int orc_forward(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
     free(x); free(h); free(y); free(row); free(hall);
     return 0;
 }
+
+/* ---- grouped GEMM over pre-permuted contiguous segments ----
+ * [FBGEMM]: the grouped GEMM that EP-MoE runs on tokens already grouped by expert, with
+ * bf16 operands or E4M3 operands and per-tensor scales.  Reading: segment e holds rows
+ * [off_e, off_e + m_sizes[e]) of X, off_e the sum of the earlier sizes; every row r of
+ * segment e gets Y[r, n] = x_scale * w_scale[e] * sum_c X[r, c] * W[e, n, c] (scales 1 for
+ * bf16), in fp64 on the decoded values.  Rows past the last segment are left untouched. */
+static double grouped_elem(int dtype, const void *base, int64_t i)
+{
+    if (dtype == ORC_BF16) return orc_bf16_to_f32(((const uint16_t *)base)[i]);
+    return orc_e4m3_to_f32(((const uint8_t *)base)[i]);
+}
+
+int orc_grouped_gemm(int E, int N, int K, int dtype, int M, const void *x, float x_scale,
+                     const void *w, const float *w_scale, const int32_t *m_sizes, double *y)
+{
+    if (E < 1 || N < 1 || K < 1 || M < 0 || (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3)) return -1;
+    if (dtype == ORC_FP8_E4M3 && !w_scale) return -1;
+    int64_t total = 0;
+    for (int e = 0; e < E; e++) {
+        if (m_sizes[e] < 0) return -1;
+        total += m_sizes[e];
+    }
+    if (total > M) return -1;
+    double *xr = malloc(sizeof(double) * K);
+    int64_t r = 0;
+    for (int e = 0; e < E; e++) {
+        double scale = dtype == ORC_FP8_E4M3 ? (double)x_scale * w_scale[e] : 1.0;
+        for (int i = 0; i < m_sizes[e]; i++, r++) {
+            for (int c = 0; c < K; c++) xr[c] = grouped_elem(dtype, x, r * K + c);
+            for (int n = 0; n < N; n++) {
+                double acc = 0.0;
+                int64_t wrow = ((int64_t)e * N + n) * K;
+                for (int c = 0; c < K; c++) acc += xr[c] * grouped_elem(dtype, w, wrow + c);
+                y[r * N + n] = scale * acc;
+            }
+        }
+    }
+    free(xr);
+    return 0;
+}

@@ -94,6 +94,15 @@ int orc_forward(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
 int orc_fp8_intermediate(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
                          const int32_t *ids, float *h, uint8_t *hq, float *scales);
 
+/* ---- grouped GEMM over pre-permuted contiguous per-expert segments (EP-MoE) ----
+ * Segment e = rows [off_e, off_e + m_sizes[e]) of x, off_e = sum of the earlier sizes;
+ * y[r, n] = x_scale * w_scale[e] * sum_c x[r, c] * w[e, n, c] in fp64 (dtype ORC_BF16:
+ * bf16 bits, scales 1; ORC_FP8_E4M3: E4M3 codes and per-tensor scales).  x [M, K],
+ * w [E, N, K], y [M, N]; rows past the last segment are not written.  Returns -1 for a
+ * negative size or sizes summing past M. */
+int orc_grouped_gemm(int E, int N, int K, int dtype, int M, const void *x, float x_scale,
+                     const void *w, const float *w_scale, const int32_t *m_sizes, double *y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,10 @@ MUTANTS = {
     "e4m3_bias_8": ("ex - 7);\n    return (float)(sign ? -v : v);\n}\n\n/* Round",
                     "ex - 8);\n    return (float)(sign ? -v : v);\n}\n\n/* Round"),
     "a2_scale_from_a1": ("pertensor_scales(amax2, &s2, &inv2);", "pertensor_scales(amax1, &s2, &inv2);"),
+    # grouped GEMM
+    "ggemm_scale_of_next_expert": ("(double)x_scale * w_scale[e] : 1.0;", "(double)x_scale * w_scale[(e + 1) % E] : 1.0;"),
+    "ggemm_weight_transposed": ("grouped_elem(dtype, w, wrow + c)", "grouped_elem(dtype, w, (int64_t)e * N * K + (int64_t)c * N + n)"),
+    "ggemm_segments_from_zero": ("for (int i = 0; i < m_sizes[e]; i++, r++) {", "for (int i = 0; i < m_sizes[e]; i++, r++) { r = r % (m_sizes[e] ? m_sizes[e] : 1);"),
     "bf16_truncates": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;", ""),
 }
 

@@ -430,3 +430,63 @@ def test_forward_empty_batch():
     W, _, _ = _bf16_weights(2, 16, 32)
     out = oracle.forward(W, np.zeros((0, 16), np.uint16), np.zeros((0, 1), np.int32), np.zeros((0, 1), np.float32))
     assert out.shape == (0, 16)
+
+
+# ---- grouped GEMM over contiguous per-expert segments (EP-MoE) --------------------------
+
+def _bits_bf16(rng, shape):
+    """Random bf16 bit patterns of normal values (the top half of fp32 normals)."""
+    return (rng.standard_normal(shape).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _e4m3_to_f64(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("sizes", [[3, 0, 5, 1, 7], [0, 0, 16, 0, 0], [1, 1, 1, 1, 1]])
+def test_grouped_gemm_bf16_is_segment_matmuls(sizes):
+    """bf16: each segment's rows times its expert's transposed weight (numpy fp64 matmul on
+    numpy's own bf16 decode); rows past the last segment stay zero."""
+    rng = np.random.default_rng(11)
+    E, N, K = 5, 24, 40
+    M = sum(sizes) + 3
+    x, w = _bits_bf16(rng, (M, K)), _bits_bf16(rng, (E, N, K))
+    y = oracle.grouped_gemm(oracle.BF16, E, N, K, x, w, sizes)
+    ref = np.zeros((M, N))
+    r = 0
+    for e, m in enumerate(sizes):
+        ref[r:r + m] = _bf16_to_f64(x[r:r + m]) @ _bf16_to_f64(w[e]).T
+        r += m
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    assert (y[sum(sizes):] == 0).all()
+
+
+def test_grouped_gemm_fp8_applies_per_tensor_scales():
+    """E4M3 codes (decoded by torch) with the activation scale and each expert's own
+    weight scale."""
+    rng = np.random.default_rng(12)
+    E, N, K = 4, 16, 48
+    sizes = [6, 2, 0, 9]
+    M = sum(sizes)
+    codes = lambda shape: np.where(((v := rng.integers(0, 256, shape, dtype=np.uint8)) & 0x7F) == 0x7F, 0, v).astype(np.uint8)  # noqa: E731
+    x, w = codes((M, K)), codes((E, N, K))
+    ws = np.array([0.5, 0.125, 3.0, 0.01], np.float32)
+    y = oracle.grouped_gemm(oracle.FP8_E4M3, E, N, K, x, w, sizes, x_scale=0.37, w_scale=ws)
+    ref = np.zeros((M, N))
+    r = 0
+    for e, m in enumerate(sizes):
+        ref[r:r + m] = np.float64(np.float32(0.37)) * np.float64(ws[e]) * (_e4m3_to_f64(x[r:r + m]) @ _e4m3_to_f64(w[e]).T)
+        r += m
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_gemm_rejects_bad_sizes():
+    E, N, K = 2, 8, 8
+    x, w = np.zeros((4, K), np.uint16), np.zeros((E, N, K), np.uint16)
+    for sizes in ([3, 2], [-1, 2]):   # past M; negative
+        with pytest.raises(ValueError):
+            oracle.grouped_gemm(oracle.BF16, E, N, K, x, w, sizes)
