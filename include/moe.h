@@ -277,6 +277,54 @@ typedef enum {
  * stream work has completed. [host, pure] */
 moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_plan *plan, int64_t *offsets);
 
+/*
+ * Grouped GEMM over pre-permuted contiguous per-expert segments: the EP-MoE workload of
+ * the aijishu article comparing FBGEMM's MoE grouped GEMM with SGLang's (tokens already
+ * grouped by expert; bf16 or fp8 per-tensor operands).  Segment e is rows
+ * [off_e, off_e + m_sizes[e]) of X, off_e = m_sizes[0] + ... + m_sizes[e-1]; each of its
+ * rows r gets
+ *     Y[r, n] = x_scale * w_scale[e] * sum_c X[r, c] * W[e, n, c]      (scales 1 for bf16)
+ * with fp32 accumulation, rounded to bf16 once.  Rows of Y past the last segment are not
+ * written.  The same grouped-GEMM kernels as moe_forward's GEMM2 (pipelined tiles only):
+ * blocks of a tile's height cut at segment ends, the partial last block of a segment
+ * computed but not stored.
+ */
+typedef struct {
+    int32_t num_groups;          /* E, 1..1024                                          */
+    int32_t N, K;                /* output columns; reduction length                    */
+    int32_t dtype;               /* MOE_DT_BF16, or MOE_DT_FP8_E4M3 (X and W as E4M3
+                                    codes with per-tensor scales)                       */
+    const void *w;               /* [device] W [E, N, K], K contiguous, 16-byte aligned */
+    const float *w_scale;        /* [device] fp8: [E] per-expert scales (NULL for bf16) */
+} moe_grouped_gemm_desc;
+
+/* The tile moe_grouped_gemm uses for M rows when given tile = -1 (a pipelined tile id of
+ * the dtype, listed like the layer's).  MOE_ERR_INVALID_ARGUMENT for an invalid
+ * descriptor, MOE_ERR_UNSUPPORTED when no compiled tile divides N and K. [host, pure] */
+moe_status moe_grouped_gemm_default_tile(const moe_grouped_gemm_desc *desc, int32_t M, int32_t *tile);
+
+/* Workspace bytes of moe_grouped_gemm for M rows and `tile` (-1: default). [host, pure] */
+moe_status moe_grouped_gemm_workspace_bytes(const moe_grouped_gemm_desc *desc, int32_t M, int32_t tile,
+                                            size_t *bytes);
+
+/* Enqueue the grouped GEMM on `stream` (no host synchronisation: the sizes stay on the
+ * device; graph-capturable).
+ *  M          rows of X and Y [host]; the sizes must sum to at most M (rows past M are
+ *             never read or written; sizes past it are clamped there, negative ones
+ *             read as 0)
+ *  x          [device] X [M, K] bf16 or E4M3, 16-byte aligned
+ *  x_scale    [device] fp8: the per-tensor activation scale (fp32 scalar); NULL for bf16
+ *  m_sizes    [device] int32 [E]
+ *  y          [device] Y [M, N] bf16, 16-byte aligned
+ *  workspace  [device] at least moe_grouped_gemm_workspace_bytes, 256-byte aligned
+ *  tile       a pipelined tile id of the dtype whose BN divides N and BK divides K, or -1
+ * Errors: MOE_ERR_INVALID_ARGUMENT (checked before anything is enqueued),
+ * MOE_ERR_UNSUPPORTED when M*K bytes of X exceed 2^32 - 1 (32-bit row offsets),
+ * MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP. */
+moe_status moe_grouped_gemm(const moe_grouped_gemm_desc *desc, int32_t M, const void *x, const float *x_scale,
+                            const int32_t *m_sizes, void *y, void *workspace, size_t workspace_bytes,
+                            int32_t tile, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ WS_REGIONS = ("topk_ids", "topk_weights", "sorted_ids", "expert_ids", "num_post_
 # every function include/moe.h declares (checked against the header by the tests)
 EXPORTS = ("moe_status_str", "moe_align_capacity", "moe_route", "moe_align", "moe_default_plan",
            "moe_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_plan_describe",
-           "moe_workspace_offsets")
+           "moe_workspace_offsets", "moe_grouped_gemm_default_tile", "moe_grouped_gemm_workspace_bytes",
+           "moe_grouped_gemm")
 
 
 class MoEError(RuntimeError):
@@ -49,6 +50,11 @@ class Layer(ctypes.Structure):
                 ("w13_s", ctypes.c_void_p), ("w13_z", ctypes.c_void_p),
                 ("w2_s", ctypes.c_void_p), ("w2_z", ctypes.c_void_p),
                 ("correction_bias", ctypes.c_void_p)]
+
+
+class GroupedGemmDesc(ctypes.Structure):
+    _fields_ = [("num_groups", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("w", ctypes.c_void_p), ("w_scale", ctypes.c_void_p)]
 
 
 class Plan(ctypes.Structure):
@@ -90,8 +96,13 @@ def lib():
                                            ctypes.POINTER(P), I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.moe_plan_describe.argtypes = [ctypes.POINTER(Layer), I32, ctypes.POINTER(Plan), ctypes.c_char_p, SZ]
         L.moe_workspace_offsets.argtypes = [ctypes.POINTER(Layer), I32, ctypes.POINTER(Plan), ctypes.POINTER(I64)]
+        G = ctypes.POINTER(GroupedGemmDesc)
+        L.moe_grouped_gemm_default_tile.argtypes = [G, I32, ctypes.POINTER(I32)]
+        L.moe_grouped_gemm_workspace_bytes.argtypes = [G, I32, I32, ctypes.POINTER(SZ)]
+        L.moe_grouped_gemm.argtypes = [G, I32, P, P, P, P, P, SZ, I32, P]
         for f in ("moe_route", "moe_align", "moe_default_plan", "moe_workspace_bytes", "moe_forward",
-                  "moe_forward_profiled", "moe_plan_describe", "moe_workspace_offsets"):
+                  "moe_forward_profiled", "moe_plan_describe", "moe_workspace_offsets",
+                  "moe_grouped_gemm_default_tile", "moe_grouped_gemm_workspace_bytes", "moe_grouped_gemm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,6 +201,34 @@ def moe_workspace_offsets(layer: Layer, T, plan: Plan = None) -> dict:
     _check(lib().moe_workspace_offsets(ctypes.byref(layer), T, ctypes.byref(plan) if plan else None, off),
            "moe_workspace_offsets")
     return {name: int(off[i]) for i, name in enumerate(WS_REGIONS)}
+
+
+def grouped_gemm_desc(w, dtype, w_scale=None) -> GroupedGemmDesc:
+    """Descriptor of a grouped GEMM over the device weights w [E, N, K] (bf16, or E4M3 codes
+    as uint8 with per-expert fp32 scales w_scale [E])."""
+    E, N, K = w.shape
+    return GroupedGemmDesc(E, N, K, dtype, _ptr(w), _ptr(w_scale))
+
+
+def moe_grouped_gemm_default_tile(desc: GroupedGemmDesc, M) -> int:
+    t = ctypes.c_int32()
+    _check(lib().moe_grouped_gemm_default_tile(ctypes.byref(desc), M, ctypes.byref(t)), "moe_grouped_gemm_default_tile")
+    return t.value
+
+
+def moe_grouped_gemm_workspace_bytes(desc: GroupedGemmDesc, M, tile=-1) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_grouped_gemm_workspace_bytes(ctypes.byref(desc), M, tile, ctypes.byref(n)),
+           "moe_grouped_gemm_workspace_bytes")
+    return n.value
+
+
+def moe_grouped_gemm(desc: GroupedGemmDesc, x, m_sizes, y, workspace, x_scale=None, tile=-1, stream=None):
+    """Y[r] = X[r] W[e]^T over the contiguous segments of m_sizes (device int32 [E])."""
+    M = x.shape[0]
+    _check(lib().moe_grouped_gemm(ctypes.byref(desc), M, _ptr(x), _ptr(x_scale), _ptr(m_sizes), _ptr(y),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), tile,
+                                  _stream(stream)), "moe_grouped_gemm")
 
 
 # ---- a layer object over device tensors ----------------------------------------------------

@@ -127,7 +127,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 int r, chunk;
                 dma_lane<C::SB>(lane, rb, r, chunk);
                 const int p = a.sorted[row0 + r];
-                const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + r;
+                const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0)
+                                     : a.gather_a       ? (p < a.pairs ? p : 0)
+                                                        : row0 + r;
                 // a filler row's products are never read back, so its LDS row may keep stale
                 // data; the lanes of the instruction's first row always load, so every load
                 // instruction runs with a non-empty mask and counts in vmcnt
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                     const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
                     const int p = a.sorted[row];
                     if (p >= a.pairs) continue;   // filler row: never read back
-                    const float w = a.topk_w[p] * scale;
+                    const float w = (a.topk_w ? a.topk_w[p] : 1.0f) * scale;   // the grouped GEMM has no weight
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const int col = nt * C::BN + wn * C::TN + fn * C::MS + lcol;

@@ -63,6 +63,7 @@ struct GemmArgs {
     float *tail_P;               // fp32 [S, tail rows, ldc]
     int32_t *tail_info;          // written by workgroup 0: first tail row, S (0: none), plane elements
     int expert_groups;           // > 0: tile groups of an expert's row blocks, at most this many (set by the launcher)
+    int gather_a;                // down: A row of block row r is sorted[r] (not r); the grouped GEMM
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
@@ -167,6 +168,16 @@ struct PrologueArgs {
     uint32_t *h_amax;            // cleared to 0 (GEMM1's |h| maximum), may be null
 };
 hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s);
+
+// Block layout of a grouped GEMM over contiguous segments (grouped.hip): E <= 1024.
+struct SegmentArgs {
+    const int32_t *m_sizes;      // [E] rows per segment (device)
+    int E, M, BM;
+    int32_t *sorted;             // [capacity] source row of each block row, M for padding
+    int32_t *eids;               // [capacity / BM] segment of each block
+    int32_t *npp;                // [1] block rows
+};
+hipError_t launch_segments(const SegmentArgs &a, hipStream_t s);
 
 int device_cu_count();
 

@@ -423,6 +423,64 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     return MOE_OK;
 }
 
+// ---- grouped GEMM over contiguous segments ----------------------------------------
+
+constexpr int kMaxGroups = 1024;   // the segment layout runs in one 1024-thread workgroup
+
+moe_status check_grouped(const moe_grouped_gemm_desc *d, int32_t tile, TileInfo *t) {
+    if (!d) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->num_groups < 1 || d->num_groups > kMaxGroups || d->N < 1 || d->K < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->dtype != MOE_DT_BF16 && d->dtype != MOE_DT_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+    if (!d->w || !aligned(d->w, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->dtype == MOE_DT_FP8_E4M3 && (!d->w_scale || !aligned(d->w_scale, 4))) return MOE_ERR_INVALID_ARGUMENT;
+    // the pipelined tiles only (they gather A rows through the layout)
+    if (tile < 0 || !gemm_tile_info(d->dtype, tile, t) || t->stages == 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->N % t->BN || d->K % t->BK) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+// Default tile by rows per group r = M / E: narrow blocks while the weights stream, wider
+// tiles as the products grow (the same tiles as the layer's GEMM2 plans, from timing the
+// Qwen2-57B TP4 w13 shape on MI355X).
+int32_t grouped_default_tile(const moe_grouped_gemm_desc *d, int32_t M) {
+    const double r = (double)M / d->num_groups;
+    static const int bf16[][2] = {{24, 9}, {96, 11}, {384, 22}, {1 << 30, 25}};
+    static const int fp8[][2] = {{24, 9}, {96, 10}, {384, 16}, {1 << 30, 14}};
+    const int (*rows)[2] = d->dtype == MOE_DT_FP8_E4M3 ? fp8 : bf16;
+    TileInfo t;
+    int first = 0;
+    while (first < 3 && r > rows[first][0]) first++;
+    for (int dd = 0; dd < 8; dd++) {   // the row's tile, else the nearest that tiles N and K
+        const int i = dd % 2 == 0 ? first + dd / 2 : first - (dd + 1) / 2;
+        if (i < 0 || i > 3) continue;
+        if (check_grouped(d, rows[i][1], &t) == MOE_OK) return rows[i][1];
+    }
+    for (int g = 0; g < 64; g++)
+        if (check_grouped(d, g, &t) == MOE_OK) return g;
+    return -1;
+}
+
+struct GroupedWorkspace {
+    size_t sorted, eids, npp, total;
+    int64_t cap;
+};
+
+GroupedWorkspace grouped_layout(const moe_grouped_gemm_desc *d, int32_t M, int BM) {
+    GroupedWorkspace w{};
+    w.cap = moe_align_capacity(M, 1, d->num_groups, BM);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + bytes, kAlign);
+        return at;
+    };
+    w.sorted = take((size_t)w.cap * 4);
+    w.eids = take((size_t)w.cap / BM * 4);
+    w.npp = take(4);
+    w.total = o;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -589,6 +647,81 @@ moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_pl
     const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos,
                                     w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p, w.tail};
     for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
+    return MOE_OK;
+}
+
+moe_status moe_grouped_gemm_default_tile(const moe_grouped_gemm_desc *desc, int32_t M, int32_t *tile) {
+    if (!desc || !tile || M < 0) return MOE_ERR_INVALID_ARGUMENT;
+    TileInfo t;
+    if (desc->num_groups < 1 || desc->num_groups > kMaxGroups) return MOE_ERR_INVALID_ARGUMENT;
+    const int32_t g = grouped_default_tile(desc, M);
+    if (g < 0) return check_grouped(desc, 0, &t) == MOE_OK ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARGUMENT;
+    *tile = g;
+    return MOE_OK;
+}
+
+moe_status moe_grouped_gemm_workspace_bytes(const moe_grouped_gemm_desc *desc, int32_t M, int32_t tile,
+                                            size_t *bytes) {
+    if (!bytes || M < 0) return MOE_ERR_INVALID_ARGUMENT;
+    moe_status st;
+    if (tile < 0 && (st = moe_grouped_gemm_default_tile(desc, M, &tile)) != MOE_OK) return st;
+    TileInfo t;
+    if ((st = check_grouped(desc, tile, &t)) != MOE_OK) return st;
+    *bytes = grouped_layout(desc, M, t.BM).total;
+    return MOE_OK;
+}
+
+moe_status moe_grouped_gemm(const moe_grouped_gemm_desc *desc, int32_t M, const void *x, const float *x_scale,
+                            const int32_t *m_sizes, void *y, void *workspace, size_t workspace_bytes, int32_t tile,
+                            void *stream) {
+    if (M < 0) return MOE_ERR_INVALID_ARGUMENT;
+    moe_status st;
+    if (tile < 0 && (st = moe_grouped_gemm_default_tile(desc, M, &tile)) != MOE_OK) return st;
+    TileInfo t;
+    if ((st = check_grouped(desc, tile, &t)) != MOE_OK) return st;
+    if (M == 0) return MOE_OK;
+    if (!x || !m_sizes || !y || !workspace || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, kAlign) ||
+        !aligned(m_sizes, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const bool fp8 = desc->dtype == MOE_DT_FP8_E4M3;
+    if (fp8 && (!x_scale || !aligned(x_scale, 4))) return MOE_ERR_INVALID_ARGUMENT;
+    const GroupedWorkspace w = grouped_layout(desc, M, t.BM);
+    if (workspace_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t ebytes = fp8 ? 1 : 2;
+    // the GEMM addresses rows of X with 32-bit byte offsets from its base
+    if ((int64_t)M * desc->K * ebytes > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    int32_t *sorted = (int32_t *)(ws + w.sorted), *eids = (int32_t *)(ws + w.eids), *npp = (int32_t *)(ws + w.npp);
+    hipError_t err;
+    SegmentArgs sa{m_sizes, desc->num_groups, M, t.BM, sorted, eids, npp};
+    if ((err = launch_segments(sa, s)) != hipSuccess) return MOE_ERR_HIP;
+    GemmArgs g{};
+    g.A = x;
+    g.lda = desc->K;
+    g.B = desc->w;
+    g.ldb = desc->K * ebytes;
+    g.b_expert_stride = (int64_t)desc->N * desc->K * ebytes;
+    g.C = y;
+    g.ldc = desc->N;
+    g.sorted = sorted;
+    g.eids = eids;
+    g.npp = npp;
+    g.topk_w = nullptr;
+    g.K = desc->K;
+    g.N = desc->N;
+    g.top_k = 1;
+    g.pairs = M;
+    g.split = 1;
+    g.ksplit = desc->K;
+    g.a_scale = x_scale;
+    g.b_scale = desc->w_scale;
+    g.out_by_pair = 1;
+    g.gather_a = 1;
+    // weight streaming (about one block per group): stagger the K walks over DRAM channels
+    g.rotate_k = (int64_t)M <= (int64_t)desc->num_groups * t.BM;
+    if ((err = launch_gemm(desc->dtype, tile, GEMM_DOWN, false, g, w.cap / t.BM * (desc->N / t.BN), s)) != hipSuccess)
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 

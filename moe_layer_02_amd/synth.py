@@ -245,3 +245,23 @@ def expert_weights(cfg: LayerConfig, device: str = "cpu") -> ExpertWeights:
             w2[e], s2[e], z2[e] = _int4_encode(mat(_T_W2, e, H, I))
         return ExpertWeights(WDT_INT4, w13, w2, w13_s=s13, w13_z=z13, w2_s=s2, w2_z=z2)
     raise ValueError("unknown weight dtype")
+
+
+_T_GG_X, _T_GG_SIZES = 20, 21
+
+
+def grouped_gemm_inputs(cfg: LayerConfig, T: int):
+    """Inputs of the EP-MoE grouped GEMM on a layer's w13 (W [E, 2I, H]: N = 2I, K = H):
+    M = T*k rows grouped by expert in contiguous segments, the sizes counted from T*k
+    expert draws (the config's Zipf popularity, else uniform); X [M, H] ~ N(0, 1) -- bf16,
+    or for fp8 weights E4M3 codes of X / s with the per-tensor scale s = amax / 448.
+    Returns (x on the host, x_scale fp32 [1] or None, m_sizes int32 [E])."""
+    M = T * cfg.k
+    rng = _rng(cfg.seed, _T_GG_SIZES, T)
+    p = zipf_popularity(cfg) if cfg.zipf_s > 0 else np.full(cfg.E, 1.0 / cfg.E)
+    sizes = np.bincount(rng.choice(cfg.E, size=M, p=p), minlength=cfg.E).astype(np.int32)
+    x32 = _rng(cfg.seed, _T_GG_X, T).standard_normal((M, cfg.H), dtype=np.float32)
+    if cfg.wdtype == WDT_FP8:
+        codes, scale = _fp8_encode(x32)
+        return codes, torch.tensor([scale], dtype=torch.float32), torch.from_numpy(sizes)
+    return _bf16(x32), None, torch.from_numpy(sizes)

@@ -50,6 +50,8 @@ int main(void) {
   printf("%zu %zu %zu %zu\\n", offsetof(moe_layer, route), offsetof(moe_layer, w13),
          offsetof(moe_layer, w13_s), offsetof(moe_layer, correction_bias));
   printf("%zu %zu\\n", offsetof(moe_route_cfg, routed_scaling), offsetof(moe_route_cfg, logits_dtype));
+  printf("%zu %zu %zu\\n", sizeof(moe_grouped_gemm_desc), offsetof(moe_grouped_gemm_desc, w),
+         offsetof(moe_grouped_gemm_desc, w_scale));
   return 0;
 }
 """)
@@ -60,6 +62,8 @@ int main(void) {
     assert got[1] == [abi.Layer.route.offset, abi.Layer.w13.offset, abi.Layer.w13_s.offset,
                       abi.Layer.correction_bias.offset]
     assert got[2] == [abi.RouteCfg.routed_scaling.offset, abi.RouteCfg.logits_dtype.offset]
+    assert got[3] == [ctypes.sizeof(abi.GroupedGemmDesc), abi.GroupedGemmDesc.w.offset,
+                      abi.GroupedGemmDesc.w_scale.offset]
 
 
 def fake_layer(cfg, wdtype=None, **over):
@@ -250,3 +254,29 @@ def test_split_tail_rules():
         abi.moe_workspace_bytes(i4, 64, abi.Plan(32, 12, 12, 1, 0, 4))
     assert abi.moe_workspace_bytes(i4, 64, abi.Plan(32, 12, 12, 1)) > 0
     assert all(abi.moe_default_plan(i4, T).split_tail == 0 for T in (1, 64, 512))
+
+
+
+def test_grouped_gemm_host_checks():
+    """The EP grouped GEMM: default tiles divide N and K, the workspace holds the block
+    layout of M rows, invalid descriptors and tiles are rejected before any enqueue."""
+    fake = 0x10000
+    d = abi.GroupedGemmDesc(64, 1280, 3584, abi.DT_BF16, fake, None)
+    for M in (0, 1, 8, 300, 2048, 32768):
+        t = abi.moe_grouped_gemm_default_tile(d, M)
+        n = abi.moe_grouped_gemm_workspace_bytes(d, M, t)
+        assert n >= 4 * M and n == abi.moe_grouped_gemm_workspace_bytes(d, M)   # a source row per block row
+    f8 = abi.GroupedGemmDesc(64, 1280, 3584, abi.DT_FP8_E4M3, fake, fake)
+    assert abi.moe_grouped_gemm_default_tile(f8, 4096) >= 0
+    for bad in [abi.GroupedGemmDesc(0, 1280, 3584, abi.DT_BF16, fake, None),        # no groups
+                abi.GroupedGemmDesc(2048, 1280, 3584, abi.DT_BF16, fake, None),     # more than 1024
+                abi.GroupedGemmDesc(64, 1280, 3584, abi.DT_INT4_G128, fake, None),  # int4 not offered
+                abi.GroupedGemmDesc(64, 1280, 3584, abi.DT_FP8_E4M3, fake, None),   # fp8 without scales
+                abi.GroupedGemmDesc(64, 1280, 3584, abi.DT_BF16, 0x10001, None)]:   # misaligned W
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_grouped_gemm_workspace_bytes(bad, 64)
+        assert ei.value.status == abi.MOE_ERR_INVALID_ARGUMENT
+    with pytest.raises(abi.MoEError):
+        abi.moe_grouped_gemm_workspace_bytes(d, 64, 0)        # a register-staged tile
+    with pytest.raises(abi.MoEError):
+        abi.moe_grouped_gemm_workspace_bytes(abi.GroupedGemmDesc(64, 1000, 3584, abi.DT_BF16, fake, None), 64)
