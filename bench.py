@@ -260,6 +260,122 @@ def cpu_baseline(b: Bench, T, budget_s=15.0):
                 sample="%d of %d tokens (random), routing of all %d; %.1f s" % (n, T, T, el + t_route))
 
 
+# ---- the EP-MoE grouped GEMM (pre-permuted contiguous segments) ------------------------
+
+GG_METRIC = "EP-MoE grouped GEMM tokens/s + TFLOP/s & HBM GB/s (% of roofline) vs batch, 1 GPU"
+
+
+def grouped_gemm_bench(args):
+    """moe_grouped_gemm on Qwen2-57B-A14B TP4's w13 (E = 64 experts, N = 1280, K = 3584) with
+    the batch's T*8 routed rows grouped by expert (synthetic sizes): the pages' FBGEMM vs
+    SGLang grouped-GEMM sweep.  The op (the segment-layout kernel and the GEMM) is timed by
+    HIP events around graph replays on its stream."""
+    base = synth.CONFIGS["qwen2"]
+    cfg = base if args.dtype == "fp8" else base.with_shape(name="qwen2_bf16", wdtype=synth.WDT_BF16)
+    fp8 = cfg.wdtype == synth.WDT_FP8
+    w = synth.expert_weights(cfg, device="cuda")
+    W, Ws = w.w13, w.w13_scale
+    desc = abi.grouped_gemm_desc(W, abi.DT_FP8_E4M3 if fp8 else abi.DT_BF16, Ws)
+    N, K = 2 * cfg.I, cfg.H
+    flush = torch.ones((FLUSH_BYTES // 4096, 1024), dtype=torch.float32, device="cuda")
+    flush_out = torch.empty(1024, dtype=torch.float32, device="cuda")
+
+    def run_T(T, steps, warmup):
+        x, xs, sizes = synth.grouped_gemm_inputs(cfg, T)
+        M = x.shape[0]
+        x, sizes = x.cuda(), sizes.cuda()
+        xs = None if xs is None else xs.cuda()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        tile = abi.moe_grouped_gemm_default_tile(desc, M)
+        ws = torch.empty(abi.moe_grouped_gemm_workspace_bytes(desc, M, tile), dtype=torch.uint8, device="cuda")
+        abi.moe_grouped_gemm(desc, x, sizes, y, ws, x_scale=xs, tile=tile)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                abi.moe_grouped_gemm(desc, x, sizes, y, ws, x_scale=xs, tile=tile)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        cold = []
+        for _ in range(max(steps, 10)):
+            torch.amax(flush, dim=0, out=flush_out)
+            t0.record()
+            g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            cold.append(t0.elapsed_time(t1))
+        active = int((sizes > 0).sum())
+        flops = 2.0 * M * N * K
+        mbytes = active * N * K * (1.0 if fp8 else 2.0) + M * K * (1.0 if fp8 else 2.0) + M * N * 2.0
+        peak = PEAK_MFMA[cfg.wdtype]
+        sec = ms / 1e3
+        c50 = float(np.median(cold))
+        return dict(T=T, rows=M, tile=tile, ms_per_step=round(ms, 4), tokens_per_s=round(T / sec, 2),
+                    tflops=round(flops / sec / 1e12, 3), hbm_gbps=round(mbytes / sec / 1e9, 2),
+                    roofline_frac=round(max(mbytes / PEAK_HBM, flops / peak) / sec, 4),
+                    bound="hbm" if mbytes / PEAK_HBM >= flops / peak else "mfma",
+                    cold_ms=round(c50, 4), flops=flops, min_bytes=mbytes, active_experts=active)
+
+    T = args.tokens or 4096
+    head = run_T(T, args.steps, args.warmup)
+    sweep = [run_T(t, args.steps, args.warmup) for t in [int(v) for v in args.sweep.split(",") if v.strip()]
+             if t != T]
+    bound_mfma = head["bound"] == "mfma"
+    dur = head["ms_per_step"] * 1e-3
+    roof = dict(kernel="grouped_gemm (segment layout + GEMM)", bound=head["bound"],
+                achieved=round(head["flops"] / dur / 1e12, 2) if bound_mfma else round(head["min_bytes"] / dur / 1e9, 2),
+                peak=PEAK_MFMA[cfg.wdtype] / 1e12 if bound_mfma else PEAK_HBM / 1e9,
+                unit="TFLOP/s" if bound_mfma else "GB/s", frac=head["roofline_frac"], traffic=None,
+                avg_us=round(head["ms_per_step"] * 1e3, 2))
+    cpu = None
+    if not args.no_cpu_baseline:   # the oracle on a bounded sample of rows
+        import oracle
+        x, xs, sizes = synth.grouped_gemm_inputs(cfg, T)
+        sizes = sizes.numpy()
+        xb = x.numpy() if fp8 else x.contiguous().view(torch.int16).numpy().view(np.uint16)
+        wh = W.cpu()
+        wb = wh.numpy() if fp8 else wh.view(torch.int16).numpy().view(np.uint16)
+        rows, el = 0, 0.0
+        starts = np.concatenate([[0], np.cumsum(sizes)])
+        for e in range(cfg.E):
+            if el > 15.0:
+                break
+            if sizes[e] == 0:
+                continue
+            sub = np.zeros(cfg.E, np.int32)
+            sub[e] = 1
+            t0 = time.time()
+            oracle.grouped_gemm(oracle.FP8_E4M3 if fp8 else oracle.BF16, cfg.E, N, K, xb[starts[e]:starts[e] + 1], wb,
+                                sub, x_scale=1.0 if xs is None else float(xs[0]),
+                                w_scale=None if Ws is None else Ws.cpu().numpy())
+            el += time.time() - t0
+            rows += 1
+        cpu = dict(value=round(rows / el / cfg.k, 4), unit="tokens/s", cores=1, kind="oracle",
+                   sample="%d rows (one per expert), %.1f s; tokens/s = rows/s / k" % (rows, el))
+    line = {
+        "metric": GG_METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE_NAME[cfg.wdtype], "data": "synthetic (seeded sizes and inputs)",
+        "config": {"workload": "EP-MoE grouped GEMM, Qwen2-57B-A14B TP4 w13 (E=64, N=1280, K=3584, top-8 rows, %s)"
+                   % ("fp8 per-tensor" if fp8 else "bf16"), "T": T, "rows": head["rows"], "tile": head["tile"]},
+        "tflops": head["tflops"], "hbm_gbps": head["hbm_gbps"], "roofline_frac": head["roofline_frac"],
+        "cold_ms": head["cold_ms"], "roofline": roof, "cpu_baseline": cpu,
+        "sweep": [{k: v for k, v in m.items() if k not in ("flops", "min_bytes")} for m in sweep],
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +386,9 @@ def main():
     ap.add_argument("--sweep", default="1,32,256,1024,4096", help="comma-separated T values ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--plan", default=None, help="block_m,gemm1_tile,gemm2_tile,split_k for the headline T")
+    ap.add_argument("--workload", default="layer", choices=("layer", "grouped_gemm"),
+                    help="the fused layer (default) or the EP-MoE grouped GEMM over pre-grouped rows")
+    ap.add_argument("--dtype", default="fp8", choices=("bf16", "fp8"), help="grouped_gemm: operand type")
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="after timing, one device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -278,6 +397,11 @@ def main():
               "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
+    if args.workload == "grouped_gemm":
+        if args.sweep == "1,32,256,1024,4096":
+            args.sweep = "1,2,4,8,16,32,64,128,256,512,1024,2048"
+        grouped_gemm_bench(args)
+        return
     cfg = synth.CONFIGS[args.config]
     T = args.tokens or cfg.t_max
     plan = abi.Plan(*[int(v) for v in args.plan.split(",")]) if args.plan else None

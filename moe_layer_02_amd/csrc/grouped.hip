@@ -6,8 +6,12 @@
 // expert per block; this kernel lays the segments out as such blocks without moving data:
 // block b of segment e covers its rows BM*(b - first block of e) ..., sorted[] names each
 // block row's source row (M for the padding past a segment's end), expert_ids[] each
-// block's segment, and num_post_pad the number of block rows.  One 1024-thread workgroup,
-// so the sizes stay on the device (no host synchronisation).
+// block's segment, and num_post_pad the number of block rows.  Each 1024-thread workgroup
+// takes the prefix sums of all sizes (at most 1024) itself and lays out its share of the
+// rows, so the sizes stay on the device (no host synchronisation) and no workgroup waits
+// for another.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -30,36 +34,43 @@ __device__ int block_scan(int v, int *buf) {
 }
 
 __global__ __launch_bounds__(1024) void k_segments(SegmentArgs a) {
-    __shared__ int scan[1024], seg_start[1024], seg_len[1024], blk_start[1024];
-    __shared__ int total_blocks;
+    __shared__ int scan[1024], seg_start[1024], seg_len[1024], blk_end[1024];
     const int t = threadIdx.x;
     const int m = t < a.E ? max(a.m_sizes[t], 0) : 0;
     const int end = block_scan(m, scan);                      // rows through segment t
     // segments are clamped to the M rows of X (sizes past M are a caller error; their
     // rows are not read or written)
     const int start = min(end - m, a.M), len = min(end, a.M) - start;
-    const int blocks = (len + a.BM - 1) / a.BM;
-    const int bend = block_scan(blocks, scan);
+    const int blocks = (len + a.BM - 1) >> a.bm_shift;
+    const int bend = block_scan(blocks, scan);                // blocks through segment t
     seg_start[t] = start;
     seg_len[t] = len;
-    blk_start[t] = bend - blocks;
-    if (t == 1023) total_blocks = bend;
+    blk_end[t] = bend;
     __syncthreads();
-    for (int b = 0; b < blocks; b++) a.eids[blk_start[t] + b] = t;
-    if (t == 0) *a.npp = total_blocks * a.BM;
-    __syncthreads();                                          // expert_ids visible to the workgroup
-    const int rows = total_blocks * a.BM;
-    for (int i = t; i < rows; i += 1024) {
-        const int e = a.eids[i / a.BM];
-        const int r = i - blk_start[e] * a.BM;
-        a.sorted[i] = r < seg_len[e] ? seg_start[e] + r : a.M;
+    const int total_blocks = blk_end[1023];
+    if (blockIdx.x == 0 && t == 0) *a.npp = total_blocks << a.bm_shift;
+    const int rows = total_blocks << a.bm_shift;
+    // every workgroup computed the same prefix sums; each lays out its share of the rows
+    for (int i = blockIdx.x * 1024 + t; i < rows; i += gridDim.x * 1024) {
+        const int b = i >> a.bm_shift;
+        int lo = 0, hi = a.E - 1;                             // the first segment ending past block b
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (blk_end[mid] > b) hi = mid;
+            else lo = mid + 1;
+        }
+        const int r = i - ((blk_end[lo] - ((seg_len[lo] + a.BM - 1) >> a.bm_shift)) << a.bm_shift);
+        a.sorted[i] = r < seg_len[lo] ? seg_start[lo] + r : a.M;
+        if ((i & (a.BM - 1)) == 0) a.eids[b] = lo;
     }
 }
 
 }  // namespace
 
-hipError_t launch_segments(const SegmentArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_segments, dim3(1), dim3(1024), 0, s, a);
+hipError_t launch_segments(const SegmentArgs &a, int64_t capacity, hipStream_t s) {
+    // about two rows per thread, up to 128 workgroups
+    const int64_t g = std::min<int64_t>(128, std::max<int64_t>(1, (capacity + 2047) / 2048));
+    hipLaunchKernelGGL(k_segments, dim3((unsigned)g), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 

@@ -169,15 +169,16 @@ struct PrologueArgs {
 };
 hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s);
 
-// Block layout of a grouped GEMM over contiguous segments (grouped.hip): E <= 1024.
+// Block layout of a grouped GEMM over contiguous segments (grouped.hip): E <= 1024, BM a
+// power of two; capacity = rows of sorted[].
 struct SegmentArgs {
     const int32_t *m_sizes;      // [E] rows per segment (device)
-    int E, M, BM;
+    int E, M, BM, bm_shift;      // BM = 1 << bm_shift
     int32_t *sorted;             // [capacity] source row of each block row, M for padding
     int32_t *eids;               // [capacity / BM] segment of each block
     int32_t *npp;                // [1] block rows
 };
-hipError_t launch_segments(const SegmentArgs &a, hipStream_t s);
+hipError_t launch_segments(const SegmentArgs &a, int64_t capacity, hipStream_t s);
 
 int device_cu_count();
 

@@ -435,17 +435,17 @@ moe_status check_grouped(const moe_grouped_gemm_desc *d, int32_t tile, TileInfo 
     if (d->dtype == MOE_DT_FP8_E4M3 && (!d->w_scale || !aligned(d->w_scale, 4))) return MOE_ERR_INVALID_ARGUMENT;
     // the pipelined tiles only (they gather A rows through the layout)
     if (tile < 0 || !gemm_tile_info(d->dtype, tile, t) || t->stages == 0) return MOE_ERR_INVALID_ARGUMENT;
-    if (d->N % t->BN || d->K % t->BK) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->N % t->BN || d->K % t->BK || (t->BM & (t->BM - 1))) return MOE_ERR_INVALID_ARGUMENT;
     return MOE_OK;
 }
 
 // Default tile by rows per group r = M / E: narrow blocks while the weights stream, wider
-// tiles as the products grow (the same tiles as the layer's GEMM2 plans, from timing the
-// Qwen2-57B TP4 w13 shape on MI355X).
+// tiles as the products grow (from timing every tile on the Qwen2-57B TP4 w13 shape,
+// M = 8..32768 rows, on MI355X).
 int32_t grouped_default_tile(const moe_grouped_gemm_desc *d, int32_t M) {
     const double r = (double)M / d->num_groups;
-    static const int bf16[][2] = {{24, 9}, {96, 11}, {384, 22}, {1 << 30, 25}};
-    static const int fp8[][2] = {{24, 9}, {96, 10}, {384, 16}, {1 << 30, 14}};
+    static const int bf16[][2] = {{24, 9}, {96, 11}, {384, 22}, {1 << 30, 26}};
+    static const int fp8[][2] = {{24, 9}, {96, 10}, {1 << 30, 16}, {1 << 30, 16}};
     const int (*rows)[2] = d->dtype == MOE_DT_FP8_E4M3 ? fp8 : bf16;
     TileInfo t;
     int first = 0;
@@ -694,8 +694,8 @@ moe_status moe_grouped_gemm(const moe_grouped_gemm_desc *desc, int32_t M, const 
     char *ws = (char *)workspace;
     int32_t *sorted = (int32_t *)(ws + w.sorted), *eids = (int32_t *)(ws + w.eids), *npp = (int32_t *)(ws + w.npp);
     hipError_t err;
-    SegmentArgs sa{m_sizes, desc->num_groups, M, t.BM, sorted, eids, npp};
-    if ((err = launch_segments(sa, s)) != hipSuccess) return MOE_ERR_HIP;
+    SegmentArgs sa{m_sizes, desc->num_groups, M, t.BM, nbits_for(t.BM), sorted, eids, npp};
+    if ((err = launch_segments(sa, w.cap, s)) != hipSuccess) return MOE_ERR_HIP;
     GemmArgs g{};
     g.A = x;
     g.lda = desc->K;
