@@ -171,6 +171,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                     lds_dma_off<16>((is_a[q] ? base_a : base_b) + koff, voff[q], st + dst[q]);
         };
 
+        // A block holds its expert's rows first and padding after them, so a wave row range
+        // with no real row starts with padding: such waves (the tail block of an expert at
+        // large block heights) skip their LDS reads and MFMAs but still load and synchronise
+        const bool wave_rows = __builtin_amdgcn_readfirstlane(a.sorted[row0 + wm * C::TM] < a.pairs);
         using Acc = typename AccOf<C::MS>::type;
         constexpr int NR = C::MS == 32 ? 16 : 4;              // accumulator values per lane per fragment
         Acc acc[C::FM][C::FN];
@@ -192,6 +196,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             block_barrier();
             if (kt + C::ST - 1 < nku) issue(kt + C::ST - 1);
             const char *sa = smem + (kt % C::ST) * C::STAGE, *sb = sa + C::A_STAGE;
+            if (wave_rows) {   // a wave whose rows are all padding only loads and keeps step
             // Fragments of step k + 1 can be read while the MFMAs of step k run (see DB below).
             if constexpr (WT == WT_BF16 && C::MS == 32) {
                 // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step.
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                             acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 af[sl & 1][fm], bfr[sl & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
                 }
+            }
             }
         }
 
