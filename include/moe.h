@@ -106,8 +106,10 @@ typedef struct {
  *  weight_dtype MOE_DT_FP8_E4M3: w13/w2 E4M3 codes, same shapes; w13_scale, w2_scale fp32
  *                                [E] (weight = code * scale of its expert and matrix).
  *  weight_dtype MOE_DT_INT4_G128: w13 uint8 [E, 2I, H/2], w2 uint8 [E, H, I/2];
- *                                w13_s, w13_z fp16 [E, 2I, H/128]; w2_s, w2_z fp16
- *                                [E, H, I/128].
+ *                                scales and zero points group-major: w13_s, w13_z fp16
+ *                                [E, H/128, 2I]; w2_s, w2_z fp16 [E, I/128, H] (the group
+ *                                g of row n of expert e at [e][g][n], so one group's
+ *                                values for consecutive rows are contiguous).
  * Rows [0, I) of each w13 matrix are the gate projection (through SiLU), rows [I, 2I) the
  * up projection.  correction_bias: fp32 [E] for the grouped gate (required there), optional
  * for SIGMOID, ignored for SOFTMAX.  Weight pointers must be 16-byte aligned; scale and bias

@@ -141,7 +141,9 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
             const int kb = WT == WT_FP8 ? kbase : WT == WT_INT4 ? kbase / 2 : kbase * 2;
             b_src[it] = bexp + grow * a.ldb + kb + ch * 16;
         }
-        // int4: this lane's B rows (one per N fragment) for scale / zero lookups
+        // int4: this lane's B rows (one per N fragment) for scale / zero lookups; the
+        // scales are group-major, sz_rows (the matrix's rows) apart from group to group
+        const int64_t sz_rows = KIND == GEMM_GATE_UP ? 2 * (int64_t)a.I : a.N;
         int64_t sz_row[C::FN];
 #pragma unroll
         for (int fn = 0; fn < C::FN; fn++) {
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
             } else {
                 grow = (int64_t)nt * C::BN + rr;
             }
-            sz_row[fn] = (int64_t)e * a.sz_expert_stride + grow * (a.K / 128);
+            sz_row[fn] = (int64_t)e * a.sz_expert_stride + grow;   // group-major [K/128][rows]
         }
 
         uint4 ra[C::A_IT], rb[C::B_IT];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                 for (int g = 0; g < C::GROUPS; g++)
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
-                        const int64_t gi = sz_row[fn] + (kbase + koff) / 128 + g;
+                        const int64_t gi = sz_row[fn] + (int64_t)((kbase + koff) / 128 + g) * sz_rows;
                         rs[g][fn] = a.bs[gi];
                         rz[g][fn] = a.bz[gi];
                     }

@@ -42,7 +42,18 @@ struct ICfg {
     static constexpr int A_SLABS = 4;                          // 4 x 64 fp16 per A row
     static constexpr int A_STAGE = A_SLABS * BM * 128, B_STAGE = BN * 128, SZ = BN * 4;
     static constexpr int STAGE = A_STAGE + B_STAGE + 2 * SZ;
-    static constexpr int A_LOADS = A_SLABS * BM / 8, B_LOADS = BN / 8, SZ_LOADS = 2 * BN / 64;
+    static constexpr int A_LOADS = A_SLABS * BM / 8, B_LOADS = BN / 8;
+    // a stage's scales (and zero points) are 2 groups x BN rows of fp16, two contiguous
+    // runs of the group-major arrays: BN / 4 chunks of 16 bytes, spread over SZ_PARTS
+    // instructions each, with SZ_PARTS the fewest that keep every wave's load count equal
+    static constexpr int sz_parts() {
+        int p = 1;
+        while ((A_LOADS + B_LOADS + 2 * p) % NW) p++;
+        return p;
+    }
+    static constexpr int SZ_PARTS = sz_parts(), SZ_LOADS = 2 * SZ_PARTS;
+    static constexpr int SZ_LANES = (BN / 4 + SZ_PARTS - 1) / SZ_PARTS;   // chunks per instruction
+    static_assert(SZ_LANES <= 64 && (SZ_PARTS - 1) * SZ_LANES < BN / 4, "every part instruction loads");
     static constexpr int LOADS = A_LOADS + B_LOADS + SZ_LOADS;
     static constexpr int LPW = LOADS / NW;
     static_assert(LOADS % NW == 0, "stage loads must split evenly over the waves");
@@ -85,7 +96,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
     const int total = mn * a.split;
     const int G = gridDim.x;
     const int nk = a.ksplit / C::BK;
-    const int groups_per_row = a.K / 128;
+    const int64_t sz_rows = KIND == GEMM_GATE_UP ? 2 * (int64_t)a.I : a.N;   // rows of the B matrix
 
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
         const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
@@ -129,11 +140,18 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                 voff[q] = (uint32_t)(b_row(rr) * a.ldb + chunk * 16);
                 dst[q] = C::A_STAGE + rb * 128;
                 kind[q] = LD_B;
-            } else {   // 64 rows' scale (or zero) pairs: 4 bytes per lane
+            } else {   // scales (or zero points): chunk c = 8 rows of group c / (BN / 8)
                 const int j = ins - C::A_LOADS - C::B_LOADS;
-                const int which = j / (C::BN / 64), r0 = j % (C::BN / 64) * 64;
-                voff[q] = (uint32_t)(b_row(r0 + lane) * groups_per_row * 2);
-                dst[q] = C::A_STAGE + C::B_STAGE + which * C::SZ + r0 * 4;
+                const int which = j / C::SZ_PARTS, c = j % C::SZ_PARTS * C::SZ_LANES + lane;
+                const int grp = c / (C::BN / 8), t0 = c % (C::BN / 8) * 8;   // t0: tile row in global order
+                int64_t grow;
+                if (KIND == GEMM_GATE_UP)   // the tile's gate rows, then its up rows
+                    grow = t0 < C::BN / 2 ? nt * (C::BN / 2) + t0 : a.I + nt * (C::BN / 2) + (t0 - C::BN / 2);
+                else
+                    grow = (int64_t)nt * C::BN + t0;
+                on[q] = lane < C::SZ_LANES && c < C::BN / 4;
+                voff[q] = (uint32_t)((grp * sz_rows + grow) * 2);
+                dst[q] = C::A_STAGE + C::B_STAGE + which * C::SZ + j % C::SZ_PARTS * C::SZ_LANES * 16;
                 kind[q] = which ? LD_Z : LD_S;
             }
         }
@@ -143,14 +161,15 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
         // bytes (256 fp16), B by 128 (256 nibbles), scales and zeros by 4 (two groups)
         const char *base_a = uniform_ptr((const char *)a.A + (int64_t)s * a.ksplit * 2);
         const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + (int64_t)s * a.ksplit / 2);
-        const char *base_s = uniform_ptr((const char *)(a.bs + (int64_t)e * a.sz_expert_stride + (int64_t)s * a.ksplit / 128));
-        const char *base_z = uniform_ptr((const char *)(a.bz + (int64_t)e * a.sz_expert_stride + (int64_t)s * a.ksplit / 128));
+        const int64_t sz0 = (int64_t)e * a.sz_expert_stride + (int64_t)s * a.ksplit / 128 * sz_rows;
+        const char *base_s = uniform_ptr((const char *)(a.bs + sz0));
+        const char *base_z = uniform_ptr((const char *)(a.bz + sz0));
         const char *qbase[C::LPW];
         int qstep[C::LPW];
 #pragma unroll
         for (int q = 0; q < C::LPW; q++) {
             qbase[q] = kind[q] == LD_A ? base_a : kind[q] == LD_B ? base_b : kind[q] == LD_S ? base_s : base_z;
-            qstep[q] = kind[q] == LD_A ? C::A_SLABS * 128 : kind[q] == LD_B ? 128 : 4;
+            qstep[q] = kind[q] == LD_A ? C::A_SLABS * 128 : kind[q] == LD_B ? 128 : 4 * sz_rows;
         }
         auto issue = [&](int kstep) {
             const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
@@ -158,10 +177,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
 #pragma unroll
             for (int q = 0; q < C::LPW; q++) {
                 const char *g = qbase[q] + (int64_t)kr * qstep[q];
-                if (kind[q] >= LD_S)
-                    lds_dma_off<4>(g, voff[q], st + dst[q]);
-                else if (on[q])
-                    lds_dma_off<16>(g, voff[q], st + dst[q]);
+                if (on[q]) lds_dma_off<16>(g, voff[q], st + dst[q]);
             }
         };
 
@@ -191,8 +207,18 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                 const int r = wn * C::TN + fn * 16 + (lane & 15);
                 braw[0][fn] = *(const uint4 *)(sb + r * 128 + ((g ^ swz(r)) << 4));
                 braw[1][fn] = *(const uint4 *)(sb + r * 128 + (((g + 4) ^ swz(r)) << 4));
-                sw[fn] = *(const uint32_t *)(ss + r * 4);
-                zw[fn] = *(const uint32_t *)(sz + r * 4);
+                // scale and zero point of B row r for the stage's 2 groups ([group][row] in
+                // the global row order: the tile's gate rows, then its up rows)
+                int t;
+                if (KIND == GEMM_GATE_UP) {
+                    const int wcol = r / C::TN, i = r % C::TN, half = C::TN / 2;
+                    t = i < half ? wcol * half + i : C::BN / 2 + wcol * half + (i - half);
+                } else {
+                    t = r;
+                }
+                const uint16_t *s16 = (const uint16_t *)ss, *z16 = (const uint16_t *)sz;
+                sw[fn] = (uint32_t)s16[t] | ((uint32_t)s16[C::BN + t] << 16);
+                zw[fn] = (uint32_t)z16[t] | ((uint32_t)z16[C::BN + t] << 16);
             }
             const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll

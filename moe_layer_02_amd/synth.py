@@ -195,7 +195,7 @@ class ExpertWeights:
     """Stacked expert weights on the host, in the layer's storage format.
     bf16: w13 bf16 [E,2I,H], w2 bf16 [E,H,I].
     fp8:  w13/w2 uint8 E4M3 codes (same shapes), w13_scale/w2_scale fp32 [E].
-    int4: w13 uint8 [E,2I,H/2], w2 uint8 [E,H,I/2], *_s/*_z fp16 [E,N,K/128]."""
+    int4: w13 uint8 [E,2I,H/2], w2 uint8 [E,H,I/2], *_s/*_z fp16 [E,K/128,N] (group-major)."""
     wdtype: int
     w13: torch.Tensor
     w2: torch.Tensor
@@ -236,13 +236,16 @@ def expert_weights(cfg: LayerConfig, device: str = "cpu") -> ExpertWeights:
     if cfg.wdtype == WDT_INT4:
         w13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device)
         w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=device)
-        s13 = torch.empty((E, 2 * I, H // 128), dtype=torch.float16, device=device)
+        # scales and zero points group-major: [E, K/128, N]
+        s13 = torch.empty((E, H // 128, 2 * I), dtype=torch.float16, device=device)
         z13 = torch.empty_like(s13)
-        s2 = torch.empty((E, H, I // 128), dtype=torch.float16, device=device)
+        s2 = torch.empty((E, I // 128, H), dtype=torch.float16, device=device)
         z2 = torch.empty_like(s2)
         for e in range(E):
-            w13[e], s13[e], z13[e] = _int4_encode(mat(_T_W13, e, 2 * I, H))
-            w2[e], s2[e], z2[e] = _int4_encode(mat(_T_W2, e, H, I))
+            w13[e], s, z = _int4_encode(mat(_T_W13, e, 2 * I, H))
+            s13[e], z13[e] = s.t(), z.t()
+            w2[e], s, z = _int4_encode(mat(_T_W2, e, H, I))
+            s2[e], z2[e] = s.t(), z.t()
         return ExpertWeights(WDT_INT4, w13, w2, w13_s=s13, w13_z=z13, w2_s=s2, w2_z=z2)
     raise ValueError("unknown weight dtype")
 

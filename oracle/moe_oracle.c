@@ -290,7 +290,7 @@ double orc_weight(const orc_weights *W, int m, int e, int64_t n, int64_t c)
     /* int4 */
     uint8_t byte = ((const uint8_t *)w)[((int64_t)e * rows + n) * (cols / 2) + c / 2];
     int q = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-    int64_t gidx = ((int64_t)e * rows + n) * (cols / 128) + c / 128;
+    int64_t gidx = ((int64_t)e * (cols / 128) + c / 128) * rows + n;   /* group-major [E, cols/128, rows] */
     double s = orc_f16_to_f32((m == 0 ? W->w13_s : W->w2_s)[gidx]);
     double z = orc_f16_to_f32((m == 0 ? W->w13_z : W->w2_z)[gidx]);
     return ((double)q - z) * s;
@@ -315,10 +315,10 @@ static void weight_row(const orc_weights *W, int m, int e, int64_t n, double *bu
         return;
     }
     const uint8_t *row = (const uint8_t *)(m == 0 ? W->w13 : W->w2) + ((int64_t)e * rows + n) * (cols / 2);
-    int64_t g0 = ((int64_t)e * rows + n) * (cols / 128);
     for (int64_t g = 0; g < cols / 128; g++) {
-        double s = orc_f16_to_f32((m == 0 ? W->w13_s : W->w2_s)[g0 + g]);
-        double z = orc_f16_to_f32((m == 0 ? W->w13_z : W->w2_z)[g0 + g]);
+        int64_t gi = ((int64_t)e * (cols / 128) + g) * rows + n;
+        double s = orc_f16_to_f32((m == 0 ? W->w13_s : W->w2_s)[gi]);
+        double z = orc_f16_to_f32((m == 0 ? W->w13_z : W->w2_z)[gi]);
         for (int64_t c = g * 128; c < (g + 1) * 128; c++) {
             int q = (c % 2 == 0) ? (row[c / 2] & 0xF) : (row[c / 2] >> 4);
             buf[c] = ((double)q - z) * s;

@@ -71,8 +71,8 @@ typedef struct {
     const void *w2;             /* bf16 bits / e4m3 codes [E,H,I];  int4: uint8 [E,H,I/2]  */
     const float *w13_scale;     /* fp8: [E] per-expert per-tensor scale of w13 */
     const float *w2_scale;      /* fp8: [E] */
-    const uint16_t *w13_s, *w13_z;  /* int4: fp16 [E,2I,H/128] scales and zero points */
-    const uint16_t *w2_s, *w2_z;    /* int4: fp16 [E,H,I/128] */
+    const uint16_t *w13_s, *w13_z;  /* int4: fp16 [E,H/128,2I] scales and zero points (group-major) */
+    const uint16_t *w2_s, *w2_z;    /* int4: fp16 [E,I/128,H] */
 } orc_weights;
 
 /* Dequantised weight element of expert e, matrix m (0 = w13, 1 = w2), row n, column c. */

@@ -32,7 +32,8 @@ MUTANTS = {
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "int4_nibbles_swapped": ("(c % 2 == 0) ? (byte & 0xF) : (byte >> 4)", "(c % 2 == 0) ? (byte >> 4) : (byte & 0xF)"),
     "int4_zero_ignored": ("return ((double)q - z) * s;", "return (double)q * s;"),
-    "int4_group_64": ("(cols / 128) + c / 128;", "(cols / 128) + c / 256;"),
+    "int4_group_64": ("(cols / 128) + c / 128) * rows + n;", "(cols / 128) + c / 256) * rows + n;"),
+    "int4_scales_row_major": ("(cols / 128) + c / 128) * rows + n;", "rows + n) * (cols / 128) + c / 128;"),
     "int4_row_nibbles_swapped": ("(c % 2 == 0) ? (row[c / 2] & 0xF) : (row[c / 2] >> 4)",
                                  "(c % 2 == 0) ? (row[c / 2] >> 4) : (row[c / 2] & 0xF)"),
     "int4_row_zero_ignored": ("buf[c] = ((double)q - z) * s;", "buf[c] = (double)q * s;"),

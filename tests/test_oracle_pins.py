@@ -336,7 +336,9 @@ def test_forward_int4_dequantises_groups():
         s = (rng.random((E, N, K // 128)) * 0.02 + 0.001).astype(np.float16)
         packed = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
         deq = (q.astype(np.float64) - np.repeat(z.astype(np.float64), 128, -1)) * np.repeat(s.astype(np.float64), 128, -1)
-        return packed, s.view(np.uint16), z.view(np.uint16), deq
+        # scales and zero points are stored group-major: [E, K/128, N]
+        gm = lambda a: np.ascontiguousarray(a.transpose(0, 2, 1)).view(np.uint16)  # noqa: E731
+        return packed, gm(s), gm(z), deq
     p13, s13, z13, d13 = make(2 * I, H)
     p2, s2, z2, d2 = make(H, I)
     W = oracle.Weights(oracle.INT4_G128, E, H, I, p13, p2, w13_s=s13, w13_z=z13, w2_s=s2, w2_z=z2)
