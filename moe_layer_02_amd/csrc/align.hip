@@ -9,15 +9,19 @@
 // flat index t*k + j and the layout is the same on every run.
 //
 // Up to kOneGroupPairs pairs one 1024-thread workgroup does everything (one launch, the
-// small-T case).  Beyond that the pairs are cut into chunks of kChunk: k_align_count
-// histograms every chunk in parallel, k_align_scan (one workgroup) turns the histograms
-// into per-chunk write offsets, and k_align_scatter ranks and writes every chunk in
-// parallel -- the same stable order, so both paths produce identical outputs.
+// small-T case).  Up to kFusedMaxPairs, k_align_fused is still one launch: every workgroup
+// scatters one chunk of kFusedChunk pairs, and to know where its rows go it counts all the
+// batch's pairs itself (at most 256 KiB of ids, read from L2), so no workgroup waits for
+// another.  Beyond that the pairs are cut into chunks of kChunk: k_align_count histograms
+// every chunk in parallel, k_align_scan (one workgroup) turns the histograms into per-chunk
+// write offsets, and k_align_scatter ranks and writes every chunk in parallel.  All three
+// paths give the same stable order, so their outputs are identical.
 #include "align_dev.h"
 
 namespace moe {
 
 constexpr int64_t kOneGroupPairs = 4096;   // up to this many pairs: the one-workgroup kernel
+constexpr int64_t kFusedMaxPairs = 65536;  // up to this many: one launch of k_align_fused
 
 namespace {
 
@@ -25,7 +29,62 @@ using namespace align_dev;
 
 __global__ __launch_bounds__(1024) void k_align(AlignArgs a) { align_group(a); }
 
-// ---- the multi-workgroup path -------------------------------------------------------------
+// ---- one launch, many workgroups --------------------------------------------------------
+
+constexpr int kFusedChunk = 2048;   // pairs scattered per workgroup: 16 waves x 128
+constexpr int kFusedSeg = kFusedChunk / kWaves;
+static_assert(kFusedChunk % (4 * kWave) == 0, "a 4-piece count step never straddles a chunk edge");
+
+__global__ __launch_bounds__(1024) void k_align_fused(AlignArgs a) {
+    __shared__ int hist[kWaves][kMaxE];   // this chunk's per-wave counts, then write cursors
+    __shared__ int before[kMaxE];         // pairs per expert in earlier chunks
+    __shared__ int cnt_s[kMaxE];          // pairs per expert in later chunks, then in all
+    __shared__ int off_s[kMaxE + 1];
+    const int tid = threadIdx.x, w = tid >> 6, G = gridDim.x;
+    const int P = a.T * a.k, E = a.E, BM = a.BM;
+    const int c0 = blockIdx.x * kFusedChunk, c1 = c0 + kFusedChunk;
+
+    for (int i = tid; i < kWaves * kMaxE; i += 1024) hist[i / kMaxE][i % kMaxE] = 0;
+    for (int i = tid; i < kMaxE; i += 1024) before[i] = cnt_s[i] = 0;
+    __syncthreads();
+    constexpr int step = kWaves * 4 * kWave;
+    count_strided4(a.ids, w * 4 * kWave, c0, step, E, a.nbits, before);
+    count_strided4(a.ids, c1 + w * 4 * kWave, P, step, E, a.nbits, cnt_s);
+    const int beg = min(P, c0 + w * kFusedSeg), end = min(P, beg + kFusedSeg);
+    count_range(a.ids, beg, end, E, a.nbits, hist[w]);
+    __syncthreads();
+    if (tid < E) {
+        int run = before[tid];
+        for (int ww = 0; ww < kWaves; ww++) {
+            const int c = hist[ww][tid];
+            hist[ww][tid] = run;   // pairs of this expert before this wave's segment
+            run += c;
+        }
+        const int cnt = run + cnt_s[tid];
+        cnt_s[tid] = cnt;
+        if (blockIdx.x == 0) a.counts[tid] = cnt;
+        off_s[tid] = (cnt + BM - 1) / BM * BM;
+    }
+    __syncthreads();
+    scan_experts(off_s, E);
+    __syncthreads();
+    const int total = off_s[kMaxE];
+    if (blockIdx.x == 0 && tid == 0) *a.npp = total;
+    if (tid < E)
+        for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += off_s[tid];
+    // rows no pair lands in: each expert's padding (experts dealt round the workgroups) and
+    // every row past the last block
+    for (int e = blockIdx.x; e < E; e += G) {
+        const int r0 = off_s[e] + cnt_s[e], r1 = off_s[e] + (cnt_s[e] + BM - 1) / BM * BM;
+        for (int r = r0 + tid; r < r1; r += 1024) a.sorted[r] = P;
+    }
+    for (int64_t r = total + (int64_t)blockIdx.x * 1024 + tid; r < a.cap; r += (int64_t)G * 1024) a.sorted[r] = P;
+    write_block_experts(off_s, E, BM, a.cap, total, a.eids, (int64_t)blockIdx.x * 1024 + tid, (int64_t)G * 1024);
+    __syncthreads();
+    scatter_range(a.ids, beg, end, E, a.nbits, hist[w], a.sorted, a.inv_pos);
+}
+
+// ---- the multi-launch path -------------------------------------------------------------
 
 constexpr int kChunk = 2048;          // pairs per workgroup (8 waves x 256)
 constexpr int kChunkWaves = 8;
@@ -68,7 +127,7 @@ __global__ __launch_bounds__(1024) void k_align_scan(AlignArgs a, int32_t *chunk
             run += cnt;
         }
     }
-    write_block_experts(off_s, E, BM, a.cap, total, a.eids);
+    write_block_experts(off_s, E, BM, a.cap, total, a.eids, tid, 1024);
 }
 
 __global__ __launch_bounds__(512) void k_align_scatter(AlignArgs a, const int32_t *chunk_base) {
@@ -96,12 +155,16 @@ __global__ __launch_bounds__(512) void k_align_scatter(AlignArgs a, const int32_
 }  // namespace
 
 int64_t align_scratch_bytes(int64_t pairs, int E) {
-    if (pairs <= kOneGroupPairs) return 0;
+    if (pairs <= kFusedMaxPairs) return 0;
     return (pairs + kChunk - 1) / kChunk * E * 4;
 }
 
 hipError_t launch_align(const AlignArgs &a, int32_t *scratch, hipStream_t s) {
     const int64_t P = (int64_t)a.T * a.k;
+    if (P > kOneGroupPairs && P <= kFusedMaxPairs) {
+        hipLaunchKernelGGL(k_align_fused, dim3((unsigned)((P + kFusedChunk - 1) / kFusedChunk)), dim3(1024), 0, s, a);
+        return hipGetLastError();
+    }
     if (P <= kOneGroupPairs || !scratch) {
         hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), 0, s, a);
         return hipGetLastError();

@@ -93,11 +93,35 @@ __device__ __forceinline__ void scan_experts(int *off_s, int E) {
     if (lane == kWave - 1) off_s[kMaxE] = incl;
 }
 
+// Count the pairs [beg, end) per expert into hist, four 64-pair pieces per step with their
+// loads issued together (the order of the pieces does not matter to a count).  beg must be
+// a multiple of 64; the wave strides by `step` pairs.
+__device__ __forceinline__ void count_strided4(const int32_t *ids, int beg, int end, int step, int E, int nbits,
+                                               int *hist) {
+    const int lane = lane_id();
+    for (int base = beg; base < end; base += step) {
+        int e[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int i = base + q * kWave + lane;
+            e[q] = i < end ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const bool valid = (unsigned)e[q] < (unsigned)E;
+            const int ev = valid ? e[q] : 0;
+            const uint64_t same = match_mask(ev, valid, nbits);
+            if (valid && (same & lanemask_lt()) == 0) atomicAdd(&hist[ev], __popcll(same));
+        }
+    }
+}
+
 // expert_ids for every block: the last expert whose first row is at or before the block's
-// first row owns it (experts with no rows share their successor's offset).
+// first row owns it (experts with no rows share their successor's offset).  Blocks first,
+// first + stride, ... are written by the calling thread.
 __device__ __forceinline__ void write_block_experts(const int *off_s, int E, int BM, int64_t cap, int total,
-                                                    int32_t *eids) {
-    for (int64_t b = threadIdx.x; b < cap / BM; b += blockDim.x) {
+                                                    int32_t *eids, int64_t first, int64_t stride) {
+    for (int64_t b = first; b < cap / BM; b += stride) {
         const int64_t r = b * BM;
         int e = -1;
         if (r < total) {
@@ -145,7 +169,7 @@ __device__ __forceinline__ void align_group(const AlignArgs &a) {
     if (tid == 0) *a.npp = total;
     if (tid < E)
         for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += off_s[tid];
-    write_block_experts(off_s, E, BM, a.cap, total, a.eids);
+    write_block_experts(off_s, E, BM, a.cap, total, a.eids, tid, 1024);
     __syncthreads();
     scatter_range(a.ids, beg, end, E, a.nbits, hist[w], a.sorted, a.inv_pos);
 }

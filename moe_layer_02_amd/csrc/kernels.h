@@ -26,8 +26,8 @@ struct AlignArgs {
     const int32_t *ids;
     int32_t *sorted, *eids, *npp, *counts, *inv_pos;
 };
-// scratch: align_scratch_bytes() of device memory for the chunked path (large T*k), or
-// null to always use the one-workgroup kernel
+// scratch: align_scratch_bytes() of device memory for the multi-launch path (T*k above
+// 65536; zero bytes below), or null to run such batches on the one-workgroup kernel
 int64_t align_scratch_bytes(int64_t pairs, int E);
 hipError_t launch_align(const AlignArgs &a, int32_t *scratch, hipStream_t s);
 

@@ -1,6 +1,8 @@
 """moe_align on the GPU vs the oracle: every output bit-exact (counts, sorted ids with
 fillers, expert per block, padded total, inverse positions) at the block heights the GEMMs
-use, with ragged sizes, zero-token experts and skewed loads."""
+use, with ragged sizes, zero-token experts and skewed loads.  Up to 4096 pairs one
+workgroup aligns the batch; up to 65536 one workgroup per 2048-pair chunk, each counting
+the whole batch; beyond that (no scratch here) the one workgroup again."""
 import numpy as np
 import pytest
 import torch
@@ -40,7 +42,8 @@ def distinct_ids(rng, T, k, E):
 
 @pytest.mark.parametrize("BM", [16, 32, 64, 128])
 @pytest.mark.parametrize("T,k,E", [(1, 1, 8), (1, 8, 256), (3, 2, 8), (37, 2, 8), (100, 8, 64), (512, 8, 256),
-                                   (4096, 8, 64), (8192, 1, 16), (4096, 2, 8), (2000, 6, 128)])
+                                   (4096, 8, 64), (8192, 1, 16), (4096, 2, 8), (2000, 6, 128), (4097, 1, 8),
+                                   (1531, 7, 64)])
 def test_align_matches_oracle(T, k, E, BM):
     rng = np.random.default_rng(T * 131 + k * 7 + E + BM)
     check(distinct_ids(rng, T, k, E), T, k, E, BM)
@@ -58,7 +61,8 @@ def test_align_skewed_and_empty_experts():
 
 def test_align_largest_pairs_and_block():
     rng = np.random.default_rng(4)
-    check(distinct_ids(rng, 8192, 8, 256), 8192, 8, 256, 16)    # 65536 pairs
+    check(distinct_ids(rng, 8192, 8, 256), 8192, 8, 256, 16)    # 65536 pairs: the largest one-launch batch
+    check(distinct_ids(rng, 8193, 8, 256), 8193, 8, 256, 16)    # one workgroup takes every pair beyond it
     check(distinct_ids(rng, 300, 4, 64), 300, 4, 64, 1024)        # largest block height
     check(distinct_ids(rng, 300, 4, 64), 300, 4, 64, 1)
 

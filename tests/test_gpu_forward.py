@@ -189,12 +189,33 @@ def test_scout_largest_T_sampled():
 # ---- fp8 w8a8 --------------------------------------------------------------------------
 
 def test_qwen2_largest_T_route_and_align():
-    """T*k = 32768 pairs: the forward's chunked multi-workgroup align must lay rows out
-    exactly as the oracle's stable sort does."""
+    """T*k = 32768 pairs: the forward's multi-workgroup align must lay rows out exactly as
+    the oracle's stable sort does."""
     c = case("qwen2")
     out, ws = c.gpu(4096)
     assert torch.isfinite(out.float()).all()
     check_intermediates(c, 4096, None, ws)
+
+
+QWEN2_NARROW = synth.CONFIGS["qwen2"].with_shape(name="qwen2_narrow", H=512, I=256)
+
+
+@pytest.mark.parametrize("T", [2000, 8192, 8193, 9000])
+def test_align_paths_in_forward(T):
+    """Qwen2's routing (64 experts, top-8) on narrow weights: 16000 and 65536 pairs take the
+    one-launch align whose workgroups each count the whole batch, 65544 and 72000 pairs the
+    count / scan / scatter launches; either way the rows are laid out exactly as the
+    oracle's stable sort does, and sampled tokens match the oracle."""
+    if "qwen2_narrow" not in _cases:
+        _cases["qwen2_narrow"] = Case("qwen2_narrow", "cuda", QWEN2_NARROW)
+    c = _cases["qwen2_narrow"]
+    out, ws = c.gpu(T)
+    tokens = [0, T // 2, T - 1]
+    ref, _, _ = c.oracle(T, tokens=tokens)
+    err = rel_l2(bf16_to_f64(out[tokens]), ref)
+    say("  sampled rel-L2 %.3e" % err)
+    assert err <= TOL[c.cfg.wdtype]
+    check_intermediates(c, T, None, ws)
 
 
 @pytest.mark.parametrize("T", [1, 8, 24])
