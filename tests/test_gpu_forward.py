@@ -197,12 +197,13 @@ def test_qwen2_largest_T_route_and_align():
     check_intermediates(c, 4096, None, ws)
 
 
-QWEN2_NARROW = synth.CONFIGS["qwen2"].with_shape(name="qwen2_narrow", H=512, I=256)
+QWEN2_NARROW = synth.CONFIGS["qwen2"].with_shape(name="qwen2_narrow", H=512, I=256, wdtype=synth.WDT_BF16)
 
 
 @pytest.mark.parametrize("T", [2000, 8192, 8193, 9000])
 def test_align_paths_in_forward(T):
-    """Qwen2's routing (64 experts, top-8) on narrow weights: 16000 and 65536 pairs take the
+    """Qwen2's routing (64 experts, top-8) on narrow bf16 weights (per-token work, so the
+    oracle computes the sampled tokens alone): 16000 and 65536 pairs take the
     one-launch align whose workgroups each count the whole batch, 65544 and 72000 pairs the
     count / scan / scatter launches; either way the rows are laid out exactly as the
     oracle's stable sort does, and sampled tokens match the oracle."""
