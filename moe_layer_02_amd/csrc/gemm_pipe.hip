@@ -29,9 +29,14 @@ namespace {
 
 enum { WT_BF16 = 0, WT_FP8 = 2, WT_INT4 = 3 };
 
-template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_>
+template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_, int BX_ = 0>
 struct PCfg {
     static constexpr int BM = BM_, BN = BN_, KS = KS_, ST = ST_, WM = WM_, WN = WN_;
+    // BX = 1 (-1): B (A) gets one stage more than the other operand, each operand in a ring
+    // of its own, so its loads run two K steps ahead while the other's run one (two
+    // stages; 160 KB of LDS for a 256x256 tile)
+    static constexpr int BX = BX_;
+    static constexpr int DA = ST + (BX < 0), DB = ST + (BX > 0);   // ring depths
     static constexpr int MS = MS_;                            // MFMA output tile: 16x16 or 32x32
     static constexpr int SB = SB_;                            // bytes of K per row and slab: 128 or 64
     static constexpr int NW = WM * WN, NT = NW * kWave;
@@ -47,6 +52,17 @@ struct PCfg {
     static_assert(MS == 16 || (MS == 32 && WT == WT_BF16), "32x32 MFMA tiles are bf16 only");
     static_assert(SB == 128 || (SB == 64 && WT == WT_BF16), "64-byte slabs hold whole MFMA K steps for bf16 only");
     static_assert((ST - 2) * LPW <= 63, "vmcnt range");
+    static constexpr int B_STAGE = STAGE - A_STAGE;
+    static constexpr int LA = A_LOADS / NW, LB = (LOADS - A_LOADS) / NW;   // per wave and stage
+    static constexpr int L_AHEAD = BX > 0 ? LB : LA;
+    static_assert(BX == 0 || ((BX == 1 || BX == -1) && ST == 2 && A_LOADS % NW == 0),
+                  "the one-operand-ahead rings are built for two stages with loads split evenly per wave");
+    static constexpr int LDS_BYTES = BX ? DA * A_STAGE + DB * B_STAGE : ST * STAGE;
+    // LDS offsets of step k's A and B
+    static __device__ __forceinline__ int a_off(int k) { return BX ? (k % DA) * A_STAGE : (k % ST) * STAGE; }
+    static __device__ __forceinline__ int b_off(int k) {
+        return BX ? DA * A_STAGE + (k % DB) * B_STAGE : (k % ST) * STAGE + A_STAGE;
+    }
     // skip loading A's filler rows: worth it where a block is mostly padding (small blocks,
     // small T); large tiles keep the registers the per-load flags would take
     static constexpr bool SKIP_FILLER = BM <= 32;
@@ -54,7 +70,7 @@ struct PCfg {
 
 template <class C, int WT, int KIND, bool PARTIAL>
 __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -161,14 +177,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nku : 0;
         const char *base_a = uniform_ptr((const char *)a.A + kb);
         const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + kb);
-        auto issue = [&](int kstep) {
-            const uint32_t st = lds_addr(smem) + (kstep % C::ST) * C::STAGE;
+        // the loads of step kstep: A's, B's or both (dst holds B's offsets past A_STAGE)
+        auto issue = [&](int kstep, bool do_a, bool do_b) {
+            const uint32_t sta = lds_addr(smem) + C::a_off(kstep);
+            const uint32_t stb = lds_addr(smem) + C::b_off(kstep) - C::A_STAGE;
             const int kr = __builtin_amdgcn_readfirstlane(kstep + krot < nku ? kstep + krot : kstep + krot - nku);
             const int64_t koff = (int64_t)kr * C::KS * C::SB;
 #pragma unroll
             for (int q = 0; q < C::LPW; q++)
-                if (on[q])
-                    lds_dma_off<16>((is_a[q] ? base_a : base_b) + koff, voff[q], st + dst[q]);
+                if (on[q] && (is_a[q] ? do_a : do_b))
+                    lds_dma_off<16>((is_a[q] ? base_a : base_b) + koff, voff[q], (is_a[q] ? sta : stb) + dst[q]);
         };
 
         // A block holds its expert's rows first and padding after them, so a wave row range
@@ -189,13 +207,24 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         block_barrier();
 #pragma unroll
         for (int p = 0; p < C::ST - 1; p++)
-            if (p < nku) issue(p);
+            if (p < nku) issue(p, true, true);
+        if constexpr (C::BX != 0)   // the operand that runs ahead: its step 1 too
+            if (1 < nku) issue(1, C::BX < 0, C::BX > 0);
 
         for (int kt = 0; kt < nku; kt++) {
-            wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nku - 1 - kt));
+            if constexpr (C::BX != 0) {
+                // issued after this step's last operand: the ahead operand's step kt + 1, if
+                // it exists (two stages)
+                if (kt + 1 < nku) wait_vmcnt<C::L_AHEAD>(); else wait_vmcnt<0>();
+            } else {
+                wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nku - 1 - kt));
+            }
             block_barrier();
-            if (kt + C::ST - 1 < nku) issue(kt + C::ST - 1);
-            const char *sa = smem + (kt % C::ST) * C::STAGE, *sb = sa + C::A_STAGE;
+            // the operand one step ahead, then (ahead rings) the other two steps ahead
+            if (kt + C::ST - 1 < nku) issue(kt + C::ST - 1, C::BX >= 0, C::BX <= 0);
+            if constexpr (C::BX != 0)
+                if (kt + 2 < nku) issue(kt + 2, C::BX < 0, C::BX > 0);
+            const char *sa = smem + C::a_off(kt), *sb = smem + C::b_off(kt);
             if (wave_rows) {   // a wave whose rows are all padding only loads and keeps step
             // Fragments of step k + 1 can be read while the MFMAs of step k run (see DB below).
             if constexpr (WT == WT_BF16 && C::MS == 32) {
@@ -439,6 +468,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     X(14, 256, 256, 1, 2, 4, 4, 16, 128) \
     X(15, 256, 128, 1, 3, 4, 4, 16, 128) \
     X(16, 128, 256, 1, 3, 4, 4, 16, 128)
+// tiles whose B (BX = 1) or A (BX = -1) runs a stage ahead of the other operand
+//        id  BM   BN  KS ST WM WN MS  SB  BX
+#define PIPE_BF16_TILES_BX(X) X(38, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(39, 256, 256, 1, 2, 4, 4, 16, 128, -1)
+#define PIPE_FP8_TILES_BX(X) X(17, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(18, 256, 256, 1, 2, 4, 4, 16, 128, -1)
 
 template <class C, int WT, int KIND, bool PARTIAL>
 hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
@@ -489,8 +522,10 @@ bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
     }
 #define PI_BF16(id, bm, bn, ks, st, wm, wn, ms, sb) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
 #define PI_FP8(id, bm, bn, ks, st, wm, wn, ms, sb) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
-    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) }
-    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) }
+#define PI_BF16_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
+#define PI_FP8_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
+    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) PIPE_BF16_TILES_BX(PI_BF16_BX) }
+    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) PIPE_FP8_TILES_BX(PI_FP8_BX) }
     if (wdtype == WT_INT4) return i4_tile_info(tile, info);
     return false;
 }
@@ -501,8 +536,12 @@ hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, c
     if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms, sb>, WT>(kind, partial, a, max_tiles, s);
 #define PL_BF16(id, bm, bn, ks, st, wm, wn, ms, sb) PLAUNCH(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
 #define PL_FP8(id, bm, bn, ks, st, wm, wn, ms, sb) PLAUNCH(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
-    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) }
-    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) }
+#define PLAUNCH_BX(WT, id, bm, bn, ks, st, wm, wn, ms, sb, bx) \
+    if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms, sb, bx>, WT>(kind, partial, a, max_tiles, s);
+#define PL_BF16_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PLAUNCH_BX(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb, bx)
+#define PL_FP8_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PLAUNCH_BX(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb, bx)
+    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) PIPE_BF16_TILES_BX(PL_BF16_BX) }
+    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) PIPE_FP8_TILES_BX(PL_FP8_BX) }
     if (wdtype == WT_INT4) return launch_gemm_i4(tile, kind, partial, a, max_tiles, s);
     return hipErrorInvalidValue;
 }
