@@ -16,6 +16,8 @@
 namespace moe {
 namespace {
 
+constexpr int kReduceMaxK = 8;   // top-k up to this: the rows' loads are issued together
+
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     const int c8 = a.H / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -32,6 +34,37 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     }
     if (a.direct && a.inv_pos[t] < tail_row0) return;   // top-1: GEMM2 wrote this token
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (a.split == 0 && a.k <= kReduceMaxK) {
+        // bf16 rows: every row's load is issued before the first add, so a thread keeps k
+        // loads in flight instead of one (the adds keep the order j = 0, 1, ...)
+        int64_t row[kReduceMaxK];
+        uint4 v[kReduceMaxK];
+#pragma unroll
+        for (int j = 0; j < kReduceMaxK; j++)
+            if (j < a.k) row[j] = a.inv_pos[t * a.k + j];
+#pragma unroll
+        for (int j = 0; j < kReduceMaxK; j++)
+            if (j < a.k && row[j] < tail_row0) v[j] = *(const uint4 *)((const uint16_t *)a.Y + row[j] * a.H + col);
+#pragma unroll
+        for (int j = 0; j < kReduceMaxK; j++) {
+            if (j >= a.k) break;
+            if (row[j] >= tail_row0) {
+                for (int s = 0; s < tail_s; s++) {
+                    const float *p = a.tail_P + s * tail_plane + (row[j] - tail_row0) * a.H + col;
+                    const float4 lo = *(const float4 *)p, hi = *(const float4 *)(p + 4);
+                    acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+                    acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+                }
+            } else {
+                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    acc[2 * i] += __uint_as_float(w[i] << 16);
+                    acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+                }
+            }
+        }
+    } else {
     for (int j = 0; j < a.k; j++) {
         const int64_t row = a.inv_pos[t * a.k + j];
         if (row >= tail_row0) {
@@ -57,6 +90,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
                 acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
             }
         }
+    }
     }
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
