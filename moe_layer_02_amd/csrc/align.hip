@@ -11,8 +11,8 @@
 // Up to kOneGroupPairs pairs one 1024-thread workgroup does everything (one launch, the
 // small-T case).  Up to kFusedMaxPairs, k_align_fused is still one launch: every workgroup
 // scatters one chunk of kFusedChunk pairs, and to know where its rows go it counts all the
-// batch's pairs itself (at most 256 KiB of ids, read from L2), so no workgroup waits for
-// another.  Beyond that the pairs are cut into chunks of kChunk: k_align_count histograms
+// batch's pairs itself (at most 256 KiB of ids, read from L2, with the next 512 ids per wave
+// in flight while the current ones are counted), so no workgroup waits for another.  Beyond that the pairs are cut into chunks of kChunk: k_align_count histograms
 // every chunk in parallel, k_align_scan (one workgroup) turns the histograms into per-chunk
 // write offsets, and k_align_scatter ranks and writes every chunk in parallel.  All three
 // paths give the same stable order, so their outputs are identical.
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(1024) void k_align(AlignArgs a) { align_group(a); }
 
 constexpr int kFusedChunk = 2048;   // pairs scattered per workgroup: 16 waves x 128
 constexpr int kFusedSeg = kFusedChunk / kWaves;
-static_assert(kFusedChunk % (4 * kWave) == 0, "a 4-piece count step never straddles a chunk edge");
+static_assert(kFusedChunk % (kCountPieces * kWave) == 0, "a count step never straddles a chunk edge");
 
 __global__ __launch_bounds__(1024) void k_align_fused(AlignArgs a) {
     __shared__ int hist[kWaves][kMaxE];   // this chunk's per-wave counts, then write cursors
@@ -47,11 +47,11 @@ __global__ __launch_bounds__(1024) void k_align_fused(AlignArgs a) {
     for (int i = tid; i < kWaves * kMaxE; i += 1024) hist[i / kMaxE][i % kMaxE] = 0;
     for (int i = tid; i < kMaxE; i += 1024) before[i] = cnt_s[i] = 0;
     __syncthreads();
-    constexpr int step = kWaves * 4 * kWave;
-    count_strided4(a.ids, w * 4 * kWave, c0, step, E, a.nbits, before);
-    count_strided4(a.ids, c1 + w * 4 * kWave, P, step, E, a.nbits, cnt_s);
+    constexpr int span = kCountPieces * kWave, step = kWaves * span;
+    count_strided(a.ids, w * span, c0, step, E, before);
+    count_strided(a.ids, c1 + w * span, P, step, E, cnt_s);
     const int beg = min(P, c0 + w * kFusedSeg), end = min(P, beg + kFusedSeg);
-    count_range(a.ids, beg, end, E, a.nbits, hist[w]);
+    count_strided(a.ids, beg, end, kCountPieces * kWave, E, hist[w]);
     __syncthreads();
     if (tid < E) {
         int run = before[tid];
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(512) void k_align_count(AlignArgs a, int32_t *chunk
     const int c0 = blockIdx.x * kChunk, w = threadIdx.x >> 6;
     const int seg = kChunk / kChunkWaves;
     const int beg = min(P, c0 + w * seg), end = min(P, beg + seg);
-    count_range(a.ids, beg, end, a.E, a.nbits, hist);
+    count_strided(a.ids, beg, end, kCountPieces * kWave, a.E, hist);
     __syncthreads();
     for (int e = threadIdx.x; e < a.E; e += 512) chunk_counts[(int64_t)blockIdx.x * a.E + e] = hist[e];
 }
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(512) void k_align_scatter(AlignArgs a, const int32_
     const int beg = min(P, c0 + w * seg), end = min(P, beg + seg);
     for (int i = threadIdx.x; i < kChunkWaves * kMaxE; i += 512) hist[i / kMaxE][i % kMaxE] = 0;
     __syncthreads();
-    count_range(a.ids, beg, end, E, a.nbits, hist[w]);
+    count_strided(a.ids, beg, end, kCountPieces * kWave, E, hist[w]);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 512) {
         int run = chunk_base[(int64_t)blockIdx.x * E + e];

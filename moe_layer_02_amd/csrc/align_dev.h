@@ -31,28 +31,16 @@ __device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
     return same;
 }
 
-// Count the pairs [beg, end) per expert into hist (LDS): per 64-pair piece, the lowest lane
-// of each group of equal experts adds the group's size (no atomic contention per expert).
-__device__ __forceinline__ void count_range(const int32_t *ids, int beg, int end, int E, int nbits, int *hist) {
-    const int lane = lane_id();
-    for (int base = beg; base < end; base += kWave) {
-        const int i = base + lane;
-        int e = i < end ? ids[i] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;   // other ids are dropped
-        if (!valid) e = 0;
-        const uint64_t same = match_mask(e, valid, nbits);
-        if (valid && (same & lanemask_lt()) == 0) atomicAdd(&hist[e], __popcll(same));
-    }
-}
-
 // Scatter the pairs [beg, end) in order; cursor[e] (LDS) is the next row of expert e for
 // this wave and advances by each piece's group sizes.
 __device__ __forceinline__ void scatter_range(const int32_t *ids, int beg, int end, int E, int nbits,
                                               volatile int *cursor, int32_t *sorted, int32_t *inv_pos) {
     const int lane = lane_id();
+    int e_next = beg + lane < end ? ids[beg + lane] : -1;   // the next piece loads while this one is placed
     for (int base = beg; base < end; base += kWave) {
         const int i = base + lane;
-        int e = i < end ? ids[i] : -1;
+        int e = e_next;
+        if (base + kWave < end) e_next = base + kWave + lane < end ? ids[base + kWave + lane] : -1;
         const bool valid = (unsigned)e < (unsigned)E;
         if (!valid) {
             if (i < end) inv_pos[i] = -1;
@@ -93,26 +81,34 @@ __device__ __forceinline__ void scan_experts(int *off_s, int E) {
     if (lane == kWave - 1) off_s[kMaxE] = incl;
 }
 
-// Count the pairs [beg, end) per expert into hist, four 64-pair pieces per step with their
-// loads issued together (the order of the pieces does not matter to a count).  beg must be
-// a multiple of 64; the wave strides by `step` pairs.
-__device__ __forceinline__ void count_strided4(const int32_t *ids, int beg, int end, int step, int E, int nbits,
-                                               int *hist) {
+// Count the pairs [beg, end) per expert into hist (LDS) with one LDS atomic add per pair:
+// the LDS serialises only the lanes that hit the same expert, where matching the lanes'
+// experts first by ballots costs a few VALU operations per id bit and piece (four cycles
+// each for a wave of 64).  kCountPieces pieces per step
+// with their loads issued together, and the next step's loads issued before this step's
+// pieces are counted (the order of the pieces does not matter to a count).  beg must be a
+// multiple of 64; the wave strides by `step` pairs.
+constexpr int kCountPieces = 8;
+
+__device__ __forceinline__ void count_strided(const int32_t *ids, int beg, int end, int step, int E, int *hist) {
     const int lane = lane_id();
-    for (int base = beg; base < end; base += step) {
-        int e[4];
+    int nxt[kCountPieces];
+    auto load = [&](int base) {
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < kCountPieces; q++) {
             const int i = base + q * kWave + lane;
-            e[q] = i < end ? ids[i] : -1;
+            nxt[q] = i < end ? ids[i] : -1;
         }
+    };
+    if (beg < end) load(beg);
+    for (int base = beg; base < end; base += step) {
+        int e[kCountPieces];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const bool valid = (unsigned)e[q] < (unsigned)E;
-            const int ev = valid ? e[q] : 0;
-            const uint64_t same = match_mask(ev, valid, nbits);
-            if (valid && (same & lanemask_lt()) == 0) atomicAdd(&hist[ev], __popcll(same));
-        }
+        for (int q = 0; q < kCountPieces; q++) e[q] = nxt[q];
+        if (base + step < end) load(base + step);
+#pragma unroll
+        for (int q = 0; q < kCountPieces; q++)
+            if ((unsigned)e[q] < (unsigned)E) atomicAdd(&hist[e[q]], 1);
     }
 }
 
@@ -150,7 +146,7 @@ __device__ __forceinline__ void align_group(const AlignArgs &a) {
     // each wave owns a contiguous segment of pairs, a multiple of 64 long
     const int seg = (P + kWaves * kWave - 1) / (kWaves * kWave) * kWave;
     const int beg = min(P, w * seg), end = min(P, beg + seg);
-    count_range(a.ids, beg, end, E, a.nbits, hist[w]);
+    count_strided(a.ids, beg, end, kCountPieces * kWave, E, hist[w]);
     __syncthreads();
     if (tid < E) {
         int run = 0;

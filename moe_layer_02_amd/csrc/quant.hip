@@ -17,26 +17,42 @@ namespace {
 
 using namespace quant_dev;
 
-__global__ __launch_bounds__(256) void k_absmax(AbsmaxArgs a) {
+// Same-address atomics serialise (about 16 ns each here), so the pass runs as at most one
+// 1024-thread workgroup per CU, each with one atomic, and keeps four 16-byte loads in
+// flight per thread (the maximum does not depend on the order).
+constexpr int kAbsmaxThreads = 1024;
+
+__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(AbsmaxArgs a) {
     float m = 0.0f;
-    const int64_t n8 = a.n / 8;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
-        const uint4 v = ((const uint4 *)a.x)[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int64_t n8 = a.n / 8, stride = (int64_t)gridDim.x * kAbsmaxThreads;
+    constexpr int U = 4;
+    for (int64_t i0 = (int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x; i0 < n8; i0 += U * stride) {
+        uint4 v[U];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
-            m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+        for (int u = 0; u < U; u++) {
+            const int64_t i = i0 + u * stride;
+            v[u] = i < n8 ? ((const uint4 *)a.x)[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
+                m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+            }
         }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    // one atomic per workgroup: same-address atomics serialise in L2
-    __shared__ float wmax[4];
+    __shared__ float wmax[kAbsmaxThreads / kWave];
     if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0)
-        atomicMax(a.amax, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+    if (threadIdx.x == 0) {
+        float b = 0.0f;
+        for (int w = 0; w < kAbsmaxThreads / kWave; w++) b = fmaxf(b, wmax[w]);
+        atomicMax(a.amax, __float_as_uint(b));
+    }
 }
 
 // 8 elements (bf16 or fp32) per thread -> 8 codes (one 8-byte store)
@@ -85,11 +101,11 @@ hipError_t launch_f16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream
 }
 
 hipError_t launch_absmax(const AbsmaxArgs &a, hipStream_t s) {
-    int64_t blocks = (a.n / 8 + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 4;
+    int64_t blocks = (a.n / 8 + kAbsmaxThreads - 1) / kAbsmaxThreads;
+    const int64_t cap = device_cu_count();
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(k_absmax, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_absmax, dim3((unsigned)blocks), dim3(kAbsmaxThreads), 0, s, a);
     return hipGetLastError();
 }
 
