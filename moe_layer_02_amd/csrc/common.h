@@ -46,6 +46,18 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8_perm(uint4 v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// A maximum of non-negative floats kept as their bits (which order like the floats) in one
+// device word.  Atomics on one address serialise (about 16 ns each on these GPUs), so a
+// caller reads the word first (amax_peek, a device-scope load that may be issued early)
+// and raises it only when its value is larger: the word only grows, so a value that is
+// not larger than a read can never be the maximum.
+__device__ __forceinline__ uint32_t amax_peek(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void amax_raise(uint32_t *p, uint32_t seen, float v) {
+    if (__float_as_uint(v) > seen) atomicMax(p, __float_as_uint(v));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int l = lane_id();
     return l == 0 ? 0ull : (~0ull >> (64 - l));

@@ -375,6 +375,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 }
         } else if constexpr (KIND == GEMM_GATE_UP) {
             float amax = 0.0f;
+            uint32_t seen = 0;   // the h maximum so far, read before the stores (see amax_peek)
+            if constexpr (WT == WT_FP8)
+                if (lane == 0 && a.amax_out) seen = amax_peek(a.amax_out);
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             if constexpr (WT == WT_FP8) {
 #pragma unroll
                 for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-                if (lane == 0 && a.amax_out) atomicMax(a.amax_out, __float_as_uint(amax));
+                if (lane == 0 && a.amax_out) amax_raise(a.amax_out, seen, amax);
             }
         } else {
 #pragma unroll

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(AbsmaxArgs a) {
     if (threadIdx.x == 0) {
         float b = 0.0f;
         for (int w = 0; w < kAbsmaxThreads / kWave; w++) b = fmaxf(b, wmax[w]);
-        atomicMax(a.amax, __float_as_uint(b));
+        amax_raise(a.amax, amax_peek(a.amax), b);
     }
 }
 

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
         __shared__ float wmax[4];
         if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
         __syncthreads();
-        if (threadIdx.x == 0) atomicMax(a.amax, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+        if (threadIdx.x == 0) amax_raise(a.amax, amax_peek(a.amax), fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
     }
 }
 
