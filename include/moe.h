@@ -144,6 +144,10 @@ typedef struct {
  * split it took.
  * max_workgroups (0: the whole device) caps the persistent grids of both GEMMs, e.g. to
  * leave compute units to concurrent work.
+ * split_tail1 (0 or 1: off; 2..16 with split_k1 <= 1 and a pipelined bf16 or fp8 GEMM1
+ * tile): the same for GEMM1 -- the split row blocks' gate and up sums go to fp32 planes and
+ * a finishing pass (stage MOE_STAGE_GEMM1_FINISH) adds them in a fixed order and applies
+ * SiLU * up to those rows before GEMM2.
  * moe_default_plan picks a plan per T; any valid plan gives results equal within rounding
  * (and bitwise reproducible for a fixed plan on a fixed device).
  */
@@ -155,6 +159,7 @@ typedef struct {
     int32_t split_k1;
     int32_t split_tail;
     int32_t max_workgroups;
+    int32_t split_tail1;
 } moe_plan;
 
 /* Steps of moe_forward, for moe_forward_profiled. */
@@ -163,7 +168,8 @@ typedef enum {
     MOE_STAGE_H_QUANT = 4, MOE_STAGE_GEMM2 = 5, MOE_STAGE_REDUCE = 6,
     MOE_STAGE_PROLOGUE = 7,   /* T <= 64 (fp8 or more than 64 experts: 16): route, align
                                  and the activation pass in one launch                  */
-    MOE_STAGE_GEMM1_FINISH = 8, /* split_k1 > 1: sum of GEMM1's partials, SiLU * up      */
+    MOE_STAGE_GEMM1_FINISH = 8, /* split_k1 > 1 or split_tail1 > 1: sum of GEMM1's
+                                   partials, SiLU * up                                  */
     MOE_STAGE_COUNT = 9
 } moe_stage;
 
@@ -263,14 +269,16 @@ typedef enum {
     MOE_WS_H_Q = 10,          /* fp8: E4M3 [capacity, I] quantised h                 */
     MOE_WS_Y = 11,            /* bf16 [capacity, H] weighted expert rows, or with split_k > 1
                                  fp32 [split_k, capacity, H] partial sums             */
-    MOE_WS_ALIGN_SCRATCH = 12, /* int32 per-chunk expert histograms of the chunked align
-                                  (T*k > 4096 only)                                   */
+    MOE_WS_ALIGN_SCRATCH = 12, /* int32 per-chunk expert histograms of the multi-launch
+                                  align (T*k > 65536 only)                            */
     MOE_WS_GEMM1_PARTIALS = 13, /* split_k1 > 1: fp32 [split_k1, capacity, 2I] gate (columns
                                    [0, I)) and up ([I, 2I)) partial sums              */
     MOE_WS_GEMM2_TAIL = 14,   /* split_tail > 1: int32 [4] = first sorted row of the split
                                  row blocks, S (0: none split), elements per plane, 0;
                                  then at byte 256 fp32 [S, rows, H] partial sums        */
-    MOE_WS_COUNT = 15
+    MOE_WS_GEMM1_TAIL = 15,   /* split_tail1 > 1: the same for GEMM1, planes fp32
+                                 [S, rows, 2I] of gate ([0, I)) and up ([I, 2I)) sums  */
+    MOE_WS_COUNT = 16
 } moe_ws_region;
 
 /* Byte offset of each moe_ws_region in the workspace of moe_forward(layer, T, plan) into

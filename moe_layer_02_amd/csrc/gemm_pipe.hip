@@ -83,12 +83,15 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     const int nk = a.ksplit / C::BK;
     const int ebytes = WT == WT_FP8 ? 1 : 2;                  // A and B element bytes
 
-    // Split tail (GEMM2 without a K split): with one tile per workgroup and round, a last
+    // Split tail (a GEMM without a K split): with one tile per workgroup and round, a last
     // round of rem = mn % G tiles leaves G - rem workgroups idle.  When the row blocks
     // holding those tiles make at most half a round, they are computed as S K splits
-    // instead (fp32 planes, added in order by the reduce step): after the whole rounds of
-    // the other blocks, S x their tiles units of 1/S of the work fill the grid.
-    constexpr bool TAIL = KIND == GEMM_DOWN && !PARTIAL;
+    // instead (fp32 planes, added in order by the reduce step after GEMM2, or by the
+    // finishing pass that applies SiLU * up after GEMM1): after the whole rounds of the
+    // other blocks, S x their tiles units of 1/S of the work fill the grid.  A plane row
+    // holds GEMM2's H outputs, or GEMM1's I gate then I up sums.
+    constexpr bool TAIL = !PARTIAL;
+    const int tail_ld = KIND == GEMM_GATE_UP ? 2 * a.I : (int)a.ldc;
     int mb_dp = mblocks, tail_s = 0, tail_tiles = 0;
     if constexpr (TAIL) {
         if (a.tail_split >= 2) {
@@ -105,14 +108,14 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             if (blockIdx.x == 0 && tid == 0) {
                 a.tail_info[0] = mb_dp * C::BM;
                 a.tail_info[1] = tail_s;
-                a.tail_info[2] = (mblocks - mb_dp) * C::BM * (int)a.ldc;
+                a.tail_info[2] = (mblocks - mb_dp) * C::BM * tail_ld;
                 a.tail_info[3] = 0;
             }
         }
     }
     const int mn_dp = mb_dp * ntiles;
     const int total = TAIL ? mn_dp + tail_tiles * tail_s : mn * a.split;
-    const int64_t tail_plane = (int64_t)(mblocks - mb_dp) * C::BM * a.ldc;
+    const int64_t tail_plane = (int64_t)(mblocks - mb_dp) * C::BM * tail_ld;
 
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
         // unit: whole-K tile (or one of split_k splits), or one split of a tail tile
@@ -366,6 +369,23 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                     const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
                     if (a.sorted[row] >= a.pairs) continue;
                     float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
+                        P[col] = acc[fm][f][i] * scale;
+                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
+                    }
+                }
+        } else if (KIND == GEMM_GATE_UP && tail) {
+            // split tail: this split's gate and up sums in fp32 (the finishing pass adds the
+            // splits in order and applies SiLU * up; for fp8 it also folds |h|)
+#pragma unroll
+            for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
+                    if (a.sorted[row] >= a.pairs) continue;
+                    float *P = a.tail_P + s * tail_plane + (int64_t)(row - mb_dp * C::BM) * tail_ld;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;

@@ -117,6 +117,10 @@ struct GateUpFinishArgs {
     void *h;                     // [cap, I] in h_kind's format
     int h_kind;                  // GATE_UP_H_*
     uint32_t *amax;              // fp32 h: |h| max as float bits (atomicMax), may be null
+    // GEMM1's split tail (null: the split-K planes of every row): rows from tail_info[0]
+    // on, tail_info[1] planes (0: none, nothing to do) of tail_info[2] elements, whose row
+    // r - tail_info[0] holds row r's sums; plane and split above are then unused
+    const int32_t *tail_info;
 };
 hipError_t launch_gate_up_finish(const GateUpFinishArgs &a, int64_t max_rows, hipStream_t s);
 // fp32 h (GATE_UP_H_F32) of a small batch, finished and quantised to E4M3 in one workgroup:

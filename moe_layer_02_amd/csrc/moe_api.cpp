@@ -118,11 +118,15 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
     if (p->split_tail < 0 || p->split_tail > 16 || p->max_workgroups < 0) return MOE_ERR_INVALID_ARGUMENT;
     if (p->split_tail > 1 && (p->split_k != 1 || t2->stages == 0 || wd == MOE_DT_INT4_G128))
         return MOE_ERR_INVALID_ARGUMENT;
+    // GEMM1's split tail: the unsplit GEMM1 of the pipelined bf16 / fp8 tiles
+    if (p->split_tail1 < 0 || p->split_tail1 > 16) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->split_tail1 > 1 && (s1 > 1 || t1->stages == 0 || wd == MOE_DT_INT4_G128)) return MOE_ERR_INVALID_ARGUMENT;
     return MOE_OK;
 }
 
-// GEMM2's split tail on / the tiles x splits its planes hold
+// GEMM2's / GEMM1's split tail on / the tiles x splits their planes hold
 bool split_tail(const moe_plan *p) { return p->split_tail > 1; }
+bool split_tail1(const moe_plan *p) { return p->split_tail1 > 1; }
 constexpr int kTailUnits = 256;
 constexpr size_t kTailInfoBytes = 256;
 
@@ -136,7 +140,8 @@ int prologue_max_t(const moe_layer *L) {
 }
 
 struct Workspace {
-    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, tail, total;
+    size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, tail, tail1,
+        total;
     int64_t cap;
 };
 
@@ -180,9 +185,12 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
                : p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
     w.align_scratch = take((size_t)align_scratch_bytes(pairs, E));
     w.g1p = take(split1(p) > 1 ? (size_t)split1(p) * w.cap * 2 * L->I * 4 : 0);
-    TileInfo t2{};
+    TileInfo t1{}, t2{};
+    gemm_tile_info(L->weight_dtype, p->gemm1_tile, &t1);
     gemm_tile_info(L->weight_dtype, p->gemm2_tile, &t2);
     w.tail = take(split_tail(p) ? kTailInfoBytes + (size_t)kTailUnits * t2.BM * t2.BN * 4 : 0);
+    // a GEMM1 tile's unit covers BN / 2 gate and BN / 2 up columns: BM x BN fp32 as well
+    w.tail1 = take(split_tail1(p) ? kTailInfoBytes + (size_t)kTailUnits * t1.BM * t1.BN * 4 : 0);
     w.total = o;
     return w;
 }
@@ -344,6 +352,12 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         g.ksplit = H / s1;
         g.amax_out = nullptr;
     }
+    // GEMM1's split tail: fp32 planes of the split row blocks, finished below
+    int32_t *tail1_info = split_tail1(&plan) ? (int32_t *)(ws + w.tail1) : nullptr;
+    g.tail_split = split_tail1(&plan) ? plan.split_tail1 : 0;
+    g.tail_cap = kTailUnits;
+    g.tail_P = split_tail1(&plan) ? (float *)(ws + w.tail1 + kTailInfoBytes) : nullptr;
+    g.tail_info = tail1_info;
     // persistent grids: at most max_workgroups workgroups when the plan caps them
     auto grid_cap = [&](int64_t tiles) {
         return plan.max_workgroups > 0 ? std::min<int64_t>(tiles, plan.max_workgroups) : tiles;
@@ -362,6 +376,15 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         err = finish_quant ? launch_gate_up_finish_quant(f, inv_pos, (uint8_t *)(ws + w.hq), (float *)&scal[3], stream)
                            : launch_gate_up_finish(f, w.cap, stream);
         if (err != hipSuccess) return fail(err);
+    } else if (split_tail1(&plan)) {
+        // the split row blocks' h (GEMM1 recorded the rows and planes; none: an empty pass)
+        if ((err = mark(MOE_STAGE_GEMM1_FINISH)) != hipSuccess) return MOE_ERR_HIP;
+        GateUpFinishArgs f{(const float *)(ws + w.tail1 + kTailInfoBytes), 0, 0, I, sorted, npp, pairs, ws + w.h,
+                           fp8 ? GATE_UP_H_F32 : GATE_UP_H_BF16, fp8 ? &scal[1] : nullptr, tail1_info};
+        // at most kTailUnits / (column tiles) row blocks are split
+        const int64_t tail_rows = (int64_t)kTailUnits / (I / (t1.BN / 2)) * plan.block_m;
+        if ((err = launch_gate_up_finish(f, std::max<int64_t>(tail_rows, plan.block_m), stream)) != hipSuccess)
+            return fail(err);
     }
 
     // 5. fp8: quantise h with its dynamic scale
@@ -543,12 +566,13 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     // (within 6% of the fastest plan at every point but Mixtral T=512, 9%).  Small r
     // streams weights (16-row blocks, narrow tiles, split-K for GEMM2, and for GEMM1 where
     // an expert's I is small next to the GPU); large r is MFMA work (128x256 and 256x256
-    // tiles of 16 waves, GEMM2's partial last round split).
-    struct Row { double r_max; int bm, g1, g2, split, split1, tail; };
+    // tiles of 16 waves, GEMM2's partial last round split; with 128-row blocks GEMM1's as
+    // well: Mixtral T=1024 and Llama-4-Scout T=2048 -3.3%, Mixtral T=512 and 1536 -1%).
+    struct Row { double r_max; int bm, g1, g2, split, split1, tail, tail1; };
     static const Row bf16[] = {{0.1, 16, 9, 9, 4, 1, 0},        {0.3, 16, 10, 9, 4, 1, 0},
                                {1.5, 16, 9, 9, 4, 1, 0},        {3, 16, 10, 9, 1, 1, 0},
                                {8, 32, 19, 12, 1, 1, 0},        {24, 64, 18, 11, 1, 1, 0},
-                               {96, 128, 22, 22, 2, 1, 0},      {384, 128, 22, 22, 1, 1, 8},
+                               {96, 128, 22, 22, 2, 1, 0},      {384, 128, 22, 22, 1, 1, 8, 8},
                                {1e30, 256, 25, 25, 1, 1, 8}};
     static const Row fp8[] = {{0.125, 16, 9, 1, 1, 2, 0},  {8, 16, 1, 1, 1, 2, 0},       {48, 32, 11, 2, 1, 1, 0},
                               {192, 128, 7, 16, 1, 1, 8},  {384, 128, 13, 16, 1, 1, 8},  {1e30, 256, 12, 14, 1, 1, 8}};
@@ -571,7 +595,8 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
         // split 2)
         const int split0 = layer->route.top_k == 1 && r > 96 ? 1 : rows[i].split;
         for (int sk = split0; sk >= 1; sk /= 2) {
-            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk, rows[i].split1, sk == 1 ? rows[i].tail : 0, 0};
+            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk, rows[i].split1, sk == 1 ? rows[i].tail : 0, 0,
+                       rows[i].tail1};
             if (check_plan(layer, &p, &t1, &t2) != MOE_OK) p.split_k1 = 1;   // H not split that way
             if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
                 *plan = p;
@@ -627,10 +652,12 @@ moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *
     if ((st = check_plan(layer, plan, &t1, &t2)) != MOE_OK) return st;
     std::snprintf(buf, len,
                   "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d stages%d mfma%d] gemm2=%d[BM%d BN%d BK%d "
-                  "waves%dx%d stages%d mfma%d] split_k=%d split_k1=%d split_tail=%d max_workgroups=%d",
+                  "waves%dx%d stages%d mfma%d] split_k=%d split_k1=%d split_tail=%d max_workgroups=%d "
+                  "split_tail1=%d",
                   plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, t1.stages, t1.mfma,
                   plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k, split1(plan),
-                  split_tail(plan) ? plan->split_tail : 0, plan->max_workgroups);
+                  split_tail(plan) ? plan->split_tail : 0, plan->max_workgroups,
+                  split_tail1(plan) ? plan->split_tail1 : 0);
     return MOE_OK;
 }
 
@@ -644,8 +671,8 @@ moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_pl
     TileInfo t1, t2;
     if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
     const Workspace w = layout(layer, T, &p);
-    const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos,
-                                    w.scal, w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p, w.tail};
+    const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos, w.scal,
+                                    w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p, w.tail, w.tail1};
     for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
     return MOE_OK;
 }

@@ -105,15 +105,23 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
 // rows only; fp32 h also folds its |h| maximum (one atomic per workgroup, max is exact).
 __global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
     const int64_t c8 = a.I / 8;
-    const int64_t rows = *a.npp;
+    int64_t r0 = 0, plane = a.plane;
+    int split = a.split;
+    if (a.tail_info) {   // GEMM1's split tail: its rows only (the same for the whole grid)
+        r0 = a.tail_info[0];
+        split = a.tail_info[1];
+        plane = a.tail_info[2];
+        if (split == 0) return;
+    }
+    const int64_t rows = *a.npp - r0;
     float m = 0.0f;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * c8; i += (int64_t)gridDim.x * 256) {
-        const int64_t r = i / c8;
+        const int64_t pr = i / c8, r = r0 + pr;   // plane row, sorted row
         const int c = (int)(i % c8) * 8;
         if (a.sorted[r] >= a.pairs) continue;
         float g[8], u[8];
-        for (int s = 0; s < a.split; s++) {
-            const float *p = a.P + s * a.plane + r * 2 * (int64_t)a.I;
+        for (int s = 0; s < split; s++) {
+            const float *p = a.P + s * plane + pr * 2 * (int64_t)a.I;
             const float4 g0 = *(const float4 *)(p + c), g1 = *(const float4 *)(p + c + 4);
             const float4 u0 = *(const float4 *)(p + a.I + c), u1 = *(const float4 *)(p + a.I + c + 4);
             const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};

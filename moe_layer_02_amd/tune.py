@@ -20,7 +20,7 @@ from moe_layer_02_amd import abi, synth
 
 
 def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64, 128, 256), tiles=None,
-                split1=(1,), tails=(0,)):
+                split1=(1,), tails=(0,), tails1=(0,)):
     out = []
     for bm in bms:
         for g1 in (tiles if tiles is not None else range(max_tile)):
@@ -28,12 +28,13 @@ def valid_plans(layer: abi.MoELayer, T: int, max_tile: int = 40, bms=(16, 32, 64
                 for sk in (1, 2, 3, 4, 5, 6, 7, 8):
                     for s1 in split1:
                         for st in tails:
-                            p = abi.Plan(bm, g1, g2, sk, s1, st)
-                            try:
-                                abi.moe_workspace_bytes(layer.struct, T, p)
-                            except abi.MoEError:
-                                continue
-                            out.append(p)
+                            for st1 in tails1:
+                                p = abi.Plan(bm, g1, g2, sk, s1, st, 0, st1)
+                                try:
+                                    abi.moe_workspace_bytes(layer.struct, T, p)
+                                except abi.MoEError:
+                                    continue
+                                out.append(p)
     return out
 
 
@@ -71,6 +72,7 @@ def main():
     ap.add_argument("--tiles", default=None, help="tile ids to try for both GEMMs (default: all)")
     ap.add_argument("--split1", default="1", help="GEMM1 K splits to try (small-T tiles only)")
     ap.add_argument("--split-tail", default="0", help="GEMM2 split-tail factors to try (0: off)")
+    ap.add_argument("--split-tail1", default="0", help="GEMM1 split-tail factors to try (0: off)")
     args = ap.parse_args()
     cfg = synth.CONFIGS[args.config]
     w = synth.expert_weights(cfg, device="cuda")
@@ -90,7 +92,8 @@ def main():
         tiles = None if args.tiles is None else [int(t) for t in args.tiles.split(",")]
         split1 = tuple(int(v) for v in args.split1.split(","))
         tails = tuple(int(v) for v in args.split_tail.split(","))
-        plans = valid_plans(layer, T, bms=bms, tiles=tiles, split1=split1, tails=tails)
+        tails1 = tuple(int(v) for v in args.split_tail1.split(","))
+        plans = valid_plans(layer, T, bms=bms, tiles=tiles, split1=split1, tails=tails, tails1=tails1)
         if plans:   # bring the clocks up before the first timed plan
             time_plan(layer, x, lg, T, plans[0], 5 * args.reps)
         for p in plans:

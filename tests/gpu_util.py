@@ -79,9 +79,9 @@ def workspace_view(layer, T, plan, ws, region, dtype, count):
     return ws[off:off + count * torch.tensor([], dtype=dtype).element_size()].view(dtype)
 
 
-def valid_plans(layer, T, split1=(1, 2, 4), splits=(1, 2, 4, 8), tails=(0,), max_workgroups=0):
-    """Every (block_m, tile1, tile2, split, split1, split_tail) the library accepts for this
-    layer (grids capped at max_workgroups)."""
+def valid_plans(layer, T, split1=(1, 2, 4), splits=(1, 2, 4, 8), tails=(0,), max_workgroups=0, tails1=(0,)):
+    """Every (block_m, tile1, tile2, split, split1, split_tail, split_tail1) the library
+    accepts for this layer (grids capped at max_workgroups)."""
     n = 40
     out = []
     for g1 in range(n):
@@ -89,31 +89,40 @@ def valid_plans(layer, T, split1=(1, 2, 4), splits=(1, 2, 4, 8), tails=(0,), max
             for sk in splits:
                 for s1 in split1:
                     for st in tails:
-                        for bm in (16, 32, 64, 128, 256):
-                            p = abi.Plan(bm, g1, g2, sk, s1, st, max_workgroups)
-                            try:
-                                abi.moe_workspace_bytes(layer.struct, T, p)
-                            except abi.MoEError:
-                                continue
-                            out.append(p)
+                        for st1 in tails1:
+                            for bm in (16, 32, 64, 128, 256):
+                                p = abi.Plan(bm, g1, g2, sk, s1, st, max_workgroups, st1)
+                                try:
+                                    abi.moe_workspace_bytes(layer.struct, T, p)
+                                except abi.MoEError:
+                                    continue
+                                out.append(p)
     return out
 
 
-def gemm2_tile(layer, T, plan):
+def gemm1_tile(layer, T, plan):
+    """(BM, BN, BK) of the plan's GEMM1 tile, from moe_plan_describe."""
+    return gemm2_tile(layer, T, plan, "gemm1=")
+
+
+def gemm2_tile(layer, T, plan, which="gemm2="):
     """(BM, BN, BK) of the plan's GEMM2 tile, from moe_plan_describe."""
     d = abi.moe_plan_describe(layer.struct, T, plan)
-    g2 = d.split("gemm2=")[1]
+    g2 = d.split(which)[1]
     f = {k: int(v) for k, v in (("BM", g2.split("BM")[1].split()[0]), ("BN", g2.split("BN")[1].split()[0]),
                                    ("BK", g2.split("BK")[1].split()[0]))}
     return f["BM"], f["BN"], f["BK"]
 
 
-def expected_tail(npp, cap, H, I, tile, max_workgroups, split_tail, units=256):
-    """The split tail GEMM2 takes with its grid capped at max_workgroups (fewer than the
-    compute units): (first tail row, S), S = 0 when it splits nothing -- the rule of the
-    split_tail plan field restated.  The grid is also at most the tiles the capacity
-    allows, and a multiple of 8 from 8 on."""
+def expected_tail(npp, cap, H, I, tile, max_workgroups, split_tail, units=256, gemm1=False):
+    """The split tail GEMM2 (GEMM1: gemm1=True) takes with its grid capped at max_workgroups
+    (fewer than the compute units): (first tail row, S), S = 0 when it splits nothing -- the
+    rule of the split_tail / split_tail1 plan fields restated.  The grid is also at most the
+    tiles the capacity allows, and a multiple of 8 from 8 on.  GEMM1's tiles cover BN / 2
+    of the I outputs and its K is H."""
     BM, BN, BK = tile
+    if gemm1:
+        H, I, BN = I, H, BN // 2
     mblocks, ntiles = npp // BM, H // BN
     grid = min(max_workgroups, cap // BM * ntiles)
     if grid >= 8:

@@ -256,6 +256,33 @@ def test_split_tail_rules():
     assert all(abi.moe_default_plan(i4, T).split_tail == 0 for T in (1, 64, 512))
 
 
+def test_split_tail1_rules():
+    """GEMM1's split tail: a pipelined bf16 or fp8 GEMM1 tile without a GEMM1 K split, at
+    most 16 splits; its gate/up planes (256 units of BM x BN fp32) get their own region."""
+    cfg = synth.CONFIGS["mixtral"]
+    layer = fake_layer(cfg)
+    T = 1024
+    plain = abi.Plan(128, 22, 22, 1, 1, 8)
+    with_tail = abi.Plan(128, 22, 22, 1, 1, 8, 0, 4)
+    base = abi.moe_workspace_bytes(layer, T, plain)
+    assert base == abi.moe_workspace_bytes(layer, T, abi.Plan(128, 22, 22, 1, 1, 8, 0, 1))
+    assert abi.moe_workspace_bytes(layer, T, with_tail) >= base + 256 + 256 * 128 * 256 * 4
+    off, off_plain = abi.moe_workspace_offsets(layer, T, with_tail), abi.moe_workspace_offsets(layer, T, plain)
+    assert off["gemm1_tail"] >= off["gemm2_tail"] and off["gemm1_tail"] == off_plain["gemm1_tail"]
+    assert abi.moe_workspace_bytes(layer, T, with_tail) - off["gemm1_tail"] >= 256 + 256 * 128 * 256 * 4
+    assert abi.moe_plan_describe(layer, T, with_tail).endswith("split_tail1=4")
+    assert with_tail.as_tuple() == (128, 22, 22, 1, 1, 8, 0, 4)
+    for bad in [abi.Plan(16, 9, 9, 1, 2, 0, 0, 4),       # with GEMM1's K split of every tile
+                abi.Plan(16, 0, 0, 1, 1, 0, 0, 4),       # register-staged GEMM1 tile
+                abi.Plan(128, 22, 22, 1, 1, 8, 0, 17), abi.Plan(128, 22, 22, 1, 1, 8, 0, -1)]:
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_workspace_bytes(layer, T, bad)
+        assert ei.value.status == abi.MOE_ERR_INVALID_ARGUMENT
+    i4 = fake_layer(synth.CONFIGS["deepseek"])
+    with pytest.raises(abi.MoEError):
+        abi.moe_workspace_bytes(i4, 64, abi.Plan(32, 12, 12, 1, 0, 0, 0, 4))
+
+
 
 def test_grouped_gemm_host_checks():
     """The EP grouped GEMM: default tiles divide N and K, the workspace holds the block

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from moe_layer_02_amd import abi, synth
-from tests.gpu_util import (TOL, bits, bf16_to_f64, device_layer, expected_tail, gemm2_tile, needs_gpu,
+from tests.gpu_util import (TOL, bits, bf16_to_f64, device_layer, expected_tail, gemm1_tile, gemm2_tile, needs_gpu,
                             oracle_route, oracle_weights, rel_l2, say, valid_plans, weights, workspace_view)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -504,6 +504,71 @@ def test_split_tail_top1(T):
     tail's tokens."""
     mixed, _ = check_tail_plans(small_case(TAIL_SMALL_TOP1), T, (24,))
     assert mixed > 0
+
+
+# ---- GEMM1 split tail ------------------------------------------------------------------
+
+def tail1_taken(c, T, plan, ws):
+    """(first tail row, S) that GEMM1 recorded in the workspace."""
+    info = workspace_view(c.layer, T, plan, ws, "gemm1_tail", torch.int32, 4).cpu().numpy()
+    return int(info[0]), int(info[1])
+
+
+def check_tail1_plans(c, T, grids, tails2=(0,)):
+    """Every GEMM1 split-tail plan on grids of `grids` workgroups against the oracle (with
+    GEMM2's split tail off, or on as well); GEMM1's recorded tail is the rule's.  Returns
+    how many runs split a tail after whole tiles."""
+    ref, _, _ = c.oracle(T)
+    mixed = 0
+    for g in grids:
+        plans = valid_plans(c.layer, T, split1=(1,), splits=(1,), tails=tails2, max_workgroups=g, tails1=(2, 8))
+        assert plans, "no GEMM1 split-tail plan"
+        for p in plans:
+            out, ws = c.gpu(T, p)
+            err = rel_l2(bf16_to_f64(out), ref)
+            assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+            npp = int(workspace_view(c.layer, T, p, ws, "num_post_pad", torch.int32, 1).cpu()[0])
+            got = tail1_taken(c, T, p, ws)
+            cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, p.block_m)
+            want = expected_tail(npp, cap, c.cfg.H, c.cfg.I, gemm1_tile(c.layer, T, p), g, p.split_tail1, gemm1=True)
+            assert got == want, (p.as_tuple(), got, want)
+            mixed += got[1] > 0 and got[0] > 0
+    return mixed
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_split_tail1_every_plan(T):
+    """GEMM1's last partial round as K splits (fp32 gate and up planes, finished in order
+    before GEMM2) on grids of 24 and 48 workgroups, every pipelined GEMM1 tile."""
+    assert check_tail1_plans(small_case(TAIL_SMALL), T, (24, 48)) > 0
+
+
+def test_split_tail1_fp8_and_both_tails():
+    """fp8 (the finishing pass also folds |h| of the tail rows), and both GEMMs' tails at once."""
+    assert check_tail1_plans(small_case(FP8_SMALL), 300, (8, 24)) > 0
+    assert check_tail1_plans(small_case(TAIL_SMALL), 300, (24,), tails2=(4,)) > 0
+
+
+def test_split_tail1_mixtral_sampled():
+    """The full-size Mixtral shard at T=1024 (a last GEMM1 round of a sixth) with GEMM1's
+    split tail on the whole device: tokens whose rows lie in the tail against the oracle,
+    and the same output on a second call."""
+    c = case("mixtral")
+    T = 1024
+    p = abi.Plan(128, 22, 22, 1, 1, 8, 0, 8)
+    out, ws = c.gpu(T, p)
+    row0, S = tail1_taken(c, T, p, ws)
+    say("  GEMM1 tail rows from %d, S=%d" % (row0, S))
+    assert S >= 2 and row0 > 0
+    inv = workspace_view(c.layer, T, p, ws, "inv_pos", torch.int32, T * c.cfg.k).cpu().numpy().reshape(T, c.cfg.k)
+    in_tail = [t for t in range(T) if (inv[t] >= row0).any()]
+    tokens = sorted(set(in_tail[:3] + [0, T - 1]))
+    ref, _, _ = c.oracle(T, tokens=tokens)
+    err = rel_l2(bf16_to_f64(out[tokens]), ref)
+    say("  sampled rel-L2 %.3e" % err)
+    assert err <= TOL[c.cfg.wdtype]
+    again, _ = c.gpu(T, p, ws=ws)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
 
 
 @pytest.mark.parametrize("grid", [112, 0])
