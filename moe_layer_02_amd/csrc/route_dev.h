@@ -30,10 +30,6 @@ __host__ __device__ inline int route_variant(int kind, int E, int n_group) {
     return (G <= 64 && (G & (G - 1)) == 0) ? V_GROUPED_POW2 : V_GROUPED_ANY;
 }
 
-__device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
-}
-
 // Lane exchanges without LDS: step S pairs every lane with one partner so that steps
 // 0..g-1 combine all lanes of each aligned group of 2^g (g <= 6).  Steps 0-3 are DPP moves
 // (xor 1, xor 2, mirror within 8, mirror within 16); steps 4 and 5 are gfx950's
@@ -65,37 +61,56 @@ __device__ __forceinline__ double partner(double x) {
     return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
 }
 
-// One arg-max step over (key descending, index ascending); the order is total, so both
-// lanes of a pair keep the same winner.
 template <int S>
-__device__ __forceinline__ void argmax_step(float &key, int &idx, float &val) {
-    const float ok = partner<S>(key), ov = partner<S>(val);
-    const int oi = partner<S>(idx);
-    if (ranks_before(ok, oi, key, idx)) {
-        key = ok;
-        idx = oi;
-        val = ov;
-    }
+__device__ __forceinline__ uint64_t partner(uint64_t x) {
+    const uint32_t lo = (uint32_t)partner<S>((int)(uint32_t)x), hi = (uint32_t)partner<S>((int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// A candidate (key, index) as one unsigned 64-bit rank whose integer order is the
+// selection order (key descending, index ascending): the key's bits mapped to an
+// order-preserving unsigned word (-0 folded into +0, so that equal keys stay equal) above
+// the complement of the index.  0 ranks below every candidate: no candidate.  One wave
+// step then moves two words and compares once, where moving key, index and payload and
+// comparing (key, index) took about twice the instructions (four cycles each per wave).
+__device__ __forceinline__ uint64_t rank_of(float key, int idx) {
+    uint32_t u = __float_as_uint(key + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)idx;
+}
+__device__ __forceinline__ int rank_index(uint64_t r) { return r ? (int)~(uint32_t)r : INT32_MAX; }
+__device__ __forceinline__ float rank_key(uint64_t r) {
+    if (!r) return -INFINITY;
+    const uint32_t u = (uint32_t)(r >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// One arg-max step: both lanes of a pair keep the larger rank.
+template <int S>
+__device__ __forceinline__ void argmax_step(uint64_t &r) {
+    const uint64_t o = partner<S>(r);
+    if (o > r) r = o;
 }
 
 // Arg-max over each aligned group of 2^g lanes (g <= 6, wave-uniform); every lane of a
-// group ends with the group's winner and its payload.
-__device__ __forceinline__ void group_argmax(float &key, int &idx, float &val, int g) {
-    if (g > 0) argmax_step<0>(key, idx, val);
-    if (g > 1) argmax_step<1>(key, idx, val);
-    if (g > 2) argmax_step<2>(key, idx, val);
-    if (g > 3) argmax_step<3>(key, idx, val);
-    if (g > 4) argmax_step<4>(key, idx, val);
-    if (g > 5) argmax_step<5>(key, idx, val);
+// group ends with the group's winner.
+__device__ __forceinline__ void group_argmax(uint64_t &r, int g) {
+    if (g > 0) argmax_step<0>(r);
+    if (g > 1) argmax_step<1>(r);
+    if (g > 2) argmax_step<2>(r);
+    if (g > 3) argmax_step<3>(r);
+    if (g > 4) argmax_step<4>(r);
+    if (g > 5) argmax_step<5>(r);
 }
 
-__device__ __forceinline__ void wave_argmax(float &key, int &idx, float &val) {
-    argmax_step<0>(key, idx, val);
-    argmax_step<1>(key, idx, val);
-    argmax_step<2>(key, idx, val);
-    argmax_step<3>(key, idx, val);
-    argmax_step<4>(key, idx, val);
-    argmax_step<5>(key, idx, val);
+__device__ __forceinline__ uint64_t wave_argmax(uint64_t r) {
+    argmax_step<0>(r);
+    argmax_step<1>(r);
+    argmax_step<2>(r);
+    argmax_step<3>(r);
+    argmax_step<4>(r);
+    argmax_step<5>(r);
+    return r;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -176,29 +191,26 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
             const int e = lane + kWave * i;
-            float k1 = live[i] ? key[i] : -INFINITY, unused = 0.0f;
-            int i1 = live[i] ? e : INT32_MAX;
-            group_argmax(k1, i1, unused, gbits);
-            float k2 = (live[i] && e != i1) ? key[i] : -INFINITY;
-            int i2 = (live[i] && e != i1) ? e : INT32_MAX;
-            group_argmax(k2, i2, unused, gbits);
-            score[i] = G >= 2 ? k1 + k2 : k1;
+            uint64_t r1 = live[i] ? rank_of(key[i], e) : 0;
+            group_argmax(r1, gbits);
+            const int i1 = rank_index(r1);
+            uint64_t r2 = (live[i] && e != i1) ? rank_of(key[i], e) : 0;
+            group_argmax(r2, gbits);
+            score[i] = G >= 2 ? rank_key(r1) + rank_key(r2) : rank_key(r1);
         }
         // keep the topk_group best groups; the first lane of each segment stands for its group
         uint64_t kept = 0;
         for (int q = 0; q < a.topk_group; q++) {
-            float gk = -INFINITY, gv = 0.0f;
-            int gi = INT32_MAX;
+            uint64_t gr = 0;
 #pragma unroll
             for (int i = 0; i < EPL; i++) {
                 const int e = lane + kWave * i, g = e / G;
-                if (e < E && (lane % G) == 0 && !((kept >> g) & 1ull) && ranks_before(score[i], g, gk, gi)) {
-                    gk = score[i];
-                    gi = g;
+                if (e < E && (lane % G) == 0 && !((kept >> g) & 1ull)) {
+                    const uint64_t c = rank_of(score[i], g);
+                    if (c > gr) gr = c;
                 }
             }
-            wave_argmax(gk, gi, gv);
-            kept |= 1ull << gi;
+            kept |= 1ull << rank_index(wave_argmax(gr));
         }
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
@@ -211,31 +223,29 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         const int G = E / a.n_group;
         float my_score = -INFINITY;
         for (int g = 0; g < a.n_group; g++) {
-            float k1 = -INFINITY, v1 = 0.0f;
-            int i1 = INT32_MAX;
+            uint64_t r1 = 0;
 #pragma unroll
             for (int i = 0; i < EPL; i++) {
                 const int e = lane + kWave * i;
-                if (live[i] && e / G == g && ranks_before(key[i], e, k1, i1)) {
-                    k1 = key[i];
-                    i1 = e;
+                if (live[i] && e / G == g) {
+                    const uint64_t c = rank_of(key[i], e);
+                    if (c > r1) r1 = c;
                 }
             }
-            wave_argmax(k1, i1, v1);
-            float score = k1;
+            r1 = wave_argmax(r1);
+            float score = rank_key(r1);
             if (G >= 2) {
-                float k2 = -INFINITY, v2 = 0.0f;
-                int i2 = INT32_MAX;
+                const int i1 = rank_index(r1);
+                uint64_t r2 = 0;
 #pragma unroll
                 for (int i = 0; i < EPL; i++) {
                     const int e = lane + kWave * i;
-                    if (live[i] && e / G == g && e != i1 && ranks_before(key[i], e, k2, i2)) {
-                        k2 = key[i];
-                        i2 = e;
+                    if (live[i] && e / G == g && e != i1) {
+                        const uint64_t c = rank_of(key[i], e);
+                        if (c > r2) r2 = c;
                     }
                 }
-                wave_argmax(k2, i2, v2);
-                score = k1 + k2;
+                score = rank_key(r1) + rank_key(wave_argmax(r2));
             }
             if (lane == g) my_score = score;
         }
@@ -243,10 +253,7 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         uint64_t kept = 0;
         bool gfree = lane < a.n_group;
         for (int q = 0; q < a.topk_group; q++) {
-            float gk = gfree ? my_score : -INFINITY;
-            int gi = gfree ? lane : INT32_MAX;
-            float gv = 0.0f;
-            wave_argmax(gk, gi, gv);
+            const int gi = rank_index(wave_argmax(gfree ? rank_of(my_score, lane) : 0));
             kept |= 1ull << gi;
             if (lane == gi) gfree = false;
         }
@@ -261,18 +268,26 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
     int my_id = 0;
     double my_val = 0.0, norm = 0.0;
     for (int j = 0; j < a.k; j++) {
-        float bk = -INFINITY, bv = 0.0f;
-        int bi = INT32_MAX;
+        uint64_t br = 0;
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
-            const int e = lane + kWave * i;
-            if (live[i] && ranks_before(key[i], e, bk, bi)) {
-                bk = key[i];
-                bi = e;
-                bv = val[i];
+            if (live[i]) {
+                const uint64_t c = rank_of(key[i], lane + kWave * i);
+                if (c > br) br = c;
             }
         }
-        wave_argmax(bk, bi, bv);
+        br = wave_argmax(br);
+        const int bi = rank_index(br);
+        // the winner's payload from the lane that holds it (bi is the same on every lane)
+        float bv = 0.0f;
+        if (br) {
+            const int slot = bi / kWave;
+            float own = val[0];
+#pragma unroll
+            for (int i = 1; i < EPL; i++)
+                if (slot == i) own = val[i];
+            bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own), bi % kWave));
+        }
 #pragma unroll
         for (int i = 0; i < EPL; i++)
             if (lane + kWave * i == bi) live[i] = false;

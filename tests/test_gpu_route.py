@@ -57,6 +57,16 @@ def test_route_forced_ties(E, k, kind, ng, tg):
     check(cfg, logits, bias)
 
 
+@pytest.mark.parametrize("kind,E,k", [(0, 8, 2), (0, 64, 8), (1, 64, 6)])
+def test_route_signed_zero_ties(kind, E, k):
+    """-0.0 and +0.0 logits are equal keys (the index decides between them), on both sides."""
+    cfg = synth.CONFIGS["tiny"].with_shape(name="zeros", E=E, k=k, route_kind=kind, renormalize=True)
+    g = torch.Generator().manual_seed(E + k + 7 * kind)
+    logits = torch.randint(0, 3, (300, E), generator=g).float()
+    logits = torch.where(logits == 0, torch.tensor(-0.0), torch.where(logits == 1, torch.tensor(0.0), -logits))
+    check(cfg, logits.to(torch.bfloat16), None)
+
+
 def test_route_fp32_logits():
     cfg = synth.CONFIGS["deepseek"]
     logits = torch.randn(300, cfg.E, generator=torch.Generator().manual_seed(5))
