@@ -92,15 +92,29 @@ __device__ __forceinline__ void argmax_step(uint64_t &r) {
     if (o > r) r = o;
 }
 
-// Arg-max over each aligned group of 2^g lanes (g <= 6, wave-uniform); every lane of a
-// group ends with the group's winner.
-__device__ __forceinline__ void group_argmax(uint64_t &r, int g) {
-    if (g > 0) argmax_step<0>(r);
-    if (g > 1) argmax_step<1>(r);
-    if (g > 2) argmax_step<2>(r);
-    if (g > 3) argmax_step<3>(r);
-    if (g > 4) argmax_step<4>(r);
-    if (g > 5) argmax_step<5>(r);
+// Arg-max over each aligned group of 2^g lanes (g <= 6, wave-uniform) for N independent
+// ranks, step by step over all N so that their dependency chains interleave; every lane of
+// a group ends with the group's winner.
+template <int N>
+__device__ __forceinline__ void group_argmax_n(uint64_t (&r)[N], int g) {
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 0) argmax_step<0>(r[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 1) argmax_step<1>(r[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 2) argmax_step<2>(r[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 3) argmax_step<3>(r[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 4) argmax_step<4>(r[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 5) argmax_step<5>(r[i]);
 }
 
 __device__ __forceinline__ uint64_t wave_argmax(uint64_t r) {
@@ -188,16 +202,18 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         const int G = E / a.n_group;
         const int gbits = __builtin_ctz(G);
         float score[EPL];
+        uint64_t r1[EPL], r2[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; i++) r1[i] = live[i] ? rank_of(key[i], lane + kWave * i) : 0;
+        group_argmax_n(r1, gbits);
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
             const int e = lane + kWave * i;
-            uint64_t r1 = live[i] ? rank_of(key[i], e) : 0;
-            group_argmax(r1, gbits);
-            const int i1 = rank_index(r1);
-            uint64_t r2 = (live[i] && e != i1) ? rank_of(key[i], e) : 0;
-            group_argmax(r2, gbits);
-            score[i] = G >= 2 ? rank_key(r1) + rank_key(r2) : rank_key(r1);
+            r2[i] = (live[i] && e != rank_index(r1[i])) ? rank_of(key[i], e) : 0;
         }
+        group_argmax_n(r2, gbits);
+#pragma unroll
+        for (int i = 0; i < EPL; i++) score[i] = G >= 2 ? rank_key(r1[i]) + rank_key(r2[i]) : rank_key(r1[i]);
         // keep the topk_group best groups; the first lane of each segment stands for its group
         uint64_t kept = 0;
         for (int q = 0; q < a.topk_group; q++) {
