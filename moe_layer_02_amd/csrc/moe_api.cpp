@@ -569,8 +569,7 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     // tiles of 16 waves, GEMM2's partial last round split; with 128-row blocks GEMM1's as
     // well: Mixtral T=1024 and Llama-4-Scout T=2048 -3.3%, Mixtral T=512 and 1536 -1%).
     struct Row { double r_max; int bm, g1, g2, split, split1, tail, tail1; };
-    static const Row bf16[] = {{0.1, 16, 9, 9, 4, 1, 0},        {0.3, 16, 9, 9, 4, 1, 0},
-                               {1.5, 16, 9, 9, 4, 1, 0},        {3, 16, 10, 9, 1, 1, 0},
+    static const Row bf16[] = {{1.5, 16, 9, 9, 4, 1, 0},        {3, 16, 10, 9, 1, 1, 0},
                                {8, 32, 19, 12, 1, 1, 0},        {24, 64, 18, 11, 1, 1, 0},
                                {96, 128, 22, 22, 2, 1, 0},      {384, 128, 22, 22, 1, 1, 8, 8},
                                {1e30, 256, 25, 25, 1, 1, 8}};
