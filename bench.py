@@ -385,7 +385,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="T of the headline step (default: largest of the sweep)")
     ap.add_argument("--sweep", default="1,32,256,1024,4096", help="comma-separated T values ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--plan", default=None, help="block_m,gemm1_tile,gemm2_tile,split_k for the headline T")
+    ap.add_argument("--plan", default=None, help="block_m,gemm1_tile,gemm2_tile,split_k[,split_k1[,split_tail"
+                    "[,max_workgroups[,split_tail1]]]] for the headline T")
     ap.add_argument("--workload", default="layer", choices=("layer", "grouped_gemm"),
                     help="the fused layer (default) or the EP-MoE grouped GEMM over pre-grouped rows")
     ap.add_argument("--dtype", default="fp8", choices=("bf16", "fp8"), help="grouped_gemm: operand type")
