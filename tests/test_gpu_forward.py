@@ -4,7 +4,8 @@ Layer outputs within the relative-L2 budget (bf16 weights 1e-2, fp8 and int4 3e-
 five configs; the routing and align intermediates the forward leaves in its workspace
 bit-exact; every plan the library accepts on the tiny layer; the full-size Mixtral and
 Llama-4-Scout shapes at the largest T on tokens the oracle computes one by one; bitwise
-determinism, hipGraph replay equal to eager, split-K on and off in agreement.
+determinism, hipGraph replay equal to eager, split-K on and off in agreement; routing that
+sends every token to the same one or two experts.
 """
 import numpy as np
 import pytest
@@ -568,6 +569,63 @@ def test_split_tail1_mixtral_sampled():
     say("  sampled rel-L2 %.3e" % err)
     assert err <= TOL[c.cfg.wdtype]
     again, _ = c.gpu(T, p, ws=ws)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg,hot", [(TAIL_SMALL, (0, 1)), (TAIL_SMALL_TOP1, (3,))], ids=["top2_two_experts", "top1_one_expert"])
+def test_degenerate_routing(cfg, hot):
+    """Every token routed to the same expert(s), all others empty: one or two experts hold
+    every pair in several row blocks.  A spread of plans (split-K, both split tails, grids
+    capped so that tails are taken) against the oracle."""
+    c = small_case(cfg)
+    T = 300
+    x, lg = c.inputs(T)
+    lg = lg.float()
+    top = lg.max(dim=1).values
+    for i, e in enumerate(hot):
+        lg[:, e] = top + 4.0 - 2.0 * i
+    lg = lg.to(torch.bfloat16)
+    ids, w = oracle_route(c.cfg, bits(lg), c.bias)
+    assert set(np.unique(ids).tolist()) == set(hot)
+    ref = oracle.forward(c.W, bits(x), ids, w)
+    n = 0
+    for g in (24, 0):
+        plans = valid_plans(c.layer, T, split1=(1,), splits=(1, 2), tails=(0, 4), max_workgroups=g, tails1=(0, 4))
+        for p in plans[::5]:
+            say("degenerate routing", cfg.name, "plan", p.as_tuple())
+            out = c.layer.forward(x.cuda(), lg.cuda(), plan=p)
+            torch.cuda.synchronize()
+            err = rel_l2(bf16_to_f64(out), ref)
+            assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+            n += 1
+    assert n >= 10
+
+
+def test_degenerate_routing_mixtral_sampled():
+    """The full-size Mixtral shard at T=4096 with every token sent to experts 5 and 6: two
+    experts of 4096 rows each, six empty, under the default plan.  Sampled tokens against the
+    oracle, and the same output on a second call."""
+    c = case("mixtral")
+    T = 4096
+    x, lg = c.inputs(T)
+    lg = lg.float()
+    top = lg.max(dim=1).values
+    lg[:, 5] = top + 4.0
+    lg[:, 6] = top + 2.0
+    lg = lg.to(torch.bfloat16)
+    ids, w = oracle_route(c.cfg, bits(lg), c.bias)
+    assert set(np.unique(ids).tolist()) == {5, 6}
+    say("degenerate routing mixtral T=%d plan %s" % (T, c.layer.plan(T).as_tuple()))
+    ws = c.layer.workspace(T)
+    out = c.layer.forward(x.cuda(), lg.cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    tokens = [0, 1, 2047, 4094, 4095]
+    ref = oracle.forward(c.W, bits(x), ids, w, tokens=tokens)
+    err = rel_l2(bf16_to_f64(out[tokens]), ref)
+    say("  sampled rel-L2 %.3e" % err)
+    assert err <= TOL[c.cfg.wdtype]
+    again = c.layer.forward(x.cuda(), lg.cuda(), workspace=ws)
+    torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
 
 
