@@ -155,9 +155,12 @@ hipError_t launch_f16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream
 // Route + align (+ the activation pass) of a batch of at most kPrologueMaxT tokens in one
 // launch (prologue.hip); results identical to launch_route, launch_align and the fp8 /
 // fp16 activation kernels.
-// Tokens: up to 64 (16 waves route 4 tokens each); 16 for the fp8 pass (the batch's amax,
-// then its codes, in one workgroup) and for layers whose routing per token is long.
-constexpr int kPrologueMaxT = 64, kPrologueMaxTFp8 = 16;
+// Tokens: up to 64 (16 waves route 4 tokens each); 16 for layers whose routing per token is
+// long (more than 64 experts, or top-k above 2).  The fp8 pass (the batch's amax, then its codes, in one workgroup whose threads
+// hold the batch in registers) takes at most kPrologueFp8Elems elements.
+constexpr int kPrologueMaxT = 64, kPrologueMaxTLongRoute = 16;
+constexpr int kPrologueActRegs = 16;                                // 16-byte groups per thread
+constexpr int64_t kPrologueFp8Elems = (int64_t)kPrologueActRegs * 1024 * 8;
 enum { PROLOGUE_ACT_NONE = 0, PROLOGUE_ACT_FP8 = 1, PROLOGUE_ACT_F16_PERM = 2 };
 struct PrologueArgs {
     RouteArgs route;             // zero_ptr unused

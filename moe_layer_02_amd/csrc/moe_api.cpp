@@ -132,11 +132,14 @@ constexpr size_t kTailInfoBytes = 256;
 
 // the one-launch prologue (route, align, activation pass) takes batches up to this size:
 // its 16 waves route the tokens in turn, which pays while a token's routing is short (up
-// to 64 experts: Mixtral T=32 265 against 272 us); the 256-expert grouped gate keeps one
-// wave per token beyond 16 tokens (DeepSeek T=64: 773 against 813 us in the prologue)
+// to 64 experts and top-2: Mixtral T=32 265 against 272 us); longer routing keeps one
+// wave per token beyond 16 tokens (DeepSeek's grouped top-8 of 256, T=64: 773 against 813
+// us; Qwen2's top-8 of 64, T=32: the prologue takes 20 us and the layer 4% longer); the
+// fp8 pass holds the batch in one workgroup's registers
 int prologue_max_t(const moe_layer *L) {
-    if (L->weight_dtype == MOE_DT_FP8_E4M3) return kPrologueMaxTFp8;
-    return L->E <= 64 ? kPrologueMaxT : kPrologueMaxTFp8;
+    const int t = L->E <= 64 && L->route.top_k <= 2 ? kPrologueMaxT : kPrologueMaxTLongRoute;
+    if (L->weight_dtype == MOE_DT_FP8_E4M3) return (int)std::min<int64_t>(t, kPrologueFp8Elems / L->H);
+    return t;
 }
 
 struct Workspace {

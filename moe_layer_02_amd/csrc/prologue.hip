@@ -6,9 +6,9 @@
 //   workgroup 0: wave w routes tokens w, w + 16, ... (route_dev.h), a barrier makes the
 //                pairs visible, then the one-workgroup align (align_dev.h) lays them out;
 //   workgroups 1..: the activation pass, independent of the routing --
-//                fp8 (one workgroup): the largest |x| over the batch (reduced inside the
-//                workgroup, no atomics), then every code with that scale (quant_dev.h), and
-//                the scale; int4: the hidden states to fp16 in the packed-nibble order.
+//                fp8 (one workgroup): the batch into registers, its largest |x| (reduced
+//                inside the workgroup, no atomics), then every code with that scale
+//                (quant_dev.h), and the scale; int4: the hidden states to fp16 in the packed-nibble order.
 #include <algorithm>
 
 #include "align_dev.h"
@@ -36,17 +36,28 @@ __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
             ((uint4 *)p.x16)[i] = bf16x8_to_f16x8_perm(((const uint4 *)p.x)[i]);
         return;
     }
-    // fp8: amax over the batch
+    // fp8: the batch is read once into registers (every load in flight at once), its
+    // largest |x| reduced in the workgroup, and the codes written from the registers.
+    // Groups beyond kPrologueActRegs per thread (none for the sizes the host sends here)
+    // are read again from memory.
+    // (past the end a thread reads the last group again: no effect on the maximum)
+    const uint4 *xv = (const uint4 *)p.x;
+    const int last = (int)min<int64_t>(n8, (int64_t)kPrologueActRegs * 1024) - 1;
+    uint4 v[kPrologueActRegs];
+#pragma unroll
+    for (int j = 0; j < kPrologueActRegs; j++) v[j] = xv[min(tid + j * 1024, last)];
     float m = 0.0f;
-    for (int64_t i = tid; i < n8; i += 1024) {
-        const uint4 v = ((const uint4 *)p.x)[i];
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    auto fold = [&](const uint4 &g) {
+        const uint32_t wv[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             m = fmaxf(m, fabsf(__uint_as_float(wv[q] << 16)));
             m = fmaxf(m, fabsf(__uint_as_float(wv[q] & 0xFFFF0000u)));
         }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < kPrologueActRegs; j++) fold(v[j]);
+    for (int64_t i = tid + (int64_t)kPrologueActRegs * 1024; i < n8; i += 1024) fold(((const uint4 *)p.x)[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
     __shared__ float wmax[16];
@@ -61,15 +72,23 @@ __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
         *p.x_amax = __float_as_uint(amax);
         *p.x_scale = scale;
     }
-    for (int64_t i = tid; i < n8; i += 1024) {
-        const uint4 v = ((const uint4 *)p.x)[i];
+    // the codes are derived from v again, not from values kept since the maximum (which
+    // would hold eight floats per group through the reduction)
+#pragma unroll
+    for (int j = 0; j < kPrologueActRegs; j++) asm volatile("" : "+v"(v[j].x), "+v"(v[j].y), "+v"(v[j].z), "+v"(v[j].w));
+    auto codes = [&](const uint4 &g) {
         uint2 out;
-        out.x = quant_dev::e4m3x4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u), inv);
-        out.y = quant_dev::e4m3x4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
-                                  __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u), inv);
-        ((uint2 *)p.xq)[i] = out;
-    }
+        out.x = quant_dev::e4m3x4(__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xFFFF0000u),
+                                  __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xFFFF0000u), inv);
+        out.y = quant_dev::e4m3x4(__uint_as_float(g.z << 16), __uint_as_float(g.z & 0xFFFF0000u),
+                                  __uint_as_float(g.w << 16), __uint_as_float(g.w & 0xFFFF0000u), inv);
+        return out;
+    };
+#pragma unroll
+    for (int j = 0; j < kPrologueActRegs; j++)
+        if (tid + j * 1024 <= last) ((uint2 *)p.xq)[tid + j * 1024] = codes(v[j]);
+    for (int64_t i = tid + (int64_t)kPrologueActRegs * 1024; i < n8; i += 1024)
+        ((uint2 *)p.xq)[i] = codes(((const uint4 *)p.x)[i]);
 }
 
 template <int EPL>

@@ -401,8 +401,9 @@ def test_graph_replay_matches_eager(name, T):
     ("mixtral", 64, ["prologue", "gemm1", "gemm2", "reduce"]),
     ("mixtral", 65, ["route", "align", "gemm1", "gemm2", "reduce"])])
 def test_small_batch_prologue(name, T, expect):
-    """Up to 64 tokens (16 for fp8 and for 256 experts), route, align and the activation
-    pass run as one launch;
+    """Up to 64 tokens (16 where a token's routing is long: more than 64 experts or top-k
+    above 2; for fp8 also at most 131072 elements of hidden states), route, align and the
+    activation pass run as one launch;
     the forward's routing and align results stay bit-exact and the output within tolerance."""
     c = case(name)
     x, lg = c.inputs(T)
@@ -422,6 +423,35 @@ def test_small_batch_prologue(name, T, expect):
     ref, _, _ = c.oracle(T, tokens=tokens)
     assert rel_l2(bf16_to_f64(out[tokens]), ref) <= TOL[c.cfg.wdtype]
     check_intermediates(c, T, plan, ws)
+
+
+FP8_WIDE = synth.CONFIGS["qwen2"].with_shape(name="fp8wide", E=8, k=2, H=8192, I=256)
+
+
+@pytest.mark.parametrize("T", [15, 16, 17])
+def test_fp8_prologue_register_limit(T):
+    """fp8 with short routing and H=8192: the prologue's activation pass holds the batch in
+    registers, 131072 elements at most, so it takes T <= 16 (T=16 fills every register
+    group, T=15 leaves the last ones reading the final group again) and T=17 goes to the
+    separate kernels.  Codes bit-exact, output within tolerance."""
+    c = small_case(FP8_WIDE)
+    x, lg = c.inputs(T)
+    plan = c.layer.plan(T)
+    ws = c.layer.workspace(T, plan)
+    out = torch.empty((T, c.cfg.H), dtype=torch.bfloat16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
+    say("profiled forward fp8wide T=%d" % T)
+    stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), out, ws, ev, plan)
+    torch.cuda.synchronize()
+    assert ("prologue" in stages) == (T <= 16), stages
+    xf = x.float().numpy()
+    amax = np.float32(np.abs(xf).max())
+    ref_codes = oracle.f32_to_e4m3((xf * np.float32(np.float32(448.0) / amax)).astype(np.float32))
+    got = workspace_view(c.layer, T, plan, ws, "x_q", torch.uint8, T * c.cfg.H).cpu().numpy().reshape(T, -1)
+    same = (got == ref_codes) | ((got & 0x7F) == 0) & ((ref_codes & 0x7F) == 0)
+    assert same.all(), "%d codes differ" % (~same).sum()
+    ref, _, _ = c.oracle(T)
+    assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype]
 
 
 def test_profiled_forward_records_every_stage():
