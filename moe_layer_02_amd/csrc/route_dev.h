@@ -280,9 +280,11 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         }
     }
 
-    // k rounds of arg-max; slot j is kept by lane j
+    // k rounds of arg-max; slot j is kept by lane j (its expert and the winner's logit or
+    // score).  The slot weights are computed afterwards, each on its own lane, so that the
+    // fp64 exp of a softmax slot is not on the chain of arg-max rounds.
     int my_id = 0;
-    double my_val = 0.0, norm = 0.0;
+    float my_bv = 0.0f;
     for (int j = 0; j < a.k; j++) {
         uint64_t br = 0;
 #pragma unroll
@@ -307,13 +309,14 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
 #pragma unroll
         for (int i = 0; i < EPL; i++)
             if (lane + kWave * i == bi) live[i] = false;
-        const double v = softmax ? exp((double)bv - m) / z : (double)bv;
-        norm += v;
         if (lane == j) {
             my_id = bi;
-            my_val = v;
+            my_bv = bv;
         }
     }
+    const double my_val = softmax ? exp((double)my_bv - m) / z : (double)my_bv;
+    double norm = 0.0;   // summed over the slots in order 0 .. k-1
+    for (int j = 0; j < a.k; j++) norm += __shfl(my_val, j, kWave);
     if (lane < a.k) {
         const double w = a.renorm ? my_val / norm : my_val;
         a.ids[(int64_t)t * a.k + lane] = my_id;
