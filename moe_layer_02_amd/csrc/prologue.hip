@@ -41,6 +41,7 @@ __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
     // Groups beyond kPrologueActRegs per thread (none for the sizes the host sends here)
     // are read again from memory.
     // (past the end a thread reads the last group again: no effect on the maximum)
+    if (n8 <= 0) return;
     const uint4 *xv = (const uint4 *)p.x;
     const int last = (int)min<int64_t>(n8, (int64_t)kPrologueActRegs * 1024) - 1;
     uint4 v[kPrologueActRegs];
