@@ -1,16 +1,20 @@
 """Benchmark of the fused-MoE layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config mixtral] [--tokens 4096] [--sweep 1,32,256]
+    python bench.py [--steps K] [--warmup W]                       # headline + every config's sweep
+    python bench.py --config mixtral [--tokens 4096] [--sweep 1,32,256]   # one config only
 
 A step is one moe_forward (route, align, [fp8 quantisation], GEMM1, GEMM2, reduce) over one
 batch of T tokens of seeded synthetic inputs already resident in HBM; steps are replayed
-from a captured hipGraph.  Prints one JSON line: whole-layer tokens/s (the headline, K
+from a captured hipGraph.  Prints one JSON line.  The headline (value, ms_per_step, config)
+is the largest single-GPU layer, Llama-4-Scout at T=8192 (bf16, 4.2 GB of weights, 2.06
+TFLOP per step); its line also carries a short T sweep of every layer (Mixtral TP2,
+Qwen2-57B TP4 fp8, DeepSeek-V3 int4, Scout).  Each point reports whole-layer tokens/s (K
 replays back to back), the same step with cold caches (a 512 MiB buffer read before each
-replay, outside the timed region; median, p10, p90),
-TFLOP/s and HBM GB/s with their fractions of the MI355X peaks, the dominant kernel's
-roofline (its duration from HIP events recorded on the launch stream around each step of
-the forward), the CPU oracle's throughput on a bounded sample of the same workload, and a
-sweep of the same numbers over T.
+replay, outside the timed region; median, p10, p90), TFLOP/s and HBM GB/s with their
+fractions of the MI355X peaks, and the step's kernels' durations.  The headline adds the
+dominant kernel's roofline (its duration from HIP events recorded on the launch stream
+around each step of the forward) and the CPU oracle's throughput on a bounded sample of the
+same workload, on the host's cores.
 """
 from __future__ import annotations
 
@@ -42,6 +46,20 @@ WORKLOAD = {
     "scout": "Llama-4-Scout MoE layer (E=16, top-1 sigmoid, Zipf(1.2) load, H=5120, I=8192, bf16)",
     "tiny": "tiny MoE layer (E=8, top-2 softmax, H=128, I=256, bf16)",
 }
+
+
+# the headline: the largest layer that fits one GPU (4.2 GB of bf16 weights, 2.06 TFLOP per step)
+HEADLINE = ("scout", 8192)
+# each layer's short T sweep in the same line: small batches stream weights, large ones are
+# MFMA work
+SWEEPS = {"scout": (1, 32, 2048, 8192), "mixtral": (1, 32, 1024, 4096), "qwen2": (1, 32, 1024, 4096),
+          "deepseek": (1, 32, 512)}
+
+
+def sweep_point(name, m):
+    d = {"config": name}
+    d.update({k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()})
+    return d
 
 
 def bytes_per_weight(cfg):
@@ -141,16 +159,20 @@ class Bench:
 
     def time_stages(self, T, plan, bufs, steps):
         """Average duration of each step of the forward, from HIP events recorded on the
-        launch stream before and after each kernel (eager launches)."""
+        launch stream before and after each kernel: `steps` eager forwards launched back to
+        back (one warm-up call first), read after one synchronisation."""
         x, lg, ws, out = bufs
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
-        acc = {}
-        names = None
-        for i in range(steps + 1):
+        abi.moe_forward_profiled(self.layer.struct, T, x, lg, out, ws,
+                                 [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)], plan)
+        torch.cuda.synchronize()
+        evs, names = [], None
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(abi.STAGE_COUNT + 1)]
             names = abi.moe_forward_profiled(self.layer.struct, T, x, lg, out, ws, ev, plan)
-            torch.cuda.synchronize()
-            if i == 0:
-                continue                                  # first call: warm
+            evs.append(ev)
+        torch.cuda.synchronize()
+        acc = {}
+        for ev in evs:
             for j, n in enumerate(names):
                 acc[n] = acc.get(n, 0.0) + ev[j].elapsed_time(ev[j + 1]) * 1e3
         return {n: acc[n] / steps for n in names}
@@ -216,9 +238,29 @@ def measured_traffic(cfg, T, kernel):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def host_cpu():
+    """(threads this process may use, the host CPU's model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
 def cpu_baseline(b: Bench, T, budget_s=15.0):
-    """The oracle (single-threaded C, fp64) on a sample of the same workload: routing of all
-    T tokens, then the layer output token by token until the time budget is spent."""
+    """The oracle (plain C, fp64, tokens spread over the host's cores, at most 16 threads) on
+    a sample of the same workload: routing of all T tokens, then the layer output of random
+    tokens in batches until the time budget is spent (w8a8 fp8 needs every token's
+    intermediate for its second scale, so there the whole layer runs at a smaller T)."""
     import oracle
     cfg = b.cfg
     x, lg = synth.hidden_states(cfg, T), synth.router_logits(cfg, T)
@@ -233,31 +275,33 @@ def cpu_baseline(b: Bench, T, budget_s=15.0):
     else:
         W = oracle.Weights(wd, cfg.E, cfg.H, cfg.I, h["w13"].numpy(), h["w2"].numpy(), w13_s=bits(h["w13_s"]),
                            w13_z=bits(h["w13_z"]), w2_s=bits(h["w2_s"]), w2_z=bits(h["w2_z"]))
+    ncpu, model = host_cpu()
+    threads = oracle.default_threads()
     t0 = time.time()
     ids, w = oracle.route(cfg.route_kind, cfg.E, cfg.k, bits(lg), renormalize=cfg.renormalize, n_group=cfg.n_group,
                           topk_group=cfg.topk_group, routed_scaling=cfg.routed_scaling,
                           bias=None if b.bias is None else b.bias.numpy())
     t_route = time.time() - t0
+    common = dict(unit="tokens/s", cores=threads, kind="oracle", host_cpus=ncpu, cpu_model=model)
     if cfg.wdtype == synth.WDT_FP8:
-        # w8a8 needs every token's intermediate for its second scale: time the whole layer at
-        # a smaller T of the same layer instead
-        Ts = max(1, min(T, 8))
+        Ts = max(1, min(T, 8 * threads))
         t0 = time.time()
-        oracle.forward(W, bits(x[:Ts]), ids[:Ts], w[:Ts])
+        oracle.forward(W, bits(x[:Ts]), ids[:Ts], w[:Ts], threads=threads)
         el = time.time() - t0
-        return dict(value=round(Ts / el, 4), unit="tokens/s", cores=1, kind="oracle",
-                    sample="whole w8a8 layer at T=%d (first %d tokens of the batch), %.1f s" % (Ts, Ts, el))
-    n, el = 0, 0.0
-    rng = np.random.default_rng(0)
-    order = rng.permutation(T)
-    while n < T and (el < budget_s or n < 2):
+        return dict(value=round(Ts / el, 4), sample="whole w8a8 layer at T=%d (first %d tokens of the batch), "
+                    "%d threads, %.1f s" % (Ts, Ts, threads, el), **common)
+    order = np.random.default_rng(0).permutation(T)
+    n, el, batch = 0, 0.0, threads
+    xb = bits(x)
+    while n < T and (el < budget_s or n == 0):
+        toks = [int(t) for t in order[n:n + batch]]
         t0 = time.time()
-        oracle.forward(W, bits(x), ids, w, tokens=[int(order[n])])
+        oracle.forward(W, xb, ids, w, tokens=toks, threads=threads)
         el += time.time() - t0
-        n += 1
+        n += len(toks)
     per_token = el / n + t_route / T
-    return dict(value=round(1.0 / per_token, 4), unit="tokens/s", cores=1, kind="oracle",
-                sample="%d of %d tokens (random), routing of all %d; %.1f s" % (n, T, T, el + t_route))
+    return dict(value=round(1.0 / per_token, 4), sample="%d of %d tokens (random, in batches of %d), routing of "
+                "all %d; %d threads, %.1f s" % (n, T, batch, T, threads, el + t_route), **common)
 
 
 # ---- the EP-MoE grouped GEMM (pre-permuted contiguous segments) ------------------------
@@ -381,9 +425,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mixtral", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--tokens", type=int, default=None, help="T of the headline step (default: largest of the sweep)")
-    ap.add_argument("--sweep", default="1,32,256,1024,4096", help="comma-separated T values ('' for none)")
+    ap.add_argument("--config", default=None, choices=sorted(synth.CONFIGS),
+                    help="one layer only (default: the Scout T=8192 headline and every layer's sweep)")
+    ap.add_argument("--tokens", type=int, default=None, help="T of the headline step (default: the layer's largest)")
+    ap.add_argument("--sweep", default=None, help="comma-separated T values of the headline layer's sweep "
+                    "('' for none; default: its standard sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--plan", default=None, help="block_m,gemm1_tile,gemm2_tile,split_k[,split_k1[,split_tail"
                     "[,max_workgroups[,split_tail1]]]] for the headline T")
@@ -399,30 +445,45 @@ def main():
         sys.exit(2)
     torch.cuda.init()
     if args.workload == "grouped_gemm":
-        if args.sweep == "1,32,256,1024,4096":
+        if args.sweep is None:
             args.sweep = "1,2,4,8,16,32,64,128,256,512,1024,2048"
         grouped_gemm_bench(args)
         return
-    cfg = synth.CONFIGS[args.config]
-    T = args.tokens or cfg.t_max
+    if args.config is None:
+        cfg, T = synth.CONFIGS[HEADLINE[0]], args.tokens or HEADLINE[1]
+        others = [c for c in SWEEPS if c != cfg.name]
+    else:
+        cfg, T = synth.CONFIGS[args.config], args.tokens or synth.CONFIGS[args.config].t_max
+        others = []
     plan = abi.Plan(*[int(v) for v in args.plan.split(",")]) if args.plan else None
     b = Bench(cfg, plan, T)
     head = measure(b, T, args.steps, args.warmup, stage_steps=max(3, min(args.steps, 10)))
-    print("[bench] T=%d %.3f ms/step %s" % (T, head["ms_per_step"], head["plan"]), file=sys.stderr, flush=True)
-    sweep = []
-    for t in [int(s) for s in args.sweep.split(",") if s.strip()]:
-        if t == T or t > cfg.t_max:
-            continue
-        m = measure(b, t, args.steps, args.warmup, stage_steps=3)
-        sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()})
-        print("[bench] T=%d %.3f ms/step" % (t, m["ms_per_step"]), file=sys.stderr, flush=True)
+    print("[bench] %s T=%d %.3f ms/step %s" % (cfg.name, T, head["ms_per_step"], head["plan"]),
+          file=sys.stderr, flush=True)
+    head_ts = SWEEPS.get(cfg.name, ()) if args.sweep is None else \
+        tuple(int(s) for s in args.sweep.split(",") if s.strip())
+    sweep = [sweep_point(cfg.name, head)]
+    for t in head_ts:
+        if t != T and t <= cfg.t_max:
+            sweep.append(sweep_point(cfg.name, measure(b, t, args.steps, args.warmup, stage_steps=3)))
+            print("[bench] %s T=%d %.3f ms/step" % (cfg.name, t, sweep[-1]["ms_per_step"]), file=sys.stderr, flush=True)
     if args.copy_probe_mib > 0:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
     cpu = None if args.no_cpu_baseline else cpu_baseline(b, T)
     roof = kernel_roofline(cfg, head)
+    del b
+    torch.cuda.empty_cache()
+    for name in others:   # the other layers' sweeps, one layer's weights on the GPU at a time
+        ob = Bench(synth.CONFIGS[name])
+        for t in SWEEPS[name]:
+            sweep.append(sweep_point(name, measure(ob, t, args.steps, args.warmup, stage_steps=3)))
+            print("[bench] %s T=%d %.3f ms/step" % (name, t, sweep[-1]["ms_per_step"]), file=sys.stderr, flush=True)
+        del ob
+        torch.cuda.empty_cache()
     line = {
         "metric": METRIC, "value": round(head["tokens_per_s"], 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),

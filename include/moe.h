@@ -329,7 +329,8 @@ moe_status moe_grouped_gemm_workspace_bytes(const moe_grouped_gemm_desc *desc, i
  *  workspace  [device] at least moe_grouped_gemm_workspace_bytes, 256-byte aligned
  *  tile       a pipelined tile id of the dtype whose BN divides N and BK divides K, or -1
  * Errors: MOE_ERR_INVALID_ARGUMENT (checked before anything is enqueued),
- * MOE_ERR_UNSUPPORTED when M*K bytes of X exceed 2^32 - 1 (32-bit row offsets),
+ * MOE_ERR_UNSUPPORTED when M*K bytes of X or N*K bytes of one group's W exceed 2^32 - 1
+ * (32-bit row offsets; moe_grouped_gemm_default_tile and _workspace_bytes report it too),
  * MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP. */
 moe_status moe_grouped_gemm(const moe_grouped_gemm_desc *desc, int32_t M, const void *x, const float *x_scale,
                             const int32_t *m_sizes, void *y, void *workspace, size_t workspace_bytes,

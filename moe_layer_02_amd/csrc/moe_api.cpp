@@ -486,6 +486,14 @@ int32_t grouped_default_tile(const moe_grouped_gemm_desc *d, int32_t M) {
     return -1;
 }
 
+// The GEMM addresses a row of one group's weight matrix with a 32-bit byte offset from the
+// group's base: N * K elements must fit that range.
+moe_status check_grouped_size(const moe_grouped_gemm_desc *d) {
+    if (!d || d->N < 1 || d->K < 1) return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t ebytes = d->dtype == MOE_DT_FP8_E4M3 ? 1 : 2;
+    return (int64_t)d->N * d->K * ebytes > (int64_t)UINT32_MAX ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
 struct GroupedWorkspace {
     size_t sorted, eids, npp, total;
     int64_t cap;
@@ -683,6 +691,8 @@ moe_status moe_grouped_gemm_default_tile(const moe_grouped_gemm_desc *desc, int3
     if (!desc || !tile || M < 0) return MOE_ERR_INVALID_ARGUMENT;
     TileInfo t;
     if (desc->num_groups < 1 || desc->num_groups > kMaxGroups) return MOE_ERR_INVALID_ARGUMENT;
+    moe_status st = check_grouped_size(desc);
+    if (st != MOE_OK) return st;
     const int32_t g = grouped_default_tile(desc, M);
     if (g < 0) return check_grouped(desc, 0, &t) == MOE_OK ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARGUMENT;
     *tile = g;
@@ -693,6 +703,7 @@ moe_status moe_grouped_gemm_workspace_bytes(const moe_grouped_gemm_desc *desc, i
                                             size_t *bytes) {
     if (!bytes || M < 0) return MOE_ERR_INVALID_ARGUMENT;
     moe_status st;
+    if ((st = check_grouped_size(desc)) != MOE_OK) return st;
     if (tile < 0 && (st = moe_grouped_gemm_default_tile(desc, M, &tile)) != MOE_OK) return st;
     TileInfo t;
     if ((st = check_grouped(desc, tile, &t)) != MOE_OK) return st;
@@ -705,6 +716,7 @@ moe_status moe_grouped_gemm(const moe_grouped_gemm_desc *desc, int32_t M, const 
                             void *stream) {
     if (M < 0) return MOE_ERR_INVALID_ARGUMENT;
     moe_status st;
+    if ((st = check_grouped_size(desc)) != MOE_OK) return st;
     if (tile < 0 && (st = moe_grouped_gemm_default_tile(desc, M, &tile)) != MOE_OK) return st;
     TileInfo t;
     if ((st = check_grouped(desc, tile, &t)) != MOE_OK) return st;

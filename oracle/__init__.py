@@ -3,8 +3,9 @@
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import this package.  The product library never loads it.
 
-This module is a thin ctypes wrapper over ``moe_oracle.c`` (plain C, fp64 accumulation);
-every formula lives there, with its citation.  Arrays are numpy; bf16 tensors travel as
+This module is a thin ctypes wrapper over ``moe_oracle.c`` (plain C, fp64 accumulation,
+tokens optionally spread over threads with results identical to one thread); every formula
+lives there, with its citation.  Arrays are numpy; bf16 tensors travel as
 their uint16 bit patterns, fp8 and packed int4 weights as uint8, fp16 scales and zero
 points as uint16 bit patterns.
 
@@ -41,7 +42,7 @@ def build(force: bool = False) -> str:
         os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "moe_oracle.h")))
     if force or stale:
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-pthread", "-fPIC", "-shared",
                                _SRC, "-lm", "-o", tmp])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -78,6 +79,8 @@ def lib():
         L.orc_weight.restype = D
         L.orc_forward.argtypes = [ctypes.POINTER(_Weights), I, I, P, P, P, I, P, P, P]
         L.orc_forward.restype = I
+        L.orc_forward_ex.argtypes = [ctypes.POINTER(_Weights), I, I, P, P, P, I, P, P, P, I, I]
+        L.orc_forward_ex.restype = I
         L.orc_fp8_intermediate.argtypes = [ctypes.POINTER(_Weights), I, I, P, P, P, P, P]
         L.orc_fp8_intermediate.restype = I
         L.orc_grouped_gemm.argtypes = [I, I, I, I, I, P, F, P, P, P, P]
@@ -192,8 +195,23 @@ class Weights:
         return lib().orc_weight(ctypes.byref(self.c), m, e, n, c)
 
 
-def forward(W: Weights, hidden_bits, ids, weights, tokens=None, return_scales=False):
-    """Layer output in fp64: [T,H], or [len(tokens),H] for the listed tokens."""
+def default_threads() -> int:
+    """Threads for the oracle's per-token work: the host's CPUs, at most 16 (MOE_ORACLE_THREADS
+    overrides).  The results do not depend on it."""
+    env = os.environ.get("MOE_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def forward(W: Weights, hidden_bits, ids, weights, tokens=None, return_scales=False, threads=None, acc32=False):
+    """Layer output in fp64: [T,H], or [len(tokens),H] for the listed tokens.  threads: how
+    many threads share the tokens (default: default_threads(); the result is the same for
+    every count); acc32: accumulate in fp32 instead of fp64 (a cross-check of the fp64 run)."""
     hidden_bits = _c(hidden_bits, np.uint16)
     ids = _c(ids, np.int32)
     weights = _c(weights, np.float32)
@@ -203,8 +221,9 @@ def forward(W: Weights, hidden_bits, ids, weights, tokens=None, return_scales=Fa
     n = T if tok is None else tok.size
     out = np.zeros((n, W.H), np.float64)
     dbg = np.zeros(2, np.float32)
-    rc = lib().orc_forward(ctypes.byref(W.c), T, k, _ptr(hidden_bits), _ptr(ids), _ptr(weights),
-                           0 if tok is None else tok.size, _ptr(tok), _ptr(out), _ptr(dbg))
+    nth = default_threads() if threads is None else int(threads)
+    rc = lib().orc_forward_ex(ctypes.byref(W.c), T, k, _ptr(hidden_bits), _ptr(ids), _ptr(weights),
+                              0 if tok is None else tok.size, _ptr(tok), _ptr(out), _ptr(dbg), int(bool(acc32)), nth)
     if rc:
         raise ValueError("orc_forward rejected its arguments")
     return (out, dbg) if return_scales else out

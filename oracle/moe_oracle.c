@@ -13,11 +13,12 @@
  * permutation and padding are an implementation device and do not change the result, so
  * the oracle applies the definition directly, one token and one expert at a time.
  *
- * Build: gcc -O2 -std=c11 -fPIC -shared moe_oracle.c -lm  (no GPU headers, no threads).
+ * Build: gcc -O2 -std=c11 -pthread -fPIC -shared moe_oracle.c -lm  (no GPU headers).
  */
 #include "moe_oracle.h"
 
 #include <math.h>
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -296,6 +297,15 @@ double orc_weight(const orc_weights *W, int m, int e, int64_t n, int64_t c)
     return ((double)q - z) * s;
 }
 
+/* E4M3 codes decoded once into a table of their values (from orc_e4m3_to_f32, so the table
+ * holds exactly what the decoder returns): the rows of an fp8 layer are decoded with it. */
+static float e4m3_value[256];
+static pthread_once_t e4m3_once = PTHREAD_ONCE_INIT;
+static void e4m3_fill(void)
+{
+    for (int c = 0; c < 256; c++) e4m3_value[c] = orc_e4m3_to_f32((uint8_t)c);
+}
+
 /* Dequantise one row of matrix m of expert e into buf (length cols): the value orc_weight
  * gives for every column, walking the row once (an int4 group's scale and zero point are
  * decoded once per group). */
@@ -311,7 +321,8 @@ static void weight_row(const orc_weights *W, int m, int e, int64_t n, double *bu
     if (W->wdtype == ORC_FP8_E4M3) {
         const uint8_t *row = (const uint8_t *)(m == 0 ? W->w13 : W->w2) + ((int64_t)e * rows + n) * cols;
         double scale = (m == 0 ? W->w13_scale : W->w2_scale)[e];
-        for (int64_t c = 0; c < cols; c++) buf[c] = (double)orc_e4m3_to_f32(row[c]) * scale;
+        pthread_once(&e4m3_once, e4m3_fill);
+        for (int64_t c = 0; c < cols; c++) buf[c] = (double)e4m3_value[row[c]] * scale;
         return;
     }
     const uint8_t *row = (const uint8_t *)(m == 0 ? W->w13 : W->w2) + ((int64_t)e * rows + n) * (cols / 2);
@@ -326,33 +337,47 @@ static void weight_row(const orc_weights *W, int m, int e, int64_t n, double *bu
     }
 }
 
-static double dot(const double *a, const double *b, int64_t n)
+/* Accumulation precision of the FFN.  ACC64: products and sums in fp64 (the reference the
+ * tests compare against).  ACC32: the layer as the definition reads in single precision --
+ * the dequantised weights and the activations taken as fp32 values, each product and
+ * running sum rounded to fp32, SiLU and the slot sum in fp32 (a second instantiation that
+ * the fp64 one must agree with to within fp32 rounding). */
+enum { ACC64 = 0, ACC32 = 1 };
+
+static double dot(const double *a, const double *b, int64_t n, int acc)
 {
+    if (acc == ACC32) {
+        float s = 0.0f;
+        for (int64_t i = 0; i < n; i++) s += (float)a[i] * (float)b[i];
+        return s;
+    }
     double s = 0.0;
     for (int64_t i = 0; i < n; i++) s += a[i] * b[i];
     return s;
 }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
+static float silu32(float z) { return z / (1.0f + expf(-z)); }
 
 /* h = SiLU(W1_e x) * (W3_e x), length I. */
-static void expert_intermediate(const orc_weights *W, int e, const double *x, double *h, double *row)
+static void expert_intermediate(const orc_weights *W, int acc, int e, const double *x, double *h, double *row)
 {
     for (int i = 0; i < W->I; i++) {
         weight_row(W, 0, e, i, row);
-        double g = dot(row, x, W->H);
+        double g = dot(row, x, W->H, acc);
         weight_row(W, 0, e, (int64_t)W->I + i, row);
-        double u = dot(row, x, W->H);
-        h[i] = silu(g) * u;
+        double u = dot(row, x, W->H, acc);
+        if (acc == ACC32) h[i] = silu32((float)g) * (float)u;
+        else h[i] = silu(g) * u;
     }
 }
 
 /* y = W2_e h, length H. */
-static void expert_output(const orc_weights *W, int e, const double *h, double *y, double *row)
+static void expert_output(const orc_weights *W, int acc, int e, const double *h, double *y, double *row)
 {
     for (int n = 0; n < W->H; n++) {
         weight_row(W, 1, e, n, row);
-        y[n] = dot(row, h, W->I);
+        y[n] = dot(row, h, W->I, acc);
     }
 }
 
@@ -362,6 +387,103 @@ static int check_weights(const orc_weights *W)
     if (W->wdtype == ORC_INT4_G128 && (W->H % 128 || W->I % 128)) return -1;
     if (W->wdtype != ORC_BF16 && W->wdtype != ORC_FP8_E4M3 && W->wdtype != ORC_INT4_G128) return -1;
     return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* threads over tokens                                                                   */
+/* ------------------------------------------------------------------------------------ */
+
+/* The per-token work below is split over threads by contiguous ranges of tokens.  Each
+ * token's arithmetic is the same whatever the split and every thread writes only its own
+ * tokens' rows, so the results do not depend on the number of threads (bit for bit). */
+typedef struct {
+    const orc_weights *W;
+    int acc, T, k;
+    const uint16_t *hidden;
+    const int32_t *ids;
+    const float *weights;
+    const int32_t *tokens;          /* output rows: token of row q (NULL: row q is token q) */
+    const double *hall;             /* fp8: dequantised intermediate of every pair, or NULL */
+    double *out;                    /* output rows, or (fp8 pass 1) the pairs' intermediates */
+    float s1, inv1;                 /* fp8 pass 1: the activation scale and its inverse */
+    int lo, hi;                     /* this thread's range */
+} job;
+
+/* fp8 pass 1 for tokens [lo, hi): the token's hidden row quantised with the per-tensor
+ * scale and dequantised, then h of each of its k pairs into out. */
+static void *fp8_pass1_range(void *arg)
+{
+    job *j = arg;
+    const orc_weights *W = j->W;
+    int H = W->H, I = W->I;
+    double *x = malloc(sizeof(double) * H), *row = malloc(sizeof(double) * (H > I ? H : I));
+    for (int t = j->lo; t < j->hi; t++) {
+        for (int c = 0; c < H; c++) {
+            float v = orc_bf16_to_f32(j->hidden[(int64_t)t * H + c]) * j->inv1;   /* fp32 product */
+            x[c] = (double)orc_e4m3_to_f32(orc_f32_to_e4m3(v)) * (double)j->s1;
+        }
+        for (int s = 0; s < j->k; s++)
+            expert_intermediate(W, j->acc, j->ids[(int64_t)t * j->k + s], x, j->out + ((int64_t)t * j->k + s) * I, row);
+    }
+    free(x);
+    free(row);
+    return NULL;
+}
+
+/* Output rows [lo, hi): out[t] = sum over slots of w_{t,j} * W2_e h_{t,j}, slots in order. */
+static void *output_range(void *arg)
+{
+    job *jb = arg;
+    const orc_weights *W = jb->W;
+    int H = W->H, I = W->I, k = jb->k;
+    double *x = malloc(sizeof(double) * H), *h = malloc(sizeof(double) * I);
+    double *y = malloc(sizeof(double) * H), *row = malloc(sizeof(double) * (H > I ? H : I));
+    for (int q = jb->lo; q < jb->hi; q++) {
+        int t = jb->tokens ? jb->tokens[q] : q;
+        double *o = jb->out + (int64_t)q * H;
+        for (int n = 0; n < H; n++) o[n] = 0.0;
+        if (!jb->hall)
+            for (int c = 0; c < H; c++) x[c] = orc_bf16_to_f32(jb->hidden[(int64_t)t * H + c]);
+        for (int j = 0; j < k; j++) {
+            int e = jb->ids[(int64_t)t * k + j];
+            const double *hj = h;
+            if (jb->hall) hj = jb->hall + ((int64_t)t * k + j) * I;
+            else expert_intermediate(W, jb->acc, e, x, h, row);
+            expert_output(W, jb->acc, e, hj, y, row);
+            double w = jb->weights[(int64_t)t * k + j];
+            if (jb->acc == ACC32)
+                for (int n = 0; n < H; n++) o[n] = (float)o[n] + (float)w * (float)y[n];
+            else
+                for (int n = 0; n < H; n++) o[n] += w * y[n];
+        }
+    }
+    free(x); free(h); free(y); free(row);
+    return NULL;
+}
+
+/* Run fn over [0, n) in nthreads contiguous ranges (n >= 0, nthreads >= 1). */
+static int run_split(void *(*fn)(void *), const job *proto, int n, int nthreads)
+{
+    if (nthreads > n) nthreads = n > 0 ? n : 1;
+    job *jobs = malloc(sizeof(job) * nthreads);
+    pthread_t *th = malloc(sizeof(pthread_t) * nthreads);
+    int rc = 0;
+    for (int i = 0; i < nthreads; i++) {
+        jobs[i] = *proto;
+        jobs[i].lo = (int)((int64_t)n * i / nthreads);
+        jobs[i].hi = (int)((int64_t)n * (i + 1) / nthreads);
+    }
+    if (nthreads == 1) {
+        fn(&jobs[0]);
+    } else {
+        int started = 0;
+        for (; started < nthreads; started++)
+            if (pthread_create(&th[started], NULL, fn, &jobs[started])) { rc = -1; break; }
+        for (int i = 0; i < started; i++) pthread_join(th[i], NULL);
+    }
+    free(jobs);
+    free(th);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -380,9 +502,9 @@ static void pertensor_scales(float amax, float *scale, float *inv)
 }
 
 /* The w8a8 intermediate of every pair: pass 1 quantises all hidden rows with one scale,
- * computes h = SiLU(g) * u in fp64 from the dequantised codes; pass 2 takes the largest
- * |h| over all T*k pairs (each h rounded to fp32 first) and quantises every h with it. */
-static int fp8_intermediate(const orc_weights *W, int T, int k, const uint16_t *hidden,
+ * computes h = SiLU(g) * u from the dequantised codes; pass 2 takes the largest |h| over
+ * all T*k pairs (each h rounded to fp32 first) and quantises every h with it. */
+static int fp8_intermediate(const orc_weights *W, int acc, int nthreads, int T, int k, const uint16_t *hidden,
                             const int32_t *ids, double *hbuf, float *h32, uint8_t *hq, float *sc)
 {
     int H = W->H, I = W->I;
@@ -393,15 +515,10 @@ static int fp8_intermediate(const orc_weights *W, int T, int k, const uint16_t *
     }
     float s1, inv1;
     pertensor_scales(amax1, &s1, &inv1);
-    double *x = malloc(sizeof(double) * H), *row = malloc(sizeof(double) * (H > I ? H : I));
-    for (int t = 0; t < T; t++) {
-        for (int c = 0; c < H; c++) {
-            float v = orc_bf16_to_f32(hidden[(int64_t)t * H + c]) * inv1;   /* fp32 product */
-            x[c] = (double)orc_e4m3_to_f32(orc_f32_to_e4m3(v)) * (double)s1;
-        }
-        for (int j = 0; j < k; j++)
-            expert_intermediate(W, ids[(int64_t)t * k + j], x, hbuf + ((int64_t)t * k + j) * I, row);
-    }
+    job p = {0};
+    p.W = W; p.acc = acc; p.T = T; p.k = k; p.hidden = hidden; p.ids = ids; p.out = hbuf;
+    p.s1 = s1; p.inv1 = inv1;
+    if (run_split(fp8_pass1_range, &p, T, nthreads)) return -1;
     float amax2 = 0.0f;
     for (int64_t i = 0; i < (int64_t)T * k * I; i++) {
         float a = fabsf((float)hbuf[i]);
@@ -417,8 +534,6 @@ static int fp8_intermediate(const orc_weights *W, int T, int k, const uint16_t *
         hbuf[i] = (double)orc_e4m3_to_f32(code) * (double)s2;
     }
     if (sc) { sc[0] = s1; sc[1] = s2; }
-    free(x);
-    free(row);
     return 0;
 }
 
@@ -427,7 +542,7 @@ int orc_fp8_intermediate(const orc_weights *W, int T, int k, const uint16_t *hid
 {
     if (check_weights(W) || W->wdtype != ORC_FP8_E4M3 || T < 0 || k < 1) return -1;
     double *hbuf = malloc(sizeof(double) * ((size_t)T * k * W->I + 1));
-    int rc = fp8_intermediate(W, T, k, hidden_bf16, ids, hbuf, h, hq, scales);
+    int rc = fp8_intermediate(W, ACC64, 1, T, k, hidden_bf16, ids, hbuf, h, hq, scales);
     free(hbuf);
     return rc;
 }
@@ -436,45 +551,37 @@ int orc_fp8_intermediate(const orc_weights *W, int T, int k, const uint16_t *hid
 /* the layer                                                                             */
 /* ------------------------------------------------------------------------------------ */
 
-int orc_forward(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
-                const int32_t *ids, const float *weights, int ntok, const int32_t *tokens,
-                double *out, float *dbg)
+int orc_forward_ex(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
+                   const int32_t *ids, const float *weights, int ntok, const int32_t *tokens,
+                   double *out, float *dbg, int acc32, int nthreads)
 {
-    if (check_weights(W) || T < 0 || k < 1) return -1;
-    int H = W->H, I = W->I;
+    if (check_weights(W) || T < 0 || k < 1 || nthreads < 1) return -1;
     int n_out = tokens ? ntok : T;
     for (int q = 0; q < n_out; q++)
         if (tokens && (tokens[q] < 0 || tokens[q] >= T)) return -1;
     for (int64_t i = 0; i < (int64_t)T * k; i++)
         if (ids[i] < 0 || ids[i] >= W->E) return -1;
-
-    double *x = malloc(sizeof(double) * H), *h = malloc(sizeof(double) * I);
-    double *y = malloc(sizeof(double) * H), *row = malloc(sizeof(double) * (H > I ? H : I));
+    int acc = acc32 ? ACC32 : ACC64;
     double *hall = NULL;
     if (W->wdtype == ORC_FP8_E4M3) {
         float sc[2];
-        hall = malloc(sizeof(double) * ((size_t)T * k * I + 1));
-        fp8_intermediate(W, T, k, hidden_bf16, ids, hall, NULL, NULL, sc);
+        hall = malloc(sizeof(double) * ((size_t)T * k * W->I + 1));
+        if (fp8_intermediate(W, acc, nthreads, T, k, hidden_bf16, ids, hall, NULL, NULL, sc)) { free(hall); return -1; }
         if (dbg) { dbg[0] = sc[0]; dbg[1] = sc[1]; }
     }
-    for (int q = 0; q < n_out; q++) {
-        int t = tokens ? tokens[q] : q;
-        double *o = out + (int64_t)q * H;
-        for (int n = 0; n < H; n++) o[n] = 0.0;
-        if (!hall)
-            for (int c = 0; c < H; c++) x[c] = orc_bf16_to_f32(hidden_bf16[(int64_t)t * H + c]);
-        for (int j = 0; j < k; j++) {
-            int e = ids[(int64_t)t * k + j];
-            const double *hj = h;
-            if (hall) hj = hall + ((int64_t)t * k + j) * I;
-            else expert_intermediate(W, e, x, h, row);
-            expert_output(W, e, hj, y, row);
-            double w = weights[(int64_t)t * k + j];
-            for (int n = 0; n < H; n++) o[n] += w * y[n];
-        }
-    }
-    free(x); free(h); free(y); free(row); free(hall);
-    return 0;
+    job p = {0};
+    p.W = W; p.acc = acc; p.T = T; p.k = k; p.hidden = hidden_bf16; p.ids = ids; p.weights = weights;
+    p.tokens = tokens; p.hall = hall; p.out = out;
+    int rc = run_split(output_range, &p, n_out, nthreads);
+    free(hall);
+    return rc;
+}
+
+int orc_forward(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
+                const int32_t *ids, const float *weights, int ntok, const int32_t *tokens,
+                double *out, float *dbg)
+{
+    return orc_forward_ex(W, T, k, hidden_bf16, ids, weights, ntok, tokens, out, dbg, 0, 1);
 }
 
 /* ---- grouped GEMM over pre-permuted contiguous segments ----

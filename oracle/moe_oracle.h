@@ -6,7 +6,9 @@
  * benchmark do.  It shares no code, header, table or helper with the GPU library.
  *
  * Everything is written for readability, not speed: one token at a time, one expert
- * at a time, fp64 accumulation on dequantised weights.  Where floating point decides
+ * at a time, fp64 accumulation on dequantised weights (an fp32-accumulation variant
+ * serves as a cross-check); tokens may be spread over threads, each computing whole
+ * tokens exactly as the single-threaded run does.  Where floating point decides
  * an integer (a top-k selection, an fp8 code) the decision is taken in fp32, the
  * precision the GPU kernels use for it.
  *
@@ -88,6 +90,14 @@ double orc_weight(const orc_weights *W, int m, int e, int64_t n, int64_t c);
 int orc_forward(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
                 const int32_t *ids, const float *weights, int ntok, const int32_t *tokens,
                 double *out, float *dbg);
+
+/* orc_forward with its two options: acc32 = 0 accumulates in fp64 (orc_forward), 1 in fp32
+ * (operands taken as fp32 values, each product and sum rounded to fp32, SiLU and the slot
+ * sum in fp32); the per-token work runs on nthreads >= 1 threads over contiguous ranges of
+ * tokens, with results identical bit for bit for every nthreads. */
+int orc_forward_ex(const orc_weights *W, int T, int k, const uint16_t *hidden_bf16,
+                   const int32_t *ids, const float *weights, int ntok, const int32_t *tokens,
+                   double *out, float *dbg, int acc32, int nthreads);
 
 /* fp8 intermediate of every (token, slot) pair, before and after its quantisation:
  * h[T*k, I] (fp32 value of the fp64 intermediate) and hq[T*k, I] (e4m3 codes). */

@@ -136,3 +136,20 @@ def expected_tail(npp, cap, H, I, tile, max_workgroups, split_tail, units=256, g
         if s >= 2:
             return (mblocks - tmb) * BM, s
     return mblocks * BM, 0
+
+
+def block_cover_tokens(sorted_ids, npp, BM, k, pairs, extra=()):
+    """Tokens whose pairs lie in every row block of an align layout: block by block, a
+    block with a real row that no chosen token covers adds the token of its last real row
+    (the ragged edge of an expert's rows) -- so each block, the split-tail blocks included,
+    holds at least one row the oracle computes.  Plus the tokens in `extra`."""
+    chosen = set(int(t) for t in extra)
+    sorted_ids = np.asarray(sorted_ids)
+    for b in range(int(npp) // BM):
+        rows = sorted_ids[b * BM:(b + 1) * BM]
+        real = rows[rows < pairs]                      # pairs = T*k is the filler value
+        if real.size == 0:
+            continue
+        if not any(int(p) // k in chosen for p in real):
+            chosen.add(int(real[-1]) // k)
+    return sorted(chosen)

@@ -307,3 +307,18 @@ def test_grouped_gemm_host_checks():
         abi.moe_grouped_gemm_workspace_bytes(d, 64, 0)        # a register-staged tile
     with pytest.raises(abi.MoEError):
         abi.moe_grouped_gemm_workspace_bytes(abi.GroupedGemmDesc(64, 1000, 3584, abi.DT_BF16, fake, None), 64)
+    # one group's weights beyond 32-bit row offsets: N * K * 2 bytes = 2^32 + 2^21 (bf16), and
+    # the same shape in fp8 (half the bytes) is fine
+    big = abi.GroupedGemmDesc(4, 65536, 32768 + 16, abi.DT_BF16, fake, None)
+    for call in (lambda: abi.moe_grouped_gemm_default_tile(big, 64),
+                 lambda: abi.moe_grouped_gemm_workspace_bytes(big, 64),
+                 lambda: abi.moe_grouped_gemm_workspace_bytes(big, 64, 9)):
+        with pytest.raises(abi.MoEError) as ei:
+            call()
+        assert ei.value.status == abi.MOE_ERR_UNSUPPORTED
+    L = abi.lib()
+    st = L.moe_grouped_gemm(ctypes.byref(big), 64, ctypes.c_void_p(fake), None, ctypes.c_void_p(fake),
+                            ctypes.c_void_p(fake), ctypes.c_void_p(fake), 1 << 30, 9, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+    ok = abi.GroupedGemmDesc(4, 65536, 32768 + 128, abi.DT_FP8_E4M3, fake, fake)
+    assert abi.moe_grouped_gemm_default_tile(ok, 64) >= 0

@@ -40,7 +40,7 @@ def distinct_ids(rng, T, k, E):
     return np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
 
 
-@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+@pytest.mark.parametrize("BM", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("T,k,E", [(1, 1, 8), (1, 8, 256), (3, 2, 8), (37, 2, 8), (100, 8, 64), (512, 8, 256),
                                    (4096, 8, 64), (8192, 1, 16), (4096, 2, 8), (2000, 6, 128), (4097, 1, 8),
                                    (1531, 7, 64)])

@@ -27,8 +27,8 @@ MUTANTS = {
                                     "for (int64_t i = pairs - 1; i >= 0; i--) {\n        int64_t r = next"),
     # FFN
     "gate_up_swapped": ("h[i] = silu(g) * u;", "h[i] = silu(u) * g;"),
-    "last_slot_dropped": ("for (int j = 0; j < k; j++) {\n            int e = ids",
-                          "for (int j = 0; j < k - 1; j++) {\n            int e = ids"),
+    "last_slot_dropped": ("for (int j = 0; j < k; j++) {\n            int e = jb->ids",
+                          "for (int j = 0; j < k - 1; j++) {\n            int e = jb->ids"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "int4_nibbles_swapped": ("(c % 2 == 0) ? (byte & 0xF) : (byte >> 4)", "(c % 2 == 0) ? (byte >> 4) : (byte & 0xF)"),
     "int4_zero_ignored": ("return ((double)q - z) * s;", "return (double)q * s;"),
@@ -63,7 +63,7 @@ def test_pins_catch_mutant(name, tmp_path):
     mut.write_text(src.replace(old, new))
     (tmp_path / "moe_oracle.h").write_text(open(os.path.join(ROOT, "oracle", "moe_oracle.h")).read())
     so = tmp_path / "liboracle_mut.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(mut), "-lm", "-o", str(so)])
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-pthread", "-fPIC", "-shared", str(mut), "-lm", "-o", str(so)])
     env = dict(os.environ, MOE_ORACLE_LIB=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
