@@ -66,9 +66,9 @@ typedef enum {
     MOE_DT_FP32 = 1,
     MOE_DT_FP8_E4M3 = 2,    /* w8a8: per-expert per-tensor weight scales, dynamic
                                per-tensor activation scales */
-    MOE_DT_INT4_G128 = 3    /* weights only: the hidden states stay bf16 at the boundary
-                               (the kernels multiply in fp16, exact for bf16 values in
-                               fp16's normal range) */
+    MOE_DT_INT4_G128 = 3    /* weights only: the hidden states and the intermediate stay
+                               bf16 (the kernels multiply on bf16 MFMA, so no activation is
+                               narrowed to a smaller range) */
 } moe_dtype;
 
 /*

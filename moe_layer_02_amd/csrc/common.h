@@ -9,7 +9,6 @@ namespace moe {
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -25,22 +24,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
-// bf16 x8 -> fp16 x8 (round to nearest even), reordered (0,4,1,5,2,6,3,7): the order in
-// which the int4 kernels dequantise 8 packed nibbles.
-__device__ __forceinline__ uint4 bf16x8_to_f16x8_perm(uint4 v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    _Float16 h[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        h[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
-        h[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
-    }
-    const _Float16 p[8] = {h[0], h[4], h[1], h[5], h[2], h[6], h[3], h[7]};
+// 8 bf16 values reordered (0,4,1,5,2,6,3,7): the order in which the int4 kernels unpack
+// the 8 nibbles of a 32-bit word (nibbles i and i + 4 land in the two halves of one packed
+// pair).  A pure permutation of 16-bit values.
+__device__ __forceinline__ uint4 bf16x8_perm(uint4 v) {
     uint4 r;
-    r.x = (uint32_t)__builtin_bit_cast(uint16_t, p[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[1]) << 16);
-    r.y = (uint32_t)__builtin_bit_cast(uint16_t, p[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[3]) << 16);
-    r.z = (uint32_t)__builtin_bit_cast(uint16_t, p[4]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[5]) << 16);
-    r.w = (uint32_t)__builtin_bit_cast(uint16_t, p[6]) | ((uint32_t)__builtin_bit_cast(uint16_t, p[7]) << 16);
+    r.x = (v.x & 0xFFFFu) | (v.z << 16);             // elements 0, 4
+    r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);         // 1, 5
+    r.z = (v.y & 0xFFFFu) | (v.w << 16);             // 2, 6
+    r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);         // 3, 7
     return r;
 }
 

@@ -15,9 +15,9 @@
 //         v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales; the per-tensor scales
 //         multiply the fp32 accumulator in the epilogue.
 //   int4 (GPTQ/AWQ group 128, vLLM PR #12185): packed nibbles stay packed in LDS; each lane
-//         turns 8 nibbles into fp16 in registers ((q | 0x6400) is 1024 + q in fp16, minus
-//         1024 + z is the exact integer q - z, times the group's fp16 scale) and multiplies
-//         on v_mfma_f32_16x16x32_f16; the bf16 activations go to fp16 on their way into LDS.
+//         turns 8 nibbles into bf16 weights in registers ((q - z) * s in fp32, exact, then
+//         rounded once to bf16) and multiplies them with the bf16 activations on
+//         v_mfma_f32_16x16x32_bf16.
 // Gate/up epilogue: SiLU(gate) * up in fp32, stored as bf16 (fp8: kept in fp32, so that
 // its E4M3 code is later decided in fp32, and the tile's largest |h| goes into a device
 // word with an integer atomicMax -- max is order-independent).  Down
@@ -52,20 +52,13 @@ struct Cfg {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// 8 nibbles (k = 0..7 of one row, byte b = k/2, low nibble first) -> fp16 (q - z) * s in
-// the order (0,4,1,5,2,6,3,7).  zs = {1024 + z, 1024 + z}, ss = {s, s}.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 zs, f16x2 ss) {
-    f16x8 out;
+// 8 nibbles (k = 0..7 of one row, byte b = k/2, low nibble first) -> bf16 (q - z) * s in
+// the natural order.  q - z is an integer of at most 4 bits and s an fp16 value, so the
+// fp32 product is exact and the bf16 weight is rounded once (to nearest even).
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float z, float s) {
+    bf16x8 out;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t bits = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;   // (1024+q_i, 1024+q_{i+4})
-        f16x2 v = __builtin_bit_cast(f16x2, bits);
-        v = (v - zs) * ss;
-        out[2 * i] = v[0];
-        out[2 * i + 1] = v[1];
-    }
+    for (int k = 0; k < 8; k++) out[k] = static_cast<__bf16>(((float)((w >> (4 * k)) & 0xFu) - z) * s);
     return out;
 }
 
@@ -118,7 +111,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                 } else {
                     arow = row0 + r;
                 }
-                // int4 A: 16 B of LDS (8 fp16) come from 16 B of bf16 global
                 a_src[it] = (const char *)a.A + (arow * a.lda + (int64_t)kbase) * g_ebytes + ch * 16;
             }
         }
@@ -195,9 +187,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                 const int c = tid + it * C::NT;
                 if (c < C::BM * C::A_CH) {
                     const int r = c / C::A_CH, ch = c % C::A_CH;
-                    uint4 v = ra[it];
-                    if constexpr (WT == WT_INT4) v = bf16x8_to_f16x8_perm(v);
-                    *(uint4 *)(st + r * C::A_LDS + ch * 16) = v;
+                    *(uint4 *)(st + r * C::A_LDS + ch * 16) = ra[it];
                 }
             }
             char *sb = st + C::BM * C::A_LDS;
@@ -276,24 +266,24 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                             acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 af[fm], bfr[fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
                 } else {   // int4
-                    f16x8 af[C::FM], bfr[C::FN];
+                    bf16x8 af[C::FM], bfr[C::FN];
                     const int kel = kk * 32 + 8 * (lane >> 4);
                     const int g = kk * 32 / 128;
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++)
-                        af[fm] = *(const f16x8 *)(sa + (wm * C::TM + fm * 16 + (lane & 15)) * C::A_LDS + kel * 2);
+                        af[fm] = *(const bf16x8 *)(sa + (wm * C::TM + fm * 16 + (lane & 15)) * C::A_LDS + kel * 2);
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const uint32_t w = *(const uint32_t *)(sb + (wn * C::TN + fn * 16 + (lane & 15)) * C::B_LDS + kel / 2);
-                        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)us[g][fn]);
-                        const _Float16 zv = __builtin_bit_cast(_Float16, (uint16_t)uz[g][fn]) + (_Float16)1024.0f;
-                        bfr[fn] = dequant8(w, f16x2{zv, zv}, f16x2{sv, sv});
+                        const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)us[g][fn]);
+                        const float zv = (float)__builtin_bit_cast(_Float16, (uint16_t)uz[g][fn]);
+                        bfr[fn] = dequant8(w, zv, sv);
                     }
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++)
-                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
                 }
             }
             if (kt + 1 < nk) store_stage(smem[(kt + 1) & 1]);

@@ -4,27 +4,28 @@
 // one launch for every expert, GPTQ/AWQ packing, dequantisation inside the GEMM), laid out
 // for gfx950.  Weights stay packed all the way into LDS: a stage holds one 128-byte slab of
 // every B row (256 K values, two quantisation groups), the rows' two fp16 scales and two
-// fp16 zero points, and the matching 256 K values of every A row in fp16 -- all moved by
+// fp16 zero points, and the matching 256 K values of every A row in bf16 -- all moved by
 // global_load_lds (16 bytes per lane for the slabs, 4 for the scales and zeros), ST stages
 // in flight, as in gemm_pipe.hip.
 //
 // Dequantisation is split between the VALU and the MFMA's fp32 accumulation.  OR-ing a
-// nibble into the low bits of fp16 1024.0 (0x6400) gives exactly 1024 + q; two nibbles are
-// taken per 32-bit operation (nibbles i and i + 4 of a word land in the two halves of a
-// packed fp16 pair), so a word of 8 consecutive K values costs 7 VALU operations and comes
-// out in the order (0,4,1,5,2,6,3,7).  The MFMAs of one quantisation group accumulate
-// D = sum a (1024 + q) and, against a fragment of ones, R = sum a; the group then adds
-// s D - s (1024 + z) R = s sum a (q - z) to the output in fp32 -- the exact dequantised
-// product up to fp32 rounding of terms 1024 times larger than the weights (relative error
-// of order 1e-4 for rows of activations with a large mean, far less for centred ones).
-// The activations are stored in the nibble order inside every group of 8 (the fp16
-// conversion pass permutes the hidden states; GEMM1 writes h permuted), so A and B agree
-// element for element and the dot products are unchanged.
+// nibble into the low bits of bf16 128.0 (0x4300) gives exactly 128 + q (bf16 holds every
+// integer of [128, 256)); two nibbles are taken per 32-bit operation (nibbles i and i + 4
+// of a word land in the two halves of a packed bf16 pair), so a word of 8 consecutive K
+// values costs 7 VALU operations and comes out in the order (0,4,1,5,2,6,3,7).  The MFMAs
+// of one quantisation group accumulate D = sum a (128 + q) and, against a fragment of
+// ones, R = sum a; the group then adds s D - s (128 + z) R = s sum a (q - z) to the output
+// in fp32 -- the exact dequantised product up to fp32 rounding of terms about 128 times
+// larger than the weights.  The activations stay bf16, so every bf16 hidden value is
+// taken as it is (no narrowing to a smaller exponent range); they are stored in the
+// nibble order inside every group of 8 (a permutation pass reorders the hidden states;
+// GEMM1 writes h permuted), so A and B agree element for element and the dot products are
+// unchanged.
 //
-// K assignment per MFMA (v_mfma_f32_16x16x32_f16, lane group g = lane / 16): in step
+// K assignment per MFMA (v_mfma_f32_16x16x32_bf16, lane group g = lane / 16): in step
 // (half, d), half = 0..1 the group of the slab and d = 0..3, lane group g takes the K
 // values 128 half + 32 g + 8 d .. +7 -- dword d of 16-byte chunk g + 4 half of its B row,
-// and 16-byte chunk 4 (g & 1) + d of fp16 A slab 2 half + g / 2.  Each B row is therefore
+// and 16-byte chunk 4 (g & 1) + d of bf16 A slab 2 half + g / 2.  Each B row is therefore
 // read with two 16-byte LDS reads per stage, and each A row with one per MFMA.
 #include "common.h"
 #include "kernels.h"
@@ -39,7 +40,7 @@ struct ICfg {
     static constexpr int NW = WM * WN, NT = NW * kWave;
     static constexpr int BK = 256;                             // K per stage: one packed slab
     static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
-    static constexpr int A_SLABS = 4;                          // 4 x 64 fp16 per A row
+    static constexpr int A_SLABS = 4;                          // 4 x 64 bf16 per A row
     static constexpr int A_STAGE = A_SLABS * BM * 128, B_STAGE = BN * 128, SZ = BN * 4;
     static constexpr int STAGE = A_STAGE + B_STAGE + 2 * SZ;
     static constexpr int A_LOADS = A_SLABS * BM / 8, B_LOADS = BN / 8;
@@ -62,15 +63,15 @@ struct ICfg {
     static constexpr bool SKIP_FILLER = BM <= 32;   // as in gemm_pipe.hip
 };
 
-// 8 nibbles (K values 0..7 of one row, low nibble first in each byte) -> fp16 1024 + q in
+// 8 nibbles (K values 0..7 of one row, low nibble first in each byte) -> bf16 128 + q in
 // the order (0,4,1,5,2,6,3,7)
-__device__ __forceinline__ f16x8 raw8(uint32_t w) {
+__device__ __forceinline__ bf16x8 raw8(uint32_t w) {
     uint4 r;
-    r.x = (w & 0x000F000Fu) | 0x64006400u;
-    r.y = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
-    r.z = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
-    r.w = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
-    return __builtin_bit_cast(f16x8, r);
+    r.x = (w & 0x000F000Fu) | 0x43004300u;
+    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ _Float16 half_of(uint32_t w, int hi) {
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
         // weight streaming: each tile starts its K walk at its own step (see gemm_pipe.hip)
         const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
         // operand bases at the split's first K (wave-uniform); a K step advances A by 512
-        // bytes (256 fp16), B by 128 (256 nibbles), scales and zeros by 4 (two groups)
+        // bytes (256 bf16), B by 128 (256 nibbles), scales and zeros by 4 (two groups)
         const char *base_a = uniform_ptr((const char *)a.A + (int64_t)s * a.ksplit * 2);
         const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + (int64_t)s * a.ksplit / 2);
         const int64_t sz0 = (int64_t)e * a.sz_expert_stride + (int64_t)s * a.ksplit / 128 * sz_rows;
@@ -220,13 +221,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                 sw[fn] = (uint32_t)s16[t] | ((uint32_t)s16[C::BN + t] << 16);
                 zw[fn] = (uint32_t)z16[t] | ((uint32_t)z16[C::BN + t] << 16);
             }
-            const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+            const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 #pragma unroll
             for (int half = 0; half < 2; half++) {
                 f32x4 dg[C::FM][C::FN], rs[C::FM];
 #pragma unroll
                 for (int d = 0; d < 4; d++) {
-                    f16x8 bq[C::FN];
+                    bf16x8 bq[C::FN];
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const uint4 v = braw[half][fn];
@@ -237,18 +238,18 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++) {
                         const int r = wm * C::TM + fm * 16 + (lane & 15);
-                        const f16x8 af = *(const f16x8 *)(sa + (slab * C::BM + r) * 128 + ((chunk ^ swz(r)) << 4));
-                        rs[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, ones, d ? rs[fm] : zero, 0, 0, 0);
+                        const bf16x8 af = *(const bf16x8 *)(sa + (slab * C::BM + r) * 128 + ((chunk ^ swz(r)) << 4));
+                        rs[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, d ? rs[fm] : zero, 0, 0, 0);
 #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++)
-                            dg[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bq[fn], d ? dg[fm][fn] : zero, 0, 0, 0);
+                            dg[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[fn], d ? dg[fm][fn] : zero, 0, 0, 0);
                     }
                 }
-                // the group's scale and zero point: acc += s D - s (1024 + z) R
+                // the group's scale and zero point: acc += s D - s (128 + z) R
 #pragma unroll
                 for (int fn = 0; fn < C::FN; fn++) {
                     const float sv = (float)half_of(sw[fn], half);
-                    const float zv = sv * (1024.0f + (float)half_of(zw[fn], half));
+                    const float zv = sv * (128.0f + (float)half_of(zw[fn], half));
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                     }
                 }
         } else if constexpr (KIND == GEMM_GATE_UP) {
-            // h = SiLU(gate) * up in fp16, columns in the permuted order GEMM2's A expects
+            // h = SiLU(gate) * up in bf16, columns in the permuted order GEMM2's A expects
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                     for (int f = 0; f < C::FN / 2; f++) {
                         const float hv = silu(acc[fm][f][i]) * acc[fm][f + C::FN / 2][i];
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + lcol;
-                        ((_Float16 *)a.C)[(int64_t)row * a.ldc + perm_col(col)] = (_Float16)hv;
+                        ((uint16_t *)a.C)[(int64_t)row * a.ldc + perm_col(col)] = f32_to_bf16_bits(hv);
                     }
                 }
         } else {

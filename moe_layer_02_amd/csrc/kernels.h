@@ -85,7 +85,7 @@ bool pipe_tile_info(int wdtype, int tile, TileInfo *info);
 hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
                             int64_t max_tiles, hipStream_t s);
 // int4 tiles of the pipelined kind (gemm_i4.hip): A is fp16 in the (0,4,1,5,2,6,3,7) order
-// inside every 8 columns (launch_f16_perm), and GEMM1 writes h as fp16 in the same order
+// inside every 8 columns (launch_bf16_perm), and GEMM1 writes h as bf16 in the same order
 bool i4_tile_info(int tile, TileInfo *info);
 hipError_t launch_gemm_i4(int tile, GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles,
                           hipStream_t s);
@@ -107,7 +107,7 @@ struct ReduceArgs {
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
 // GEMM1 split-K finish: h from the split planes of gate/up sums (fp32 [split, cap, 2I]).
-enum { GATE_UP_H_BF16 = 0, GATE_UP_H_F32 = 1, GATE_UP_H_F16_PERM = 2 };
+enum { GATE_UP_H_BF16 = 0, GATE_UP_H_F32 = 1, GATE_UP_H_BF16_PERM = 2 };
 struct GateUpFinishArgs {
     const float *P;
     int64_t plane;               // elements between split planes
@@ -149,8 +149,8 @@ struct QuantArgs {
 };
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 
-// bf16 [n8 * 8] -> fp16 with each group of 8 reordered (0,4,1,5,2,6,3,7) (int4 GEMM1's A)
-hipError_t launch_f16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream_t s);
+// bf16 [n8 * 8] with each group of 8 reordered (0,4,1,5,2,6,3,7) (int4 GEMM1's A)
+hipError_t launch_bf16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream_t s);
 
 // Route + align (+ the activation pass) of a batch of at most kPrologueMaxT tokens in one
 // launch (prologue.hip); results identical to launch_route, launch_align and the fp8 /
@@ -161,7 +161,7 @@ hipError_t launch_f16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream
 constexpr int kPrologueMaxT = 64, kPrologueMaxTLongRoute = 16;
 constexpr int kPrologueActRegs = 16;                                // 16-byte groups per thread
 constexpr int64_t kPrologueFp8Elems = (int64_t)kPrologueActRegs * 1024 * 8;
-enum { PROLOGUE_ACT_NONE = 0, PROLOGUE_ACT_FP8 = 1, PROLOGUE_ACT_F16_PERM = 2 };
+enum { PROLOGUE_ACT_NONE = 0, PROLOGUE_ACT_FP8 = 1, PROLOGUE_ACT_BF16_PERM = 2 };
 struct PrologueArgs {
     RouteArgs route;             // zero_ptr unused
     AlignArgs align;             // ids = route.ids
@@ -169,7 +169,7 @@ struct PrologueArgs {
     const uint16_t *x;           // bf16 hidden [n]
     int64_t n;                   // T * H
     uint8_t *xq;                 // fp8: codes [n]
-    uint16_t *x16;               // int4: fp16 [n] in the packed-nibble order
+    uint16_t *xperm;             // int4: bf16 [n] in the packed-nibble order
     uint32_t *x_amax;            // fp8: |x| max as float bits
     float *x_scale;              // fp8: amax / 448 (1 when amax is 0)
     uint32_t *h_amax;            // cleared to 0 (GEMM1's |h| maximum), may be null

@@ -105,8 +105,8 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
     if (p->split_k1 < 0 || s1 > 16) return MOE_ERR_INVALID_ARGUMENT;
     // GEMM1 split K: the small-T tiles only, each split a whole number of K steps
     if (s1 > 1 && (t1->BM > 32 || L->H % (t1->BK * s1))) return MOE_ERR_INVALID_ARGUMENT;
-    // int4: the pipelined tiles pass h between the GEMMs as permuted fp16, the
-    // register-staged ones as bf16, so both GEMMs must be of one kind
+    // int4: the pipelined tiles pass h between the GEMMs as bf16 in the nibble order, the
+    // register-staged ones in the natural order, so both GEMMs must be of one kind
     if (wd == MOE_DT_INT4_G128 && (t1->stages > 0) != (t2->stages > 0)) return MOE_ERR_INVALID_ARGUMENT;
     // GEMM1: K = H, output columns I (each tile covers BN/2 gate and BN/2 up rows, and each
     // wave an equal number of gate and up fragments)
@@ -151,8 +151,9 @@ struct Workspace {
 // scal words: [0] amax(x) bits, [1] amax(h) bits, [2] s1, [3] s2
 constexpr int kScalarWords = 4;
 
-// int4 with the pipelined tiles: GEMM1 reads the hidden states as permuted fp16
-bool f16_activations(const moe_layer *L, const moe_plan *p) {
+// int4 with the pipelined tiles: GEMM1 reads the hidden states as bf16 permuted into the
+// order the kernel unpacks nibbles
+bool perm_activations(const moe_layer *L, const moe_plan *p) {
     TileInfo t;
     return L->weight_dtype == MOE_DT_INT4_G128 && gemm_tile_info(L->weight_dtype, p->gemm1_tile, &t) && t.stages > 0;
 }
@@ -181,7 +182,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.inv_pos = take(pairs * 4);
     w.scal = take(kScalarWords * 4);
     const bool fp8 = L->weight_dtype == MOE_DT_FP8_E4M3;
-    w.xq = take(fp8 ? (size_t)T * L->H : f16_activations(L, p) ? (size_t)T * L->H * 2 : 0);
+    w.xq = take(fp8 ? (size_t)T * L->H : perm_activations(L, p) ? (size_t)T * L->H * 2 : 0);
     w.h = take((size_t)w.cap * L->I * (fp8 ? 4 : 2));
     w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
     w.y = take(direct_output(L, p) ? 0
@@ -272,11 +273,11 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         PrologueArgs pa{};
         pa.route = ra;
         pa.align = aa;
-        pa.act = fp8 ? PROLOGUE_ACT_FP8 : f16_activations(L, &plan) ? PROLOGUE_ACT_F16_PERM : PROLOGUE_ACT_NONE;
+        pa.act = fp8 ? PROLOGUE_ACT_FP8 : perm_activations(L, &plan) ? PROLOGUE_ACT_BF16_PERM : PROLOGUE_ACT_NONE;
         pa.x = (const uint16_t *)hidden;
         pa.n = (int64_t)T * H;
         pa.xq = (uint8_t *)(ws + w.xq);
-        pa.x16 = (uint16_t *)(ws + w.xq);
+        pa.xperm = (uint16_t *)(ws + w.xq);
         pa.x_amax = &scal[0];
         pa.x_scale = (float *)&scal[2];
         pa.h_amax = &scal[1];
@@ -302,10 +303,10 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
             QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs};
             if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
             a1 = ws + w.xq;
-        } else if (f16_activations(L, &plan)) {
-            // int4: the hidden states as fp16 in the order the kernel dequantises nibbles
+        } else if (perm_activations(L, &plan)) {
+            // int4: the hidden states in the order the kernel unpacks nibbles
             if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-            if ((err = launch_f16_perm((const uint16_t *)hidden, (uint16_t *)(ws + w.xq), (int64_t)T * H / 8, stream)) !=
+            if ((err = launch_bf16_perm((const uint16_t *)hidden, (uint16_t *)(ws + w.xq), (int64_t)T * H / 8, stream)) !=
                 hipSuccess)
                 return fail(err);
             a1 = ws + w.xq;
@@ -374,7 +375,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     if (s1 > 1) {
         if ((err = mark(MOE_STAGE_GEMM1_FINISH)) != hipSuccess) return MOE_ERR_HIP;
         GateUpFinishArgs f{(const float *)(ws + w.g1p), w.cap * 2 * (int64_t)I, s1, I, sorted, npp, pairs, ws + w.h,
-                           fp8 ? GATE_UP_H_F32 : f16_activations(L, &plan) ? GATE_UP_H_F16_PERM : GATE_UP_H_BF16,
+                           fp8 ? GATE_UP_H_F32 : perm_activations(L, &plan) ? GATE_UP_H_BF16_PERM : GATE_UP_H_BF16,
                            fp8 ? &scal[1] : nullptr};
         err = finish_quant ? launch_gate_up_finish_quant(f, inv_pos, (uint8_t *)(ws + w.hq), (float *)&scal[3], stream)
                            : launch_gate_up_finish(f, w.cap, stream);

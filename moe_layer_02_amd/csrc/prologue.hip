@@ -30,10 +30,10 @@ __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
     }
     const int64_t n8 = p.n / 8;
     const int tid = threadIdx.x;
-    if (p.act == PROLOGUE_ACT_F16_PERM) {   // workgroups 1 .. G-1 share the conversion
+    if (p.act == PROLOGUE_ACT_BF16_PERM) {   // workgroups 1 .. G-1 share the permutation
         const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
         for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + tid; i < n8; i += stride)
-            ((uint4 *)p.x16)[i] = bf16x8_to_f16x8_perm(((const uint4 *)p.x)[i]);
+            ((uint4 *)p.xperm)[i] = bf16x8_perm(((const uint4 *)p.x)[i]);
         return;
     }
     // fp8: the batch is read once into registers (every load in flight at once), its
@@ -108,7 +108,7 @@ hipError_t launch_prologue(const PrologueArgs &p, hipStream_t s) {
     // fp8: one workgroup for the pass; fp16 conversion: one per 4096 16-byte groups, up to 32
     int g = 1;
     if (p.act == PROLOGUE_ACT_FP8) g = 2;
-    if (p.act == PROLOGUE_ACT_F16_PERM) g = 1 + (int)std::min<int64_t>(32, std::max<int64_t>(1, (p.n / 8 + 4095) / 4096));
+    if (p.act == PROLOGUE_ACT_BF16_PERM) g = 1 + (int)std::min<int64_t>(32, std::max<int64_t>(1, (p.n / 8 + 4095) / 4096));
     const dim3 grid(g), block(1024);
     if (p.route.E <= 64)
         launch_epl<1>(p, grid, block, s);

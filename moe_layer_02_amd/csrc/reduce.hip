@@ -141,14 +141,10 @@ __global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
             *(float4 *)(o + 4) = make_float4(h[4], h[5], h[6], h[7]);
 #pragma unroll
             for (int j = 0; j < 8; j++) m = fmaxf(m, fabsf(h[j]));
-        } else if (a.h_kind == GATE_UP_H_F16_PERM) {   // fp16, order (0,4,1,5,2,6,3,7) in the 8
-            const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-            uint32_t w[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-                w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h[perm[2 * q]]) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h[perm[2 * q + 1]]) << 16);
-            *(uint4 *)((uint16_t *)a.h + r * a.I + c) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else if (a.h_kind == GATE_UP_H_BF16_PERM) {   // bf16, order (0,4,1,5,2,6,3,7) in the 8
+            *(uint4 *)((uint16_t *)a.h + r * a.I + c) =
+                make_uint4(pack_bf16x2(h[0], h[4]), pack_bf16x2(h[1], h[5]), pack_bf16x2(h[2], h[6]),
+                           pack_bf16x2(h[3], h[7]));
         } else {
             *(uint4 *)((uint16_t *)a.h + r * a.I + c) =
                 make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),

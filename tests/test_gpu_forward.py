@@ -399,6 +399,36 @@ def test_int4_every_plan(T):
     check_intermediates(c, T, plans[-1], ws)
 
 
+@pytest.mark.parametrize("scale", [3e4, 1e5, 1e6])
+def test_int4_outlier_channels(scale):
+    """Hidden states with outlier channels far past fp16's range (65504), as real DeepSeek
+    activations carry: the int4 kernels keep activations and the intermediate in bf16 (bf16
+    MFMA), so every plan of both tile kinds stays finite and within tolerance of the oracle
+    on the same bf16 inputs."""
+    if "i4small" not in _cases:
+        _cases["i4small"] = Case("i4small", "cpu", I4_SMALL)
+    c = _cases["i4small"]
+    T = 37
+    x, lg = c.inputs(T)
+    xf = x.float()
+    xf[:, [5, 300, 701]] = torch.tensor([scale, -scale, 0.5 * scale])
+    xf[3, 100] = -2.0 * scale
+    x = xf.to(torch.bfloat16)
+    ids, w = oracle_route(c.cfg, bits(lg), c.bias)
+    ref = oracle.forward(c.W, bits(x), ids, w)
+    assert np.isfinite(ref).all()
+    plans = valid_plans(c.layer, T)
+    kinds = {p.gemm1_tile >= 4 for p in plans}
+    assert kinds == {False, True}                       # register-staged and pipelined tiles
+    for p in plans[::3] + [plans[-1]]:
+        say("int4 outliers %.0e plan %s" % (scale, p.as_tuple()))
+        out = c.layer.forward(x.cuda(), lg.cuda(), plan=p)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all(), p.as_tuple()
+        err = rel_l2(bf16_to_f64(out), ref)
+        assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+
+
 # ---- properties ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,T", [("mixtral", 1), ("qwen2", 3), ("deepseek", 2), ("scout", 5)])
