@@ -235,6 +235,26 @@ moe_status moe_forward(const moe_layer *layer, int32_t T, const void *hidden, co
                        void *stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory (code under hipGraph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same steps and results as
+ * moe_forward with the same plan, but the workspace is a static device array of
+ * MOE_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on until the
+ * process ends (its address is looked up once per device, on the first call with that
+ * device current).  Nothing is allocated or freed.
+ *  - MOE_ERR_WORKSPACE_TOO_SMALL, before anything is enqueued or any HIP call, when
+ *    moe_workspace_bytes(layer, T, plan) exceeds MOE_STATIC_WORKSPACE_BYTES (128 MiB holds
+ *    the small and mid batches under the default plans: Mixtral TP2 up to T = 512, Qwen2
+ *    fp8, DeepSeek int4 and Llama-4-Scout up to T = 256).
+ *  - Every call on one GPU uses that GPU's one array and leaves its contents there: calls
+ *    that overlap on one GPU (two streams, or two host threads without ordering between
+ *    their streams) race and give undefined results; the caller orders them.
+ * Arguments as moe_forward, without workspace and workspace_bytes.
+ */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+moe_status moe_forward_static(const moe_layer *layer, int32_t T, const void *hidden, const void *logits,
+                              void *out, const moe_plan *plan, void *stream);
+
+/*
  * moe_forward, with a hipEvent_t recorded on `stream` before each step it launches and one
  * after the last.  events [host] holds n_events >= MOE_STAGE_COUNT + 1 hipEvent_t handles;
  * stages [host] int32 [MOE_STAGE_COUNT] receives the moe_stage of each launched step, and

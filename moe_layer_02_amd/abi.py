@@ -28,7 +28,8 @@ WS_REGIONS = ("topk_ids", "topk_weights", "sorted_ids", "expert_ids", "num_post_
 EXPORTS = ("moe_status_str", "moe_align_capacity", "moe_route", "moe_align", "moe_default_plan",
            "moe_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_plan_describe",
            "moe_workspace_offsets", "moe_grouped_gemm_default_tile", "moe_grouped_gemm_workspace_bytes",
-           "moe_grouped_gemm")
+           "moe_grouped_gemm", "moe_forward_static")
+STATIC_WORKSPACE_BYTES = 128 << 20   # MOE_STATIC_WORKSPACE_BYTES
 
 
 class MoEError(RuntimeError):
@@ -93,6 +94,7 @@ def lib():
         L.moe_default_plan.argtypes = [ctypes.POINTER(Layer), I32, ctypes.POINTER(Plan)]
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(Layer), I32, ctypes.POINTER(Plan), ctypes.POINTER(SZ)]
         L.moe_forward.argtypes = [ctypes.POINTER(Layer), I32, P, P, P, P, SZ, ctypes.POINTER(Plan), P]
+        L.moe_forward_static.argtypes = [ctypes.POINTER(Layer), I32, P, P, P, ctypes.POINTER(Plan), P]
         L.moe_forward_profiled.argtypes = [ctypes.POINTER(Layer), I32, P, P, P, P, SZ, ctypes.POINTER(Plan), P,
                                            ctypes.POINTER(P), I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.moe_plan_describe.argtypes = [ctypes.POINTER(Layer), I32, ctypes.POINTER(Plan), ctypes.c_char_p, SZ]
@@ -103,7 +105,8 @@ def lib():
         L.moe_grouped_gemm.argtypes = [G, I32, P, P, P, P, P, SZ, I32, P]
         for f in ("moe_route", "moe_align", "moe_default_plan", "moe_workspace_bytes", "moe_forward",
                   "moe_forward_profiled", "moe_plan_describe", "moe_workspace_offsets",
-                  "moe_grouped_gemm_default_tile", "moe_grouped_gemm_workspace_bytes", "moe_grouped_gemm"):
+                  "moe_grouped_gemm_default_tile", "moe_grouped_gemm_workspace_bytes", "moe_grouped_gemm",
+                  "moe_forward_static"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -173,6 +176,12 @@ def moe_forward(layer: Layer, T, hidden, logits, out, workspace, plan: Plan = No
     _check(lib().moe_forward(ctypes.byref(layer), T, _ptr(hidden), _ptr(logits), _ptr(out), _ptr(workspace),
                              workspace.numel() * workspace.element_size(),
                              ctypes.byref(plan) if plan else None, _stream(stream)), "moe_forward")
+
+
+def moe_forward_static(layer: Layer, T, hidden, logits, out, plan: Plan = None, stream=None):
+    """moe_forward on the library's own static device workspace (no allocation anywhere)."""
+    _check(lib().moe_forward_static(ctypes.byref(layer), T, _ptr(hidden), _ptr(logits), _ptr(out),
+                                    ctypes.byref(plan) if plan else None, _stream(stream)), "moe_forward_static")
 
 
 def moe_forward_profiled(layer: Layer, T, hidden, logits, out, workspace, events, plan: Plan = None, stream=None):

@@ -516,6 +516,28 @@ GroupedWorkspace grouped_layout(const moe_grouped_gemm_desc *d, int32_t M, int B
     return w;
 }
 
+// ---- the workspace of moe_forward_static --------------------------------------------------
+
+// Device memory the library holds for callers that cannot allocate: one array per GPU (each
+// device that loads the library gets its own copy at its own address).  In host code this
+// name is only a stand-in for the symbol: kernels are given the device address that
+// hipGetSymbolAddress returns for the current device, never the name itself.
+static __device__ __align__(256) char scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+// The device address of `scratch` on the current device, looked up on the first call per
+// device (with that device current) and kept; null if the lookup fails.
+void *static_workspace() {
+    static std::atomic<void *> addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev].store(p, std::memory_order_release);   // the same value from every thread
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -643,6 +665,20 @@ moe_status moe_workspace_bytes(const moe_layer *layer, int32_t T, const moe_plan
 moe_status moe_forward(const moe_layer *layer, int32_t T, const void *hidden, const void *logits, void *out,
                        void *workspace, size_t workspace_bytes, const moe_plan *plan, void *stream) {
     return forward_impl(layer, T, hidden, logits, out, workspace, workspace_bytes, plan, (hipStream_t)stream,
+                        nullptr, 0, nullptr, nullptr);
+}
+
+moe_status moe_forward_static(const moe_layer *layer, int32_t T, const void *hidden, const void *logits, void *out,
+                              const moe_plan *plan, void *stream) {
+    // every size check first, without touching the device
+    size_t need = 0;
+    moe_status st = moe_workspace_bytes(layer, T, plan, &need);
+    if (st != MOE_OK) return st;
+    if (need > MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (T == 0) return MOE_OK;
+    void *ws = static_workspace();
+    if (!ws) return MOE_ERR_HIP;
+    return forward_impl(layer, T, hidden, logits, out, ws, MOE_STATIC_WORKSPACE_BYTES, plan, (hipStream_t)stream,
                         nullptr, 0, nullptr, nullptr);
 }
 

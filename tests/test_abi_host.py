@@ -322,3 +322,22 @@ def test_grouped_gemm_host_checks():
     assert st == abi.MOE_ERR_UNSUPPORTED
     ok = abi.GroupedGemmDesc(4, 65536, 32768 + 128, abi.DT_FP8_E4M3, fake, fake)
     assert abi.moe_grouped_gemm_default_tile(ok, 64) >= 0
+
+
+def test_static_forward_size_checks_come_first():
+    """moe_forward_static rejects a batch whose workspace exceeds its static array, and any
+    invalid argument, before any HIP call (so on a machine without a GPU as well); T = 0 is
+    a no-op."""
+    fake = ctypes.c_void_p(0x10000)
+    L = abi.lib()
+    mix = fake_layer(synth.CONFIGS["mixtral"])
+    assert abi.moe_workspace_bytes(mix, 4096) > abi.STATIC_WORKSPACE_BYTES
+    assert L.moe_forward_static(ctypes.byref(mix), 4096, fake, fake, fake, None, None) == \
+        abi.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_forward_static(ctypes.byref(mix), 0, fake, fake, fake, None, None) == abi.MOE_OK
+    assert L.moe_forward_static(ctypes.byref(mix), -1, fake, fake, fake, None, None) == abi.MOE_ERR_INVALID_ARGUMENT
+    bad = fake_layer(synth.CONFIGS["mixtral"], w13=0x10001)                      # misaligned weights
+    assert L.moe_forward_static(ctypes.byref(bad), 8, fake, fake, fake, None, None) == abi.MOE_ERR_INVALID_ARGUMENT
+    # the sizes the array is stated to hold under the default plans
+    for name, T in (("mixtral", 512), ("qwen2", 256), ("deepseek", 256), ("scout", 256)):
+        assert abi.moe_workspace_bytes(fake_layer(synth.CONFIGS[name]), T) <= abi.STATIC_WORKSPACE_BYTES, name

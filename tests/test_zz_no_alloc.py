@@ -1,0 +1,60 @@
+"""moe_forward_static (the entry point that allocates nothing: its workspace is the
+library's static device array) against moe_forward with a caller-allocated workspace.
+
+Same kernels, same plan, so the outputs are bit-identical; two calls in a row on the
+shared array, the second with a smaller batch (the array keeps the first call's contents,
+which the forward must not depend on); a batch whose workspace exceeds the array is
+rejected before anything runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_layer_02_amd import abi, synth
+from tests.gpu_util import device_layer, needs_gpu, say
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _layer(cfg):
+    w = synth.expert_weights(cfg, device="cuda")
+    return device_layer(cfg, w, synth.correction_bias(cfg))
+
+
+@pytest.mark.parametrize("name,Ts", [("mixtral", (512, 8)), ("qwen2", (256, 5)), ("deepseek", (200, 3)),
+                                     ("scout", (256, 1))])
+def test_static_matches_allocating_forward(name, Ts):
+    cfg = synth.CONFIGS[name]
+    layer = _layer(cfg)
+    for T in Ts:                                          # the second call is smaller
+        x, lg = synth.hidden_states(cfg, T).cuda(), synth.router_logits(cfg, T).cuda()
+        plan = layer.plan(T)
+        assert abi.moe_workspace_bytes(layer.struct, T, plan) <= abi.STATIC_WORKSPACE_BYTES
+        say("static forward", name, "T=%d" % T, plan.as_tuple())
+        ref = layer.forward(x, lg, plan=plan)
+        out = torch.full_like(ref, float("nan"))
+        abi.moe_forward_static(layer.struct, T, x, lg, out, plan)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (name, T)
+
+
+def test_static_rejects_a_batch_past_its_array():
+    cfg = synth.CONFIGS["mixtral"]
+    layer = _layer(cfg)
+    T = 4096
+    assert abi.moe_workspace_bytes(layer.struct, T) > abi.STATIC_WORKSPACE_BYTES
+    x, lg = synth.hidden_states(cfg, T).cuda(), synth.router_logits(cfg, T).cuda()
+    out = torch.zeros((T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(abi.MoEError) as ei:
+        abi.moe_forward_static(layer.struct, T, x, lg, out)
+    assert ei.value.status == abi.MOE_ERR_WORKSPACE_TOO_SMALL
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()                      # nothing ran
+    # the next call that fits still runs, on the same array
+    T = 16
+    x, lg = synth.hidden_states(cfg, T).cuda(), synth.router_logits(cfg, T).cuda()
+    ref = layer.forward(x, lg)
+    got = torch.empty_like(ref)
+    abi.moe_forward_static(layer.struct, T, x, lg, got)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
