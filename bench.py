@@ -9,8 +9,9 @@ from a captured hipGraph.  Prints one JSON line.  The headline (value, ms_per_st
 is the largest single-GPU layer, Llama-4-Scout at T=8192 (bf16, 4.2 GB of weights, 2.06
 TFLOP per step); its line also carries a short T sweep of every layer (Mixtral TP2,
 Qwen2-57B TP4 fp8, DeepSeek-V3 int4, Scout).  Each point reports whole-layer tokens/s (K
-replays back to back), the same step with cold caches (a 512 MiB buffer read before each
-replay, outside the timed region; median, p10, p90), TFLOP/s and HBM GB/s with their
+replays back to back, after W warm-up replays, themselves after the cold replays below), the
+same step with cold caches (a 512 MiB buffer read before each replay, outside the timed
+region; median, p10, p90), TFLOP/s and HBM GB/s with their
 fractions of the MI355X peaks, and the step's kernels' durations.  The headline adds the
 dominant kernel's roofline (its duration from HIP events recorded on the launch stream
 around each step of the forward) and the CPU oracle's throughput on a bounded sample of the
@@ -122,7 +123,11 @@ class Bench:
         counts = ws[off:off + 4 * self.cfg.E].view(torch.int32).cpu().numpy()
         return int((counts > 0).sum())
 
-    def time_graph(self, T, steps, warmup):
+    def time_graph(self, T, steps, warmup, stage_steps):
+        """The step captured in a graph.  The cold-cache replays first (untimed for the
+        headline), then W warm-up replays and the K timed replays back to back, so the timed
+        replays do not start on a clock that is still ramping up from idle; then the
+        per-kernel event timing (eager forwards) on the same warm clock."""
         x, lg, plan, ws, out = self.prepare(T)
         self.layer.forward(x, lg, out=out, workspace=ws, plan=plan)        # eager once (first-use setup)
         torch.cuda.synchronize()
@@ -133,16 +138,7 @@ class Bench:
             with torch.cuda.graph(g, stream=s):
                 self.layer.forward(x, lg, out=out, workspace=ws, plan=plan)
         torch.cuda.current_stream().wait_stream(s)
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(steps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / steps
         # cold caches: before each timed replay, read a buffer larger than the 256 MB
         # last-level cache and the L2s together, outside the timed region (a read leaves
         # clean lines; a write would leave dirty ones whose write-back lands in the replay)
@@ -154,8 +150,18 @@ class Bench:
             t1.record()
             torch.cuda.synchronize()
             cold.append(t0.elapsed_time(t1))
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        stages = self.time_stages(T, plan, (x, lg, ws, out), stage_steps)
         active = self.active_experts(T, plan, ws)
-        return ms, np.array(cold), active, plan, (x, lg, ws, out)
+        return ms, np.array(cold), active, plan, stages
 
     def time_stages(self, T, plan, bufs, steps):
         """Average duration of each step of the forward, from HIP events recorded on the
@@ -180,8 +186,7 @@ class Bench:
 
 def measure(b: Bench, T, steps, warmup, stage_steps):
     cfg = b.cfg
-    ms, cold, active, plan, bufs = b.time_graph(T, steps, warmup)
-    stages = b.time_stages(T, plan, bufs, stage_steps)
+    ms, cold, active, plan, stages = b.time_graph(T, steps, warmup, stage_steps)
     sec = ms / 1e3
     flops, mbytes = layer_flops(cfg, T), layer_min_bytes(cfg, T, active)
     t_hbm, t_mfma = mbytes / PEAK_HBM, flops / PEAK_MFMA[cfg.wdtype]

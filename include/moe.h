@@ -148,6 +148,14 @@ typedef struct {
  * tile): the same for GEMM1 -- the split row blocks' gate and up sums go to fp32 planes and
  * a finishing pass (stage MOE_STAGE_GEMM1_FINISH) adds them in a fixed order and applies
  * SiLU * up to those rows before GEMM2.
+ * ragged (0 or 1): 0 pads each expert's rows to whole blocks of block_m (moe_align's
+ * layout: filler entries in sorted_token_ids, and the intermediates h and y hold a row for
+ * every entry).  1 lays the pairs out with no padding -- the permutation of TensorRT-LLM's
+ * expand_and_permute and of the FBGEMM article's MetaShuffling, which the pages name for
+ * avoiding padding: sorted_token_ids holds exactly the T*k pairs, expert by expert, and h
+ * and y hold T*k rows in that order; the GEMM tiles are cut at expert boundaries (block b
+ * covers rows [block_start[b], block_start[b + 1]) of one expert, at most block_m of them),
+ * so a tile's rows past its expert's end are computed but never read or stored.
  * moe_default_plan picks a plan per T; any valid plan gives results equal within rounding
  * (and bitwise reproducible for a fixed plan on a fixed device).
  */
@@ -160,6 +168,7 @@ typedef struct {
     int32_t split_tail;
     int32_t max_workgroups;
     int32_t split_tail1;
+    int32_t ragged;
 } moe_plan;
 
 /* Steps of moe_forward, for moe_forward_profiled. */
@@ -243,8 +252,8 @@ moe_status moe_forward(const moe_layer *layer, int32_t T, const void *hidden, co
  * device current).  Nothing is allocated or freed.
  *  - MOE_ERR_WORKSPACE_TOO_SMALL, before anything is enqueued or any HIP call, when
  *    moe_workspace_bytes(layer, T, plan) exceeds MOE_STATIC_WORKSPACE_BYTES (128 MiB holds
- *    the small and mid batches under the default plans: Mixtral TP2 up to T = 512, Qwen2
- *    fp8, DeepSeek int4 and Llama-4-Scout up to T = 256).
+ *    the small and mid batches under the default plans: Mixtral TP2, Qwen2 fp8, DeepSeek
+ *    int4 and Llama-4-Scout up to T = 256).
  *  - Every call on one GPU uses that GPU's one array and leaves its contents there: calls
  *    that overlap on one GPU (two streams, or two host threads without ordering between
  *    their streams) race and give undefined results; the caller orders them.
@@ -276,29 +285,33 @@ moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *
 typedef enum {
     MOE_WS_TOPK_IDS = 0,      /* int32 [T, k]                                        */
     MOE_WS_TOPK_WEIGHTS = 1,  /* fp32 [T, k]                                         */
-    MOE_WS_SORTED_IDS = 2,    /* int32 [capacity] (moe_align's sorted_token_ids)     */
+    MOE_WS_SORTED_IDS = 2,    /* int32 [capacity] (moe_align's sorted_token_ids); ragged:
+                                 [T * k], the pairs only                              */
     MOE_WS_EXPERT_IDS = 3,    /* int32 [capacity / block_m]                          */
     MOE_WS_NUM_POST_PAD = 4,  /* int32 [1]                                           */
     MOE_WS_EXPERT_COUNTS = 5, /* int32 [E]                                           */
-    MOE_WS_INV_POS = 6,       /* int32 [T * k]                                       */
+    MOE_WS_INV_POS = 6,       /* int32 [T * k] row of each pair (in h and y)          */
     MOE_WS_SCALARS = 7,       /* fp8: [0] amax(x) and [1] amax(h) as fp32 bits, [2] the
                                  activation scale s1, [3] the intermediate scale s2     */
     MOE_WS_X_Q = 8,           /* fp8: E4M3 [T, H] quantised hidden states            */
-    MOE_WS_H = 9,             /* [capacity, I] SiLU(gate) * up per sorted row: bf16, or
-                                 fp32 for fp8 weights (its E4M3 code is chosen in fp32) */
-    MOE_WS_H_Q = 10,          /* fp8: E4M3 [capacity, I] quantised h                 */
-    MOE_WS_Y = 11,            /* bf16 [capacity, H] weighted expert rows, or with split_k > 1
-                                 fp32 [split_k, capacity, H] partial sums             */
+    MOE_WS_H = 9,             /* [rows, I] SiLU(gate) * up per sorted row: bf16, or fp32
+                                 for fp8 weights (its E4M3 code is chosen in fp32); rows =
+                                 capacity, or T * k when ragged (also below)            */
+    MOE_WS_H_Q = 10,          /* fp8: E4M3 [rows, I] quantised h                     */
+    MOE_WS_Y = 11,            /* bf16 [rows, H] weighted expert rows, or with split_k > 1
+                                 fp32 [split_k, rows, H] partial sums                 */
     MOE_WS_ALIGN_SCRATCH = 12, /* int32 per-chunk expert histograms of the multi-launch
                                   align (T*k > 65536 only)                            */
-    MOE_WS_GEMM1_PARTIALS = 13, /* split_k1 > 1: fp32 [split_k1, capacity, 2I] gate (columns
+    MOE_WS_GEMM1_PARTIALS = 13, /* split_k1 > 1: fp32 [split_k1, rows, 2I] gate (columns
                                    [0, I)) and up ([I, 2I)) partial sums              */
     MOE_WS_GEMM2_TAIL = 14,   /* split_tail > 1: int32 [4] = first sorted row of the split
                                  row blocks, S (0: none split), elements per plane, 0;
                                  then at byte 256 fp32 [S, rows, H] partial sums        */
     MOE_WS_GEMM1_TAIL = 15,   /* split_tail1 > 1: the same for GEMM1, planes fp32
                                  [S, rows, 2I] of gate ([0, I)) and up ([I, 2I)) sums  */
-    MOE_WS_COUNT = 16
+    MOE_WS_BLOCK_START = 16,  /* ragged: int32 [capacity / block_m + 1] first row of each
+                                 block, T * k past the last block                    */
+    MOE_WS_COUNT = 17
 } moe_ws_region;
 
 /* Byte offset of each moe_ws_region in the workspace of moe_forward(layer, T, plan) into

@@ -22,7 +22,7 @@ STAGES = ("route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce", 
 STAGE_COUNT = len(STAGES)
 WS_REGIONS = ("topk_ids", "topk_weights", "sorted_ids", "expert_ids", "num_post_pad", "expert_counts",
               "inv_pos", "scalars", "x_q", "h", "h_q", "y", "align_scratch", "gemm1_partials", "gemm2_tail",
-              "gemm1_tail")
+              "gemm1_tail", "block_start")
 
 # every function include/moe.h declares (checked against the header by the tests)
 EXPORTS = ("moe_status_str", "moe_align_capacity", "moe_route", "moe_align", "moe_default_plan",
@@ -62,16 +62,16 @@ class GroupedGemmDesc(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("gemm1_tile", ctypes.c_int32), ("gemm2_tile", ctypes.c_int32),
                 ("split_k", ctypes.c_int32), ("split_k1", ctypes.c_int32), ("split_tail", ctypes.c_int32),
-                ("max_workgroups", ctypes.c_int32), ("split_tail1", ctypes.c_int32)]
+                ("max_workgroups", ctypes.c_int32), ("split_tail1", ctypes.c_int32), ("ragged", ctypes.c_int32)]
 
     def as_tuple(self):
         """(block_m, gemm1_tile, gemm2_tile, split_k[, split_k1[, split_tail[, max_workgroups[,
-        split_tail1]]]]), trailing defaults left out."""
+        split_tail1[, ragged]]]]]), trailing defaults left out."""
         t = (self.block_m, self.gemm1_tile, self.gemm2_tile, self.split_k, self.split_k1, self.split_tail,
-             self.max_workgroups, self.split_tail1)
+             self.max_workgroups, self.split_tail1, self.ragged)
         n = 4
-        for i in range(4, 8):
-            if t[i] > (0 if i == 6 else 1):
+        for i in range(4, 9):
+            if t[i] > (0 if i in (6, 8) else 1):
                 n = i + 1
         return t[:n]
 

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(1024) void k_align_fused(AlignArgs a) {
     __shared__ int hist[kWaves][kMaxE];   // this chunk's per-wave counts, then write cursors
     __shared__ int before[kMaxE];         // pairs per expert in earlier chunks
     __shared__ int cnt_s[kMaxE];          // pairs per expert in later chunks, then in all
-    __shared__ int off_s[kMaxE + 1];
+    __shared__ int off_s[kMaxE + 1];      // padded offsets
+    __shared__ int coff_s[kMaxE + 1];     // unpadded offsets
     const int tid = threadIdx.x, w = tid >> 6, G = gridDim.x;
     const int P = a.T * a.k, E = a.E, BM = a.BM;
     const int c0 = blockIdx.x * kFusedChunk, c1 = c0 + kFusedChunk;
@@ -64,22 +65,28 @@ __global__ __launch_bounds__(1024) void k_align_fused(AlignArgs a) {
         cnt_s[tid] = cnt;
         if (blockIdx.x == 0) a.counts[tid] = cnt;
         off_s[tid] = (cnt + BM - 1) / BM * BM;
+        coff_s[tid] = cnt;
     }
     __syncthreads();
     scan_experts(off_s, E);
+    scan_experts(coff_s, E);
     __syncthreads();
     const int total = off_s[kMaxE];
     if (blockIdx.x == 0 && tid == 0) *a.npp = total;
+    const int *base = a.blk_start ? coff_s : off_s;   // where each expert's rows start
     if (tid < E)
-        for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += off_s[tid];
-    // rows no pair lands in: each expert's padding (experts dealt round the workgroups) and
-    // every row past the last block
-    for (int e = blockIdx.x; e < E; e += G) {
-        const int r0 = off_s[e] + cnt_s[e], r1 = off_s[e] + (cnt_s[e] + BM - 1) / BM * BM;
-        for (int r = r0 + tid; r < r1; r += 1024) a.sorted[r] = P;
+        for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += base[tid];
+    if (!a.blk_start) {
+        // rows no pair lands in: each expert's padding (experts dealt round the workgroups)
+        // and every row past the last block
+        for (int e = blockIdx.x; e < E; e += G) {
+            const int r0 = off_s[e] + cnt_s[e], r1 = off_s[e] + (cnt_s[e] + BM - 1) / BM * BM;
+            for (int r = r0 + tid; r < r1; r += 1024) a.sorted[r] = P;
+        }
+        for (int64_t r = total + (int64_t)blockIdx.x * 1024 + tid; r < a.cap; r += (int64_t)G * 1024) a.sorted[r] = P;
     }
-    for (int64_t r = total + (int64_t)blockIdx.x * 1024 + tid; r < a.cap; r += (int64_t)G * 1024) a.sorted[r] = P;
-    write_block_experts(off_s, E, BM, a.cap, total, a.eids, (int64_t)blockIdx.x * 1024 + tid, (int64_t)G * 1024);
+    write_block_experts(off_s, coff_s, E, BM, a.cap, total, P, a.eids, a.blk_start, (int64_t)blockIdx.x * 1024 + tid,
+                        (int64_t)G * 1024);
     __syncthreads();
     scatter_range(a.ids, beg, end, E, a.nbits, hist[w], a.sorted, a.inv_pos);
 }
@@ -105,29 +112,33 @@ __global__ __launch_bounds__(512) void k_align_count(AlignArgs a, int32_t *chunk
 // One workgroup: totals, padded offsets, expert_ids, fillers, and chunk_counts rewritten in
 // place as each chunk's first row per expert.
 __global__ __launch_bounds__(1024) void k_align_scan(AlignArgs a, int32_t *chunk_counts, int nchunks) {
-    __shared__ int off_s[kMaxE + 1];
+    __shared__ int off_s[kMaxE + 1];      // padded offsets
+    __shared__ int coff_s[kMaxE + 1];     // unpadded offsets
     const int tid = threadIdx.x, P = a.T * a.k, E = a.E, BM = a.BM;
-    for (int64_t r = tid; r < a.cap; r += 1024) a.sorted[r] = P;
+    if (!a.blk_start)   // the padded layout's filler entries
+        for (int64_t r = tid; r < a.cap; r += 1024) a.sorted[r] = P;
     if (tid < E) {
         int run = 0;
         for (int c = 0; c < nchunks; c++) run += chunk_counts[(int64_t)c * E + tid];
         a.counts[tid] = run;
         off_s[tid] = (run + BM - 1) / BM * BM;
+        coff_s[tid] = run;
     }
     __syncthreads();
     scan_experts(off_s, E);
+    scan_experts(coff_s, E);
     __syncthreads();
     const int total = off_s[kMaxE];
     if (tid == 0) *a.npp = total;
     if (tid < E) {
-        int run = off_s[tid];
+        int run = a.blk_start ? coff_s[tid] : off_s[tid];
         for (int c = 0; c < nchunks; c++) {
             const int cnt = chunk_counts[(int64_t)c * E + tid];
             chunk_counts[(int64_t)c * E + tid] = run;
             run += cnt;
         }
     }
-    write_block_experts(off_s, E, BM, a.cap, total, a.eids, tid, 1024);
+    write_block_experts(off_s, coff_s, E, BM, a.cap, total, P, a.eids, a.blk_start, tid, 1024);
 }
 
 __global__ __launch_bounds__(512) void k_align_scatter(AlignArgs a, const int32_t *chunk_base) {

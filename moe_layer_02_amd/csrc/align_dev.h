@@ -112,12 +112,17 @@ __device__ __forceinline__ void count_strided(const int32_t *ids, int beg, int e
     }
 }
 
-// expert_ids for every block: the last expert whose first row is at or before the block's
-// first row owns it (experts with no rows share their successor's offset).  Blocks first,
-// first + stride, ... are written by the calling thread.
-__device__ __forceinline__ void write_block_experts(const int *off_s, int E, int BM, int64_t cap, int total,
-                                                    int32_t *eids, int64_t first, int64_t stride) {
-    for (int64_t b = first; b < cap / BM; b += stride) {
+// expert_ids for every block: the last expert whose first padded row is at or before the
+// block's first padded row owns it (experts with no rows share their successor's offset).
+// Without padding (blk_start non-null) also the block's first row among the unpadded rows,
+// coff_s[e] + (its padded first row - off_s[e]), and P (the number of pairs) for the blocks
+// past the last one, through blk_start[cap / BM].  Blocks first, first + stride, ... are
+// written by the calling thread.
+__device__ __forceinline__ void write_block_experts(const int *off_s, const int *coff_s, int E, int BM, int64_t cap,
+                                                    int total, int P, int32_t *eids, int32_t *blk_start,
+                                                    int64_t first, int64_t stride) {
+    const int64_t nb = cap / BM;
+    for (int64_t b = first; b <= nb; b += stride) {
         const int64_t r = b * BM;
         int e = -1;
         if (r < total) {
@@ -128,7 +133,8 @@ __device__ __forceinline__ void write_block_experts(const int *off_s, int E, int
             }
             e = lo;
         }
-        eids[b] = e;
+        if (b < nb) eids[b] = e;
+        if (blk_start) blk_start[b] = e >= 0 ? coff_s[e] + (int)(r - off_s[e]) : P;
     }
 }
 
@@ -136,12 +142,14 @@ __device__ __forceinline__ void write_block_experts(const int *off_s, int E, int
 // thread must call; the pairs must already be visible to the workgroup).
 __device__ __forceinline__ void align_group(const AlignArgs &a) {
     __shared__ int hist[kWaves][kMaxE];   // per-wave counts, then per-wave write cursors
-    __shared__ int off_s[kMaxE + 1];
+    __shared__ int off_s[kMaxE + 1];      // padded offsets
+    __shared__ int coff_s[kMaxE + 1];     // unpadded offsets (the layout without padding)
     const int tid = threadIdx.x, w = tid >> 6;
     const int P = a.T * a.k, E = a.E, BM = a.BM;
 
     for (int i = tid; i < kWaves * kMaxE; i += 1024) hist[i / kMaxE][i % kMaxE] = 0;
-    for (int64_t r = tid; r < a.cap; r += 1024) a.sorted[r] = P;
+    if (!a.blk_start)   // the padded layout's filler entries
+        for (int64_t r = tid; r < a.cap; r += 1024) a.sorted[r] = P;
     __syncthreads();
     // each wave owns a contiguous segment of pairs, a multiple of 64 long
     const int seg = (P + kWaves * kWave - 1) / (kWaves * kWave) * kWave;
@@ -157,15 +165,18 @@ __device__ __forceinline__ void align_group(const AlignArgs &a) {
         }
         a.counts[tid] = run;
         off_s[tid] = (run + BM - 1) / BM * BM;
+        coff_s[tid] = run;
     }
     __syncthreads();
     scan_experts(off_s, E);
+    scan_experts(coff_s, E);
     __syncthreads();
     const int total = off_s[kMaxE];
     if (tid == 0) *a.npp = total;
+    const int *base = a.blk_start ? coff_s : off_s;   // where each expert's rows start
     if (tid < E)
-        for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += off_s[tid];
-    write_block_experts(off_s, E, BM, a.cap, total, a.eids, tid, 1024);
+        for (int ww = 0; ww < kWaves; ww++) hist[ww][tid] += base[tid];
+    write_block_experts(off_s, coff_s, E, BM, a.cap, total, P, a.eids, a.blk_start, tid, 1024);
     __syncthreads();
     scatter_range(a.ids, beg, end, E, a.nbits, hist[w], a.sorted, a.inv_pos);
 }

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
         const int mb = gm0 + local % gsz;
         const int nt = local / gsz;
         const int e = a.eids[mb];
-        const int row0 = mb * C::BM;
+        const BlockRows br = block_rows(a, mb, C::BM);
+        const int row0 = br.row0;   // first row of the block in h / y (the layout's)
         const int kbase = s * a.ksplit;
 
         // ---- per-thread global sources for this tile (fixed over the K loop) ----
@@ -105,11 +106,11 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                 const int g_ebytes = WT == WT_FP8 ? 1 : 2;     // A element bytes in global
                 int64_t arow;
                 if (KIND == GEMM_GATE_UP) {
-                    const int p = a.sorted[row0 + r];
+                    const int p = block_pair(a, br, r);
                     a_ok[it] = p < a.pairs;
                     arow = a_ok[it] ? p / a.top_k : 0;
                 } else {
-                    arow = row0 + r;
+                    arow = row0 + (r < br.n ? r : 0);   // past the block's pairs: never stored
                 }
                 a_src[it] = (const char *)a.A + (arow * a.lda + (int64_t)kbase) * g_ebytes + ch * 16;
             }
@@ -300,8 +301,8 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int row = row0 + wm * C::TM + fm * 16 + 4 * (lane >> 4) + i;
-                    if (a.sorted[row] >= a.pairs) continue;
+                    const int lr = wm * C::TM + fm * 16 + 4 * (lane >> 4) + i, row = row0 + lr;
+                    if (block_pair(a, br, lr) >= a.pairs) continue;
                     float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
@@ -323,11 +324,12 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                     for (int i = 0; i < 4; i++) {
                         const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
                         const float hv = silu(g) * u;
-                        const int row = row0 + wm * C::TM + fm * 16 + 4 * (lane >> 4) + i;
+                        const int lr = wm * C::TM + fm * 16 + 4 * (lane >> 4) + i, row = row0 + lr;
+                        if (lr >= br.n) continue;   // without padding: the next block's row
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
                         if constexpr (WT == WT_FP8) {   // fp32: its E4M3 code is decided in fp32
                             ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
-                            if (a.sorted[row] < a.pairs) amax = fmaxf(amax, fabsf(hv));   // valid rows only
+                            if (block_pair(a, br, lr) < a.pairs) amax = fmaxf(amax, fabsf(hv));   // valid rows only
                         } else {
                             ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
                         }
@@ -342,8 +344,8 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int row = row0 + wm * C::TM + fm * 16 + 4 * (lane >> 4) + i;
-                    const int p = a.sorted[row];
+                    const int lr = wm * C::TM + fm * 16 + 4 * (lane >> 4) + i, row = row0 + lr;
+                    const int p = block_pair(a, br, lr);
                     if (p >= a.pairs) continue;   // filler row: never read back
                     const float w = a.topk_w[p] * scale;
 #pragma unroll

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
         const TileCoord tc = tile_coord(tile, mn, mblocks, ntiles, a.group_m);
         const int s = tc.s, mb = tc.mb, nt = tc.nt;
         const int e = __builtin_amdgcn_readfirstlane(a.eids[mb]);
-        const int row0 = mb * C::BM;
+        const BlockRows br = block_rows(a, mb, C::BM);
+        const int row0 = br.row0;   // first row of the block in h / y (the layout's)
 
         // B row (of the expert's matrix) that tile row rr of the B slab holds
         auto b_row = [&](int rr) -> int64_t {
@@ -128,8 +129,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                 const int slab = ins / (C::BM / 8), rb = ins % (C::BM / 8) * 8;
                 const int r = rb + (lane >> 3);
                 const int chunk = (lane & 7) ^ swz(r);
-                const int p = a.sorted[row0 + r];
-                const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + r;
+                const int p = block_pair(a, br, r);
+                // a row past the block's pairs reads its block's first row (never stored)
+                const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + (r < br.n ? r : 0);
                 on[q] = !C::SKIP_FILLER || p < a.pairs || (lane >> 3) == 0;
                 voff[q] = (uint32_t)(arow * a.lda * 2 + slab * 128 + chunk * 16);
                 dst[q] = (slab * C::BM + rb) * 128;
@@ -270,8 +272,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int row = row0 + wm * C::TM + fm * 16 + frag_row<16>(lane, i);
-                    if (a.sorted[row] >= a.pairs) continue;
+                    const int lr = wm * C::TM + fm * 16 + frag_row<16>(lane, i), row = row0 + lr;
+                    if (block_pair(a, br, lr) >= a.pairs) continue;
                     float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
@@ -286,7 +288,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int row = row0 + wm * C::TM + fm * 16 + frag_row<16>(lane, i);
+                    const int lr = wm * C::TM + fm * 16 + frag_row<16>(lane, i), row = row0 + lr;
+                    if (lr >= br.n) continue;   // without padding: the next block's row
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
                         const float hv = silu(acc[fm][f][i]) * acc[fm][f + C::FN / 2][i];
@@ -299,8 +302,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int row = row0 + wm * C::TM + fm * 16 + frag_row<16>(lane, i);
-                    const int p = a.sorted[row];
+                    const int lr = wm * C::TM + fm * 16 + frag_row<16>(lane, i), row = row0 + lr;
+                    const int p = block_pair(a, br, lr);
                     if (p >= a.pairs) continue;   // filler row: never read back
                     const float w = a.topk_w[p];
 #pragma unroll

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 }
             }
             if (blockIdx.x == 0 && tid == 0) {
-                a.tail_info[0] = mb_dp * C::BM;
+                a.tail_info[0] = block_rows(a, mb_dp, C::BM).row0;   // the tail's first row
                 a.tail_info[1] = tail_s;
                 a.tail_info[2] = (mblocks - mb_dp) * C::BM * tail_ld;
                 a.tail_info[3] = 0;
@@ -115,7 +115,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     }
     const int mn_dp = mb_dp * ntiles;
     const int total = TAIL ? mn_dp + tail_tiles * tail_s : mn * a.split;
-    const int64_t tail_plane = (int64_t)(mblocks - mb_dp) * C::BM * tail_ld;
+    const int64_t tail_plane = (int64_t)(mblocks - mb_dp) * C::BM * tail_ld;   // at least the tail's rows
+    const int tail_row0 = tail_tiles ? block_rows(a, mb_dp, C::BM).row0 : 0;
 
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
         // unit: whole-K tile (or one of split_k splits), or one split of a tail tile
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         const int kbeg = tail ? s * nk / tail_s : s * nk;     // first K step and number of steps
         const int nku = tail ? (s + 1) * nk / tail_s - kbeg : nk;
         const int e = __builtin_amdgcn_readfirstlane(a.eids[mb]);
-        const int row0 = mb * C::BM;
+        const BlockRows br = block_rows(a, mb, C::BM);
+        const int row0 = br.row0;   // first row of the block in h / y (the layout's)
         const int64_t kb = (int64_t)kbeg * C::BK * ebytes;    // byte offset of this unit's K
 
         // per load instruction q of this wave: operand (A or B), the lane's byte offset from
@@ -145,10 +147,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                 const int slab = ins / (C::BM / C::RPI), rb = ins % (C::BM / C::RPI) * C::RPI;
                 int r, chunk;
                 dma_lane<C::SB>(lane, rb, r, chunk);
-                const int p = a.sorted[row0 + r];
+                const int p = block_pair(a, br, r);
+                // a row past the block's pairs reads its block's first row (in bounds; its
+                // products are never stored)
                 const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0)
                                      : a.gather_a       ? (p < a.pairs ? p : 0)
-                                                        : row0 + r;
+                                                        : row0 + (r < br.n ? r : 0);
                 // a filler row's products are never read back, so its LDS row may keep stale
                 // data; the lanes of the instruction's first row always load, so every load
                 // instruction runs with a non-empty mask and counts in vmcnt
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         // A block holds its expert's rows first and padding after them, so a wave row range
         // with no real row starts with padding: such waves (the tail block of an expert at
         // large block heights) skip their LDS reads and MFMAs but still load and synchronise
-        const bool wave_rows = __builtin_amdgcn_readfirstlane(a.sorted[row0 + wm * C::TM] < a.pairs);
+        const bool wave_rows = __builtin_amdgcn_readfirstlane(block_pair(a, br, wm * C::TM) < a.pairs);
         using Acc = typename AccOf<C::MS>::type;
         constexpr int NR = C::MS == 32 ? 16 : 4;              // accumulator values per lane per fragment
         Acc acc[C::FM][C::FN];
@@ -366,8 +370,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < NR; i++) {
-                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
-                    if (a.sorted[row] >= a.pairs) continue;
+                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
+                    if (block_pair(a, br, lr) >= a.pairs) continue;
                     float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
@@ -383,9 +387,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < NR; i++) {
-                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
-                    if (a.sorted[row] >= a.pairs) continue;
-                    float *P = a.tail_P + s * tail_plane + (int64_t)(row - mb_dp * C::BM) * tail_ld;
+                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
+                    if (block_pair(a, br, lr) >= a.pairs) continue;
+                    float *P = a.tail_P + s * tail_plane + (int64_t)(row - tail_row0) * tail_ld;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
@@ -402,8 +406,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < NR; i++) {
-                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
-                    const bool valid = a.sorted[row] < a.pairs;
+                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
+                    const bool valid = block_pair(a, br, lr) < a.pairs;
+                    // without padding the rows past the block are the next block's: not written
+                    if (lr >= br.n) continue;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
                         const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
@@ -427,8 +433,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < NR; i++) {
-                    const int row = row0 + wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i);
-                    const int p = a.sorted[row];
+                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
+                    const int p = block_pair(a, br, lr);
                     if (p >= a.pairs) continue;   // filler row: never read back
                     const float w = (a.topk_w ? a.topk_w[p] : 1.0f) * scale;   // the grouped GEMM has no weight
 #pragma unroll
@@ -438,7 +444,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         if constexpr (PARTIAL)
                             ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
                         else if (tail)
-                            a.tail_P[s * tail_plane + (int64_t)(row - mb_dp * C::BM) * a.ldc + col] = v;
+                            a.tail_P[s * tail_plane + (int64_t)(row - tail_row0) * a.ldc + col] = v;
                         else
                             ((uint16_t *)a.C)[(a.out_by_pair ? (int64_t)p : row) * a.ldc + col] = f32_to_bf16_bits(v);
                     }

@@ -25,6 +25,10 @@ struct AlignArgs {
     int64_t cap;
     const int32_t *ids;
     int32_t *sorted, *eids, *npp, *counts, *inv_pos;
+    // null: the padded layout; else no padding -- sorted holds the T*k pairs expert by
+    // expert, and blk_start[b] the first row of block b (blocks cut at expert ends; T*k for
+    // b past the last block, capacity / BM + 1 entries)
+    int32_t *blk_start;
 };
 // scratch: align_scratch_bytes() of device memory for the multi-launch path (T*k above
 // 65536; zero bytes below), or null to run such batches on the one-workgroup kernel
@@ -45,6 +49,8 @@ struct GemmArgs {
     int64_t ldc;                 // elements per row of C
     int64_t partial_stride;      // elements between split-K partial planes
     const int32_t *sorted, *eids, *npp;
+    const int32_t *blk_start;    // null: padded layout (block b = rows b*BM ..); else block b = rows
+                                 // [blk_start[b], blk_start[b + 1]) of one expert, at most BM
     const float *topk_w;         // down: pair weights
     int K, N;                    // reduction length; output columns
     int I;                       // gate/up: offset of the up rows in w13
@@ -67,6 +73,25 @@ struct GemmArgs {
 };
 
 enum GemmKind { GEMM_GATE_UP = 1, GEMM_DOWN = 2 };
+
+// The rows [row0, row0 + n) of the intermediates (h, y, split planes) that row block mb
+// covers: mb * BM and BM in the padded layout, the block table's entries without padding.
+struct BlockRows {
+    int row0, n;
+};
+__device__ __forceinline__ BlockRows block_rows(const GemmArgs &a, int mb, int BM) {
+    if (a.blk_start) {
+        const int s = a.blk_start[mb];
+        return BlockRows{s, a.blk_start[mb + 1] - s};
+    }
+    return BlockRows{mb * BM, BM};
+}
+// The pair held by row r (0 <= r < BM) of the block: a.pairs (the filler value) for a
+// padded layout's filler rows and for the rows past a block's end without padding (whose
+// entries belong to the next block).
+__device__ __forceinline__ int block_pair(const GemmArgs &a, BlockRows b, int r) {
+    return r < b.n ? a.sorted[b.row0 + r] : a.pairs;
+}
 
 struct TileInfo {
     int BM, BN, BK, WM, WN;      // tile rows, B rows per tile, K step, wave grid
@@ -121,6 +146,7 @@ struct GateUpFinishArgs {
     // on, tail_info[1] planes (0: none, nothing to do) of tail_info[2] elements, whose row
     // r - tail_info[0] holds row r's sums; plane and split above are then unused
     const int32_t *tail_info;
+    int ragged;                  // rows are the T*k pairs (no filler rows; sorted unused)
 };
 hipError_t launch_gate_up_finish(const GateUpFinishArgs &a, int64_t max_rows, hipStream_t s);
 // fp32 h (GATE_UP_H_F32) of a small batch, finished and quantised to E4M3 in one workgroup:

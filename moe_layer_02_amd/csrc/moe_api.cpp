@@ -5,11 +5,13 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 
 #include "../../include/moe.h"
 #include "kernels.h"
+#include "plan_table.h"
 
 namespace moe {
 
@@ -121,6 +123,7 @@ moe_status check_plan(const moe_layer *L, const moe_plan *p, TileInfo *t1, TileI
     // GEMM1's split tail: the unsplit GEMM1 of the pipelined bf16 / fp8 tiles
     if (p->split_tail1 < 0 || p->split_tail1 > 16) return MOE_ERR_INVALID_ARGUMENT;
     if (p->split_tail1 > 1 && (s1 > 1 || t1->stages == 0 || wd == MOE_DT_INT4_G128)) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->ragged != 0 && p->ragged != 1) return MOE_ERR_INVALID_ARGUMENT;
     return MOE_OK;
 }
 
@@ -144,8 +147,9 @@ int prologue_max_t(const moe_layer *L) {
 
 struct Workspace {
     size_t ids, weights, sorted, eids, npp, counts, inv_pos, scal, xq, h, hq, y, align_scratch, g1p, tail, tail1,
-        total;
+        blk_start, total;
     int64_t cap;
+    int64_t rows;   // rows of h, y and the K-split planes: cap, or T*k with no padding
 };
 
 // scal words: [0] amax(x) bits, [1] amax(h) bits, [2] s1, [3] s2
@@ -167,6 +171,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     const int k = L->route.top_k, E = L->E;
     const int64_t pairs = (int64_t)T * k;
     w.cap = moe_align_capacity(T, k, E, p->block_m);
+    w.rows = p->ragged ? pairs : w.cap;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -175,7 +180,7 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     };
     w.ids = take(pairs * 4);
     w.weights = take(pairs * 4);
-    w.sorted = take(w.cap * 4);
+    w.sorted = take((p->ragged ? pairs : w.cap) * 4);
     w.eids = take(w.cap / p->block_m * 4);
     w.npp = take(4);
     w.counts = take((size_t)E * 4);
@@ -183,18 +188,19 @@ Workspace layout(const moe_layer *L, int T, const moe_plan *p) {
     w.scal = take(kScalarWords * 4);
     const bool fp8 = L->weight_dtype == MOE_DT_FP8_E4M3;
     w.xq = take(fp8 ? (size_t)T * L->H : perm_activations(L, p) ? (size_t)T * L->H * 2 : 0);
-    w.h = take((size_t)w.cap * L->I * (fp8 ? 4 : 2));
-    w.hq = take(fp8 ? (size_t)w.cap * L->I : 0);
+    w.h = take((size_t)w.rows * L->I * (fp8 ? 4 : 2));
+    w.hq = take(fp8 ? (size_t)w.rows * L->I : 0);
     w.y = take(direct_output(L, p) ? 0
-               : p->split_k > 1 ? (size_t)p->split_k * w.cap * L->H * 4 : (size_t)w.cap * L->H * 2);
+               : p->split_k > 1 ? (size_t)p->split_k * w.rows * L->H * 4 : (size_t)w.rows * L->H * 2);
     w.align_scratch = take((size_t)align_scratch_bytes(pairs, E));
-    w.g1p = take(split1(p) > 1 ? (size_t)split1(p) * w.cap * 2 * L->I * 4 : 0);
+    w.g1p = take(split1(p) > 1 ? (size_t)split1(p) * w.rows * 2 * L->I * 4 : 0);
     TileInfo t1{}, t2{};
     gemm_tile_info(L->weight_dtype, p->gemm1_tile, &t1);
     gemm_tile_info(L->weight_dtype, p->gemm2_tile, &t2);
     w.tail = take(split_tail(p) ? kTailInfoBytes + (size_t)kTailUnits * t2.BM * t2.BN * 4 : 0);
     // a GEMM1 tile's unit covers BN / 2 gate and BN / 2 up columns: BM x BN fp32 as well
     w.tail1 = take(split_tail1(p) ? kTailInfoBytes + (size_t)kTailUnits * t1.BM * t1.BN * 4 : 0);
+    w.blk_start = take(p->ragged ? (size_t)(w.cap / p->block_m + 1) * 4 : 0);
     w.total = o;
     return w;
 }
@@ -264,7 +270,8 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     hipError_t err;
 
     RouteArgs ra = route_args(&L->route, T, logits, L->correction_bias, ids, topk_w);
-    AlignArgs aa{T, k, E, plan.block_m, nbits_for(E), w.cap, ids, sorted, eids, npp, counts, inv_pos};
+    int32_t *blk_start = plan.ragged ? (int32_t *)(ws + w.blk_start) : nullptr;
+    AlignArgs aa{T, k, E, plan.block_m, nbits_for(E), w.cap, ids, sorted, eids, npp, counts, inv_pos, blk_start};
     const void *a1 = hidden;
     const bool prologue = T <= prologue_max_t(L);
     if (prologue) {
@@ -332,6 +339,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     g.sorted = sorted;
     g.eids = eids;
     g.npp = npp;
+    g.blk_start = blk_start;
     g.topk_w = topk_w;
     g.K = H;
     g.N = I;
@@ -351,7 +359,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     if (s1 > 1) {   // fp32 partial planes of gate and up, finished below
         g.C = ws + w.g1p;
         g.ldc = 2 * (int64_t)I;
-        g.partial_stride = w.cap * 2 * (int64_t)I;
+        g.partial_stride = w.rows * 2 * (int64_t)I;
         g.split = s1;
         g.ksplit = H / s1;
         g.amax_out = nullptr;
@@ -374,17 +382,17 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     const bool finish_quant = fp8 && s1 > 1 && (int64_t)pairs * I * s1 <= 32768;
     if (s1 > 1) {
         if ((err = mark(MOE_STAGE_GEMM1_FINISH)) != hipSuccess) return MOE_ERR_HIP;
-        GateUpFinishArgs f{(const float *)(ws + w.g1p), w.cap * 2 * (int64_t)I, s1, I, sorted, npp, pairs, ws + w.h,
+        GateUpFinishArgs f{(const float *)(ws + w.g1p), w.rows * 2 * (int64_t)I, s1, I, sorted, npp, pairs, ws + w.h,
                            fp8 ? GATE_UP_H_F32 : perm_activations(L, &plan) ? GATE_UP_H_BF16_PERM : GATE_UP_H_BF16,
-                           fp8 ? &scal[1] : nullptr};
+                           fp8 ? &scal[1] : nullptr, nullptr, plan.ragged};
         err = finish_quant ? launch_gate_up_finish_quant(f, inv_pos, (uint8_t *)(ws + w.hq), (float *)&scal[3], stream)
-                           : launch_gate_up_finish(f, w.cap, stream);
+                           : launch_gate_up_finish(f, w.rows, stream);
         if (err != hipSuccess) return fail(err);
     } else if (split_tail1(&plan)) {
         // the split row blocks' h (GEMM1 recorded the rows and planes; none: an empty pass)
         if ((err = mark(MOE_STAGE_GEMM1_FINISH)) != hipSuccess) return MOE_ERR_HIP;
         GateUpFinishArgs f{(const float *)(ws + w.tail1 + kTailInfoBytes), 0, 0, I, sorted, npp, pairs, ws + w.h,
-                           fp8 ? GATE_UP_H_F32 : GATE_UP_H_BF16, fp8 ? &scal[1] : nullptr, tail1_info};
+                           fp8 ? GATE_UP_H_F32 : GATE_UP_H_BF16, fp8 ? &scal[1] : nullptr, tail1_info, plan.ragged};
         // at most kTailUnits / (column tiles) row blocks are split
         const int64_t tail_rows = (int64_t)kTailUnits / (I / (t1.BN / 2)) * plan.block_m;
         if ((err = launch_gate_up_finish(f, std::max<int64_t>(tail_rows, plan.block_m), stream)) != hipSuccess)
@@ -397,7 +405,11 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         a2 = ws + w.hq;
     } else if (fp8) {
         if ((err = mark(MOE_STAGE_H_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-        QuantArgs q{ws + w.h, 1, (uint8_t *)(ws + w.hq), w.cap, I, &scal[1], (float *)&scal[3], sorted, npp, pairs};
+        // padded: the rows of the layout up to its end, filler rows zeroed; ragged: every row a pair
+        QuantArgs q = plan.ragged ? QuantArgs{ws + w.h, 1, (uint8_t *)(ws + w.hq), pairs, I, &scal[1], (float *)&scal[3],
+                                              nullptr, nullptr, pairs}
+                                  : QuantArgs{ws + w.h, 1, (uint8_t *)(ws + w.hq), w.cap, I, &scal[1], (float *)&scal[3],
+                                              sorted, npp, pairs};
         if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
         a2 = ws + w.hq;
     }
@@ -417,7 +429,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     d.C = direct ? out : (void *)(ws + w.y);
     d.ldc = H;
     d.out_by_pair = direct;
-    d.partial_stride = w.cap * (int64_t)H;
+    d.partial_stride = w.rows * (int64_t)H;
     d.K = I;
     d.N = H;
     d.split = plan.split_k;
@@ -431,7 +443,7 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
     d.tail_cap = kTailUnits;
     d.tail_P = tail_P;
     d.tail_info = tail_info;
-    const ReduceArgs r{ws + w.y, w.cap * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out,
+    const ReduceArgs r{ws + w.y, w.rows * (int64_t)H, plan.split_k > 1 ? plan.split_k : 0, inv_pos, (uint16_t *)out,
                        T, k, H, tail_info, tail_P, direct ? 1 : 0};
     if ((err = launch_gemm(wd, plan.gemm2_tile, GEMM_DOWN, plan.split_k > 1, d,
                            grid_cap(mblocks_max * (H / t2.BN) * plan.split_k), stream)) != hipSuccess)
@@ -594,52 +606,44 @@ moe_status moe_default_plan(const moe_layer *layer, int32_t T, moe_plan *plan) {
     moe_status st = check_layer(layer);
     if (st != MOE_OK) return st;
     if (T < 0 || !plan) return MOE_ERR_INVALID_ARGUMENT;
-    // Plans by rows per expert r = T*k/E, from timing every valid plan of the Mixtral,
-    // Llama-4-Scout, Qwen2 and DeepSeek-V3 shapes on MI355X (graph replays): each row is the
-    // plan with the smallest worst-case slowdown over the measured points of its range
-    // (within 6% of the fastest plan at every point but Mixtral T=512, 9%).  Small r
-    // streams weights (16-row blocks, narrow tiles, split-K for GEMM2, and for GEMM1 where
-    // an expert's I is small next to the GPU); large r is MFMA work (128x256 and 256x256
-    // tiles of 16 waves, GEMM2's partial last round split; with 128-row blocks GEMM1's as
-    // well: Mixtral T=1024 and Llama-4-Scout T=2048 -3.3%, Mixtral T=512 and 1536 -1%).
-    struct Row { double r_max; int bm, g1, g2, split, split1, tail, tail1; };
-    static const Row bf16[] = {{1.5, 16, 9, 9, 4, 1, 0},        {3, 16, 10, 9, 1, 1, 0},
-                               {8, 32, 19, 12, 1, 1, 0},        {24, 64, 18, 11, 1, 1, 0},
-                               {96, 128, 22, 22, 2, 1, 0},      {384, 128, 22, 22, 1, 1, 8, 8},
-                               {1e30, 256, 25, 25, 1, 1, 8}};
-    static const Row fp8[] = {{0.125, 16, 9, 1, 1, 2, 0},  {8, 16, 1, 1, 1, 2, 0},       {48, 32, 11, 2, 1, 1, 0},
-                              {192, 128, 7, 16, 1, 1, 8},  {384, 128, 13, 16, 1, 1, 8},  {1e30, 256, 12, 14, 1, 1, 8}};
-    static const Row int4[] = {{0.05, 16, 11, 11, 1, 2, 0}, {8, 16, 11, 11, 1, 1, 0}, {1e30, 32, 12, 12, 1, 1, 0}};
-    const Row *rows = bf16;
-    int n = sizeof(bf16) / sizeof(Row);
-    if (layer->weight_dtype == MOE_DT_FP8_E4M3) { rows = fp8; n = sizeof(fp8) / sizeof(Row); }
-    if (layer->weight_dtype == MOE_DT_INT4_G128) { rows = int4; n = sizeof(int4) / sizeof(Row); }
-    const double r = (double)T * layer->route.top_k / layer->E;
+    // The table measured by the tuner (plan_table.h, per layer shape and batch size): a tuned
+    // shape takes the plan of its tuned T nearest to T (on a log scale, the smaller on a tie);
+    // any other layer the plan of the tuned point of its weight type whose rows per expert
+    // are nearest to its own (T k / E, log scale) among those valid for it; else any valid plan.
+    const TunedPlan *best = nullptr;
+    double bd = 0;
+    const double lt = std::log2((double)std::max(T, 1));
+    for (const TunedPlan &t : kTunedPlans) {
+        if (t.wdtype != layer->weight_dtype || t.E != layer->E || t.k != layer->route.top_k || t.H != layer->H ||
+            t.I != layer->I)
+            continue;
+        const double d = std::fabs(std::log2((double)t.T) - lt);
+        if (!best || d < bd || (d == bd && t.T < best->T)) { best = &t; bd = d; }
+    }
+    auto as_plan = [](const TunedPlan &t) {
+        return moe_plan{t.block_m, t.gemm1_tile, t.gemm2_tile, t.split_k, t.split_k1, t.split_tail, t.max_workgroups,
+                        t.split_tail1, t.ragged};
+    };
     TileInfo t1, t2;
-    int first = 0;
-    while (first < n - 1 && r > rows[first].r_max) first++;
-    // the row for r, else (shapes it does not tile) the nearest row that fits; fewer K
-    // splits when the split does not divide the reduction
-    for (int d = 0; d < 2 * n; d++) {
-        const int i = d % 2 == 0 ? first + d / 2 : first - (d + 1) / 2;
-        if (i < 0 || i >= n) continue;
-        // top-1 at large r: no split, so that GEMM2 writes the output rows itself and the
-        // reduce pass only adds a split tail (Llama-4-Scout T=8192: 2.31 ms against 2.45 with
-        // split 2)
-        const int split0 = layer->route.top_k == 1 && r > 96 ? 1 : rows[i].split;
-        for (int sk = split0; sk >= 1; sk /= 2) {
-            moe_plan p{rows[i].bm, rows[i].g1, rows[i].g2, sk, rows[i].split1, sk == 1 ? rows[i].tail : 0, 0,
-                       rows[i].tail1};
-            if (check_plan(layer, &p, &t1, &t2) != MOE_OK) p.split_k1 = 1;   // H not split that way
-            if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
-                *plan = p;
-                return MOE_OK;
-            }
+    if (best) {
+        moe_plan p = as_plan(*best);
+        if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
+            *plan = p;
+            return MOE_OK;
         }
     }
-    // any valid plan (tiny or unusual shapes)
+    const double lr = std::log2(std::max((double)T * layer->route.top_k / layer->E, 1.0 / 64));
+    bool found = false;
+    for (const TunedPlan &t : kTunedPlans) {
+        if (t.wdtype != layer->weight_dtype) continue;
+        moe_plan p = as_plan(t);
+        if (check_plan(layer, &p, &t1, &t2) != MOE_OK) continue;
+        const double d = std::fabs(std::log2((double)t.T * t.k / t.E) - lr);
+        if (!found || d < bd) { *plan = p; bd = d; found = true; }
+    }
+    if (found) return MOE_OK;
     for (int bm : {16, 32, 64, 128, 256})
-        for (int g = 0; g < 40; g++) {
+        for (int g = 0; g < 64; g++) {
             moe_plan p{bm, g, g, 1, 1};
             if (check_plan(layer, &p, &t1, &t2) == MOE_OK) {
                 *plan = p;
@@ -700,11 +704,11 @@ moe_status moe_plan_describe(const moe_layer *layer, int32_t T, const moe_plan *
     std::snprintf(buf, len,
                   "block_m=%d gemm1=%d[BM%d BN%d BK%d waves%dx%d stages%d mfma%d] gemm2=%d[BM%d BN%d BK%d "
                   "waves%dx%d stages%d mfma%d] split_k=%d split_k1=%d split_tail=%d max_workgroups=%d "
-                  "split_tail1=%d",
+                  "split_tail1=%d ragged=%d",
                   plan->block_m, plan->gemm1_tile, t1.BM, t1.BN, t1.BK, t1.WM, t1.WN, t1.stages, t1.mfma,
                   plan->gemm2_tile, t2.BM, t2.BN, t2.BK, t2.WM, t2.WN, t2.stages, t2.mfma, plan->split_k, split1(plan),
                   split_tail(plan) ? plan->split_tail : 0, plan->max_workgroups,
-                  split_tail1(plan) ? plan->split_tail1 : 0);
+                  split_tail1(plan) ? plan->split_tail1 : 0, plan->ragged);
     return MOE_OK;
 }
 
@@ -719,7 +723,7 @@ moe_status moe_workspace_offsets(const moe_layer *layer, int32_t T, const moe_pl
     if ((st = check_plan(layer, &p, &t1, &t2)) != MOE_OK) return st;
     const Workspace w = layout(layer, T, &p);
     const size_t v[MOE_WS_COUNT] = {w.ids, w.weights, w.sorted, w.eids, w.npp, w.counts, w.inv_pos, w.scal,
-                                    w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p, w.tail, w.tail1};
+                                    w.xq, w.h, w.hq, w.y, w.align_scratch, w.g1p, w.tail, w.tail1, w.blk_start};
     for (int i = 0; i < MOE_WS_COUNT; i++) offsets[i] = (int64_t)v[i];
     return MOE_OK;
 }

@@ -113,12 +113,14 @@ __global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
         plane = a.tail_info[2];
         if (split == 0) return;
     }
-    const int64_t rows = *a.npp - r0;
+    // the padded layout's rows up to its end (filler rows skipped), or the T*k rows of the
+    // layout without padding (every one a pair)
+    const int64_t rows = (a.ragged ? (int64_t)a.pairs : (int64_t)*a.npp) - r0;
     float m = 0.0f;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * c8; i += (int64_t)gridDim.x * 256) {
         const int64_t pr = i / c8, r = r0 + pr;   // plane row, sorted row
         const int c = (int)(i % c8) * 8;
-        if (a.sorted[r] >= a.pairs) continue;
+        if (!a.ragged && a.sorted[r] >= a.pairs) continue;
         float g[8], u[8];
         for (int s = 0; s < split; s++) {
             const float *p = a.P + s * plane + pr * 2 * (int64_t)a.I;

@@ -79,24 +79,26 @@ def workspace_view(layer, T, plan, ws, region, dtype, count):
     return ws[off:off + count * torch.tensor([], dtype=dtype).element_size()].view(dtype)
 
 
-def valid_plans(layer, T, split1=(1, 2, 4), splits=(1, 2, 4, 8), tails=(0,), max_workgroups=0, tails1=(0,)):
-    """Every (block_m, tile1, tile2, split, split1, split_tail, split_tail1) the library
-    accepts for this layer (grids capped at max_workgroups)."""
+def valid_plans(layer, T, split1=(1, 2, 4), splits=(1, 2, 4, 8), tails=(0,), max_workgroups=0, tails1=(0,),
+                ragged=(0,)):
+    """Every (block_m, tile1, tile2, split, split1, split_tail, split_tail1, ragged) the
+    library accepts for this layer (grids capped at max_workgroups)."""
     n = 40
     out = []
-    for g1 in range(n):
-        for g2 in range(n):
-            for sk in splits:
-                for s1 in split1:
-                    for st in tails:
-                        for st1 in tails1:
-                            for bm in (16, 32, 64, 128, 256):
-                                p = abi.Plan(bm, g1, g2, sk, s1, st, max_workgroups, st1)
-                                try:
-                                    abi.moe_workspace_bytes(layer.struct, T, p)
-                                except abi.MoEError:
-                                    continue
-                                out.append(p)
+    for rg in ragged:
+        for g1 in range(n):
+            for g2 in range(n):
+                for sk in splits:
+                    for s1 in split1:
+                        for st in tails:
+                            for st1 in tails1:
+                                for bm in (16, 32, 64, 128, 256):
+                                    p = abi.Plan(bm, g1, g2, sk, s1, st, max_workgroups, st1, rg)
+                                    try:
+                                        abi.moe_workspace_bytes(layer.struct, T, p)
+                                    except abi.MoEError:
+                                        continue
+                                    out.append(p)
     return out
 
 
@@ -138,15 +140,20 @@ def expected_tail(npp, cap, H, I, tile, max_workgroups, split_tail, units=256, g
     return mblocks * BM, 0
 
 
-def block_cover_tokens(sorted_ids, npp, BM, k, pairs, extra=()):
+def block_cover_tokens(sorted_ids, npp, BM, k, pairs, extra=(), blk_start=None):
     """Tokens whose pairs lie in every row block of an align layout: block by block, a
     block with a real row that no chosen token covers adds the token of its last real row
     (the ragged edge of an expert's rows) -- so each block, the split-tail blocks included,
-    holds at least one row the oracle computes.  Plus the tokens in `extra`."""
+    holds at least one row the oracle computes.  Plus the tokens in `extra`.  blk_start:
+    the block table of the layout without padding (block b = sorted_ids[blk_start[b] :
+    blk_start[b + 1]])."""
     chosen = set(int(t) for t in extra)
     sorted_ids = np.asarray(sorted_ids)
     for b in range(int(npp) // BM):
-        rows = sorted_ids[b * BM:(b + 1) * BM]
+        if blk_start is None:
+            rows = sorted_ids[b * BM:(b + 1) * BM]
+        else:
+            rows = sorted_ids[int(blk_start[b]):int(blk_start[b + 1])]
         real = rows[rows < pairs]                      # pairs = T*k is the filler value
         if real.size == 0:
             continue

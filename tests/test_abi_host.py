@@ -270,7 +270,7 @@ def test_split_tail1_rules():
     off, off_plain = abi.moe_workspace_offsets(layer, T, with_tail), abi.moe_workspace_offsets(layer, T, plain)
     assert off["gemm1_tail"] >= off["gemm2_tail"] and off["gemm1_tail"] == off_plain["gemm1_tail"]
     assert abi.moe_workspace_bytes(layer, T, with_tail) - off["gemm1_tail"] >= 256 + 256 * 128 * 256 * 4
-    assert abi.moe_plan_describe(layer, T, with_tail).endswith("split_tail1=4")
+    assert abi.moe_plan_describe(layer, T, with_tail).endswith("split_tail1=4 ragged=0")
     assert with_tail.as_tuple() == (128, 22, 22, 1, 1, 8, 0, 4)
     for bad in [abi.Plan(16, 9, 9, 1, 2, 0, 0, 4),       # with GEMM1's K split of every tile
                 abi.Plan(16, 0, 0, 1, 1, 0, 0, 4),       # register-staged GEMM1 tile
@@ -339,5 +339,30 @@ def test_static_forward_size_checks_come_first():
     bad = fake_layer(synth.CONFIGS["mixtral"], w13=0x10001)                      # misaligned weights
     assert L.moe_forward_static(ctypes.byref(bad), 8, fake, fake, fake, None, None) == abi.MOE_ERR_INVALID_ARGUMENT
     # the sizes the array is stated to hold under the default plans
-    for name, T in (("mixtral", 512), ("qwen2", 256), ("deepseek", 256), ("scout", 256)):
+    for name, T in (("mixtral", 256), ("qwen2", 256), ("deepseek", 256), ("scout", 256)):
         assert abi.moe_workspace_bytes(fake_layer(synth.CONFIGS[name]), T) <= abi.STATIC_WORKSPACE_BYTES, name
+
+
+def test_ragged_plan_layout():
+    """The layout without padding: the plan field is 0 or 1; the intermediates hold T*k rows
+    instead of the padded capacity, the sorted ids T*k entries, and the block table one entry
+    per block and one past the last."""
+    for name, T in (("mixtral", 512), ("qwen2", 300), ("deepseek", 64), ("scout", 1000)):
+        cfg = synth.CONFIGS[name]
+        layer = fake_layer(cfg)
+        p = abi.moe_default_plan(layer, T)
+        r = abi.Plan(*(p.as_tuple() + (0,) * (8 - len(p.as_tuple()))), 1)
+        assert "ragged=1" in abi.moe_plan_describe(layer, T, r)
+        pad, rag = abi.moe_workspace_offsets(layer, T, p), abi.moe_workspace_offsets(layer, T, r)
+        cap = abi.moe_align_capacity(T, cfg.k, cfg.E, p.block_m)
+        assert rag["expert_ids"] - rag["sorted_ids"] >= 4 * T * cfg.k
+        assert rag["expert_ids"] - rag["sorted_ids"] < 4 * T * cfg.k + 256
+        assert pad["expert_ids"] - pad["sorted_ids"] >= 4 * cap
+        assert abi.moe_workspace_bytes(layer, T, r) < abi.moe_workspace_bytes(layer, T, p)
+        order = sorted(abi.WS_REGIONS, key=lambda n: rag[n])
+        nxt = {n: rag[order[i + 1]] if i + 1 < len(order) else abi.moe_workspace_bytes(layer, T, r)
+               for i, n in enumerate(order)}
+        assert nxt["block_start"] - rag["block_start"] >= 4 * (cap // p.block_m + 1)
+        bad = abi.Plan(*(p.as_tuple() + (0,) * (8 - len(p.as_tuple()))), 2)
+        with pytest.raises(abi.MoEError):
+            abi.moe_workspace_bytes(layer, T, bad)

@@ -71,10 +71,28 @@ def check_intermediates(c, T, plan, ws):
     np.testing.assert_allclose(w.reshape(T, cfg.k), rw, rtol=1e-5, atol=1e-7)
     ref = oracle.align(rids, T, cfg.k, cfg.E, plan.block_m)
     cap = abi.moe_align_capacity(T, cfg.k, cfg.E, plan.block_m)
-    srt = workspace_view(c.layer, T, plan, ws, "sorted_ids", torch.int32, cap).cpu().numpy()
-    assert (srt == ref["sorted_token_ids"]).all()
-    inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, T * cfg.k).cpu().numpy()
-    assert (inv == ref["inv_pos"]).all()
+    pairs = T * cfg.k
+    if plan.ragged:
+        # no padding: the oracle's stable order with its filler entries removed, each pair's
+        # row in that order, and the blocks cut at expert ends
+        want = ref["sorted_token_ids"][ref["sorted_token_ids"] < pairs]
+        srt = workspace_view(c.layer, T, plan, ws, "sorted_ids", torch.int32, pairs).cpu().numpy()
+        assert (srt == want).all()
+        inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, pairs).cpu().numpy()
+        assert (inv == np.argsort(want, kind="stable")).all()
+        nb = cap // plan.block_m
+        blk = workspace_view(c.layer, T, plan, ws, "block_start", torch.int32, nb + 1).cpu().numpy()
+        coff = np.concatenate([[0], np.cumsum(ref["expert_counts"])])
+        poff = np.concatenate([[0], np.cumsum((ref["expert_counts"] + plan.block_m - 1) // plan.block_m
+                                              * plan.block_m)])
+        for b in range(nb + 1):
+            e = ref["expert_ids"][b] if b < nb else -1
+            assert blk[b] == (coff[e] + b * plan.block_m - poff[e] if e >= 0 else pairs), b
+    else:
+        srt = workspace_view(c.layer, T, plan, ws, "sorted_ids", torch.int32, cap).cpu().numpy()
+        assert (srt == ref["sorted_token_ids"]).all()
+        inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, pairs).cpu().numpy()
+        assert (inv == ref["inv_pos"]).all()
     npp = workspace_view(c.layer, T, plan, ws, "num_post_pad", torch.int32, 1).cpu().numpy()
     assert npp[0] == ref["num_tokens_post_padded"][0]
     eids = workspace_view(c.layer, T, plan, ws, "expert_ids", torch.int32, cap // plan.block_m).cpu().numpy()
@@ -103,10 +121,14 @@ def check_sampled(name, T, tokens=None, plan=None):
     out, ws = c.gpu(T, plan)
     plan = plan or c.layer.plan(T)
     cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, plan.block_m)
-    srt = workspace_view(c.layer, T, plan, ws, "sorted_ids", torch.int32, cap).cpu().numpy()
+    srt = workspace_view(c.layer, T, plan, ws, "sorted_ids", torch.int32,
+                         T * c.cfg.k if plan.ragged else cap).cpu().numpy()
     npp = int(workspace_view(c.layer, T, plan, ws, "num_post_pad", torch.int32, 1).cpu()[0])
+    blk = None
+    if plan.ragged:
+        blk = workspace_view(c.layer, T, plan, ws, "block_start", torch.int32, cap // plan.block_m + 1).cpu().numpy()
     if tokens is None:
-        tokens = block_cover_tokens(srt, npp, plan.block_m, c.cfg.k, T * c.cfg.k, extra=(0, T - 1))
+        tokens = block_cover_tokens(srt, npp, plan.block_m, c.cfg.k, T * c.cfg.k, extra=(0, T - 1), blk_start=blk)
         # the split tails GEMM1 / GEMM2 took (rows from row0 on) are among the covered blocks
         inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, T * c.cfg.k).cpu().numpy()
         inv = inv.reshape(T, c.cfg.k)
@@ -429,6 +451,73 @@ def test_int4_outlier_channels(scale):
         assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
 
 
+# ---- the layout without padding (ragged plans) -------------------------------------------
+
+def ragged_of(plan):
+    return abi.Plan(*(plan.as_tuple() + (0,) * (8 - len(plan.as_tuple()))), 1) if not plan.ragged else plan
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 37), ("tiny", 100), ("tiny_top1", 37), ("fp8small", 40),
+                                    ("fp8small", 300), ("i4small", 37), ("i4small", 200)])
+def test_ragged_every_plan(name, T):
+    """Every plan of the layout without padding (the pairs expert by expert, no filler rows;
+    GEMM tiles cut at expert ends) on the small shapes of all three weight types: output
+    within tolerance, routing and the unpadded layout bit-exact."""
+    cfg = {"tiny_top1": TINY_TOP1, "fp8small": FP8_SMALL, "i4small": I4_SMALL}.get(name)
+    c = case(name) if cfg is None else small_case(cfg)
+    plans = valid_plans(c.layer, T, ragged=(1,))
+    assert len(plans) >= 8 and all(p.ragged for p in plans)
+    ref, _, _ = c.oracle(T)
+    for p in plans:
+        out, ws = c.gpu(T, p)
+        err = rel_l2(bf16_to_f64(out), ref)
+        assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+    for p in (plans[0], plans[len(plans) // 2], plans[-1]):
+        check_intermediates(c, T, p, c.gpu(T, p)[1])
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_ragged_split_tails(T):
+    """Both split tails and the K splits on grids capped so that whole tiles are followed by
+    a split tail, without padding: the tails' first rows are rows of the unpadded layout."""
+    c = small_case(TAIL_SMALL)
+    ref, _, _ = c.oracle(T)
+    n = 0
+    for g in (24, 48):
+        for p in valid_plans(c.layer, T, split1=(1,), splits=(1, 2), tails=(0, 4), max_workgroups=g, tails1=(0, 4),
+                             ragged=(1,))[::2]:
+            out, ws = c.gpu(T, p)
+            err = rel_l2(bf16_to_f64(out), ref)
+            assert err <= TOL[c.cfg.wdtype], "plan %s rel-L2 %.3e" % (p.as_tuple(), err)
+            n += 1
+    assert n >= 10
+
+
+@pytest.mark.parametrize("name,T,whole", [("mixtral", 4096, False), ("mixtral", 512, False), ("scout", 8192, False),
+                                          ("qwen2", 512, True), ("qwen2", 4096, False), ("deepseek", 512, False),
+                                          ("mixtral", 8, True)])
+def test_ragged_full_size(name, T, whole):
+    """The full-size layers under their default plans made unpadded: the whole output (or one
+    token per row block), routing and the unpadded layout bit-exact."""
+    c = case(name)
+    p = ragged_of(c.layer.plan(T))
+    if whole:
+        check_full(name, T, p)
+    else:
+        check_sampled(name, T, plan=p)
+
+
+def test_ragged_equals_padded_bitwise():
+    """A row's products do not depend on where it sits: with the same tiles and splits, the
+    unpadded layout gives the padded layout's output bit for bit."""
+    c = case("mixtral")
+    for T in (64, 1024):
+        p = c.layer.plan(T)
+        a, _ = c.gpu(T, p)
+        b, _ = c.gpu(T, ragged_of(p))
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), T
+
+
 # ---- properties ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,T", [("mixtral", 1), ("qwen2", 3), ("deepseek", 2), ("scout", 5)])
@@ -470,12 +559,14 @@ def test_split_k_on_and_off_agree():
     assert rel_l2(bf16_to_f64(a), bf16_to_f64(b)) < 5e-3
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 37), ("mixtral", 8), ("qwen2", 8)])
-def test_graph_replay_matches_eager(name, T):
+@pytest.mark.parametrize("name,T,ragged", [("tiny", 37, 0), ("mixtral", 8, 0), ("qwen2", 8, 0), ("qwen2", 300, 1)])
+def test_graph_replay_matches_eager(name, T, ragged):
     c = case(name)
     x, lg = c.inputs(T)
     x, lg = x.cuda(), lg.cuda()
     plan = c.layer.plan(T)
+    if ragged:
+        plan = ragged_of(plan)
     ws = c.layer.workspace(T, plan)
     out = torch.empty((T, c.cfg.H), dtype=torch.bfloat16, device="cuda")
     eager = c.layer.forward(x, lg, out=torch.empty_like(out), workspace=ws, plan=plan).clone()
@@ -518,9 +609,9 @@ def test_small_batch_prologue(name, T, expect):
     say("profiled forward", name, "T=%d" % T)
     stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), out, ws, ev, plan)
     torch.cuda.synchronize()
-    if plan.split_k1 > 1:   # a K-split GEMM1 is followed by its finishing pass
+    if plan.split_k1 > 1 or plan.split_tail1 > 1:   # a K-split GEMM1 is followed by its finishing pass
         expect = expect[:expect.index("gemm1") + 1] + ["gemm1_finish"] + expect[expect.index("gemm1") + 1:]
-        if c.cfg.wdtype == synth.WDT_FP8 and T * c.cfg.k * c.cfg.I * plan.split_k1 <= 32768:
+        if c.cfg.wdtype == synth.WDT_FP8 and plan.split_k1 > 1 and T * c.cfg.k * c.cfg.I * plan.split_k1 <= 32768:
             expect.remove("h_quant")   # which also quantises h in a tiny batch
     assert stages == expect
     tokens = list(range(T)) if T <= 16 else [0, 1, T // 2, T - 1]   # the oracle token by token
@@ -568,7 +659,7 @@ def test_profiled_forward_records_every_stage():
     stages = abi.moe_forward_profiled(c.layer.struct, T, x.cuda(), lg.cuda(), out, ws, ev)
     torch.cuda.synchronize()
     expect = ["route", "align", "act_quant", "gemm1", "h_quant", "gemm2", "reduce"]
-    if c.layer.plan(T).split_k1 > 1:
+    if c.layer.plan(T).split_k1 > 1 or c.layer.plan(T).split_tail1 > 1:
         expect.insert(4, "gemm1_finish")
     assert stages == expect
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(stages))]

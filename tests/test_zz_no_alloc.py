@@ -21,7 +21,7 @@ def _layer(cfg):
     return device_layer(cfg, w, synth.correction_bias(cfg))
 
 
-@pytest.mark.parametrize("name,Ts", [("mixtral", (512, 8)), ("qwen2", (256, 5)), ("deepseek", (200, 3)),
+@pytest.mark.parametrize("name,Ts", [("mixtral", (256, 8)), ("qwen2", (256, 5)), ("deepseek", (200, 3)),
                                      ("scout", (256, 1))])
 def test_static_matches_allocating_forward(name, Ts):
     cfg = synth.CONFIGS[name]
