@@ -29,13 +29,23 @@ namespace {
 
 enum { WT_BF16 = 0, WT_FP8 = 2, WT_INT4 = 3 };
 
-template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_, int BX_ = 0>
+template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_, int BX_ = 0, int IL_ = 0>
 struct PCfg {
     static constexpr int BM = BM_, BN = BN_, KS = KS_, ST = ST_, WM = WM_, WN = WN_;
     // BX = 1 (-1): B (A) gets one stage more than the other operand, each operand in a ring
     // of its own, so its loads run two K steps ahead while the other's run one (two
     // stages; 160 KB of LDS for a 256x256 tile)
     static constexpr int BX = BX_;
+    // IL = 1 (bf16, 16x16 MFMAs, every buffer filled ahead): each wave holds the fragments of
+    // two 32-K substeps in registers and reads the next substep's while the MFMAs of the
+    // current one run (interleaved by the scheduler); the stage barrier sits between a
+    // stage's last two substeps, so the next stage's first fragments are read while that
+    // stage's last MFMAs run.  Built for 8 waves of 64x64 each (a 128x256 or 256x128 tile):
+    // at two waves per SIMD a lane has 256 registers, room for two fragment sets beside the
+    // accumulators.
+    static constexpr int IL = IL_;
+    static_assert(!IL || (WT == WT_BF16 && MS_ == 16 && BX == 0 && SB_ == 128 && KS == 1),
+                  "interleaved fragments: bf16 16x16 tiles of one 128-byte slab per stage");
     static constexpr int DA = ST + (BX < 0), DB = ST + (BX > 0);   // ring depths
     static constexpr int MS = MS_;                            // MFMA output tile: 16x16 or 32x32
     static constexpr int SB = SB_;                            // bytes of K per row and slab: 128 or 64
@@ -210,151 +220,224 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
 #pragma unroll
                 for (int r = 0; r < NR; r++) acc[i][j][r] = 0.f;
 
-        // every wave is done with the previous tile's buffers before they are refilled
-        block_barrier();
-#pragma unroll
-        for (int p = 0; p < C::ST - 1; p++)
-            if (p < nku) issue(p, true, true);
-        if constexpr (C::BX != 0)   // the operand that runs ahead: its step 1 too
-            if (1 < nku) issue(1, C::BX < 0, C::BX > 0);
-
-        for (int kt = 0; kt < nku; kt++) {
-            if constexpr (C::BX != 0) {
-                // issued after this step's last operand: the ahead operand's step kt + 1, if
-                // it exists (two stages)
-                if (kt + 1 < nku) wait_vmcnt<C::L_AHEAD>(); else wait_vmcnt<0>();
-            } else {
-                wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nku - 1 - kt));
-            }
+        if constexpr (C::IL) {
+            // every buffer filled ahead; a stage's buffer is refilled after the barrier that
+            // follows every wave's last read of it
+            constexpr int NK = C::SB / 64;                  // 32-K substeps per stage (2)
             block_barrier();
-            // the operand one step ahead, then (ahead rings) the other two steps ahead
-            if (kt + C::ST - 1 < nku) issue(kt + C::ST - 1, C::BX >= 0, C::BX <= 0);
-            if constexpr (C::BX != 0)
-                if (kt + 2 < nku) issue(kt + 2, C::BX < 0, C::BX > 0);
-            const char *sa = smem + C::a_off(kt), *sb = smem + C::b_off(kt);
-            if (wave_rows) {   // a wave whose rows are all padding only loads and keeps step
-            // Fragments of step k + 1 can be read while the MFMAs of step k run (see DB below).
-            if constexpr (WT == WT_BF16 && C::MS == 32) {
-                // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step.
-                // Double-buffered: the reads of step k + 1 are issued before the MFMAs of
-                // step k (scheduling barriers keep that order).
-                constexpr int KPS = C::SB / 32;                 // 16-K steps per slab
-                constexpr int NK = C::KS * KPS;
-                bf16x8 af[2][C::FM], bfr[2][C::FN];
-                auto load = [&](int k, int buf) {
-                    const int sl = k / KPS, ci = (k % KPS) * 2 + (lane >> 5);
 #pragma unroll
-                    for (int fm = 0; fm < C::FM; fm++) {
-                        const int r = wm * C::TM + fm * 32 + (lane & 31);
-                        af[buf][fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
-                    }
+            for (int p = 0; p < C::ST; p++)
+                if (p < nku) issue(p, true, true);
+            bf16x8 af[2][C::FM], bfr[2][C::FN];
+            // fragments of substep q of stage k into set buf: lane l holds row l % 16 and K
+            // elements 8 (l / 16) .. +7 of the substep
+            auto frag_load = [&](int k, int q, int buf) {
+                const char *sa = smem + C::a_off(k), *sb = smem + C::b_off(k);
+                const int ci = q * 4 + (lane >> 4);
 #pragma unroll
-                    for (int fn = 0; fn < C::FN; fn++) {
-                        const int r = wn * C::TN + fn * 32 + (lane & 31);
-                        bfr[buf][fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
-                    }
-                };
-                load(0, 0);
+                for (int fm = 0; fm < C::FM; fm++)
+                    af[buf][fm] = *(const bf16x8 *)(sa + slab_off<C::SB>(wm * C::TM + fm * 16 + (lane & 15), ci));
 #pragma unroll
-                for (int k = 0; k < NK; k++) {
-                    if (k + 1 < NK) load(k + 1, (k + 1) & 1);
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int fn = 0; fn < C::FN; fn++)
+                    bfr[buf][fn] = *(const bf16x8 *)(sb + slab_off<C::SB>(wn * C::TN + fn * 16 + (lane & 15), ci));
+            };
+            auto mma = [&](int buf) {
 #pragma unroll
-                    for (int fm = 0; fm < C::FM; fm++)
+                for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
-                        for (int fn = 0; fn < C::FN; fn++)
-                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k & 1][fm], bfr[k & 1][fn],
-                                                                                 acc[fm][fn], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int fn = 0; fn < C::FN; fn++)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[buf][fm], bfr[buf][fn], acc[fm][fn], 0, 0, 0);
+            };
+            // the reads issued above go between the MFMAs: one read after every few MFMAs
+            auto interleave = [&]() {
+                constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN, PER = NM / NR;
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
                 }
-            } else if constexpr (WT == WT_BF16) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
+            };
+            // stage 0 landed (later stages may still be in flight)
+            wait_stages<C::LPW, C::ST - 1>(min(C::ST - 1, nku - 1));
+            block_barrier();
+            if (wave_rows) frag_load(0, 0, 0);
+            for (int kt = 0; kt < nku; kt++) {
 #pragma unroll
-                for (int sl = 0; sl < C::KS; sl++)
-#pragma unroll
-                    for (int kk = 0; kk < C::SB / 64; kk++) {
-                        // 16x16x32: lane l holds row l%16, K elements 8*(l/16) .. +7 of the step
-                        const int ci = kk * 4 + (lane >> 4);
-                        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
+                for (int q = 0; q < NK; q++) {
+                    const int cur = q & 1;
+                    if (q + 1 < NK) {
+                        if (wave_rows) {
+                            frag_load(kt, q + 1, cur ^ 1);
+                            mma(cur);
+                            interleave();
+                        }
+                    } else {
+                        if (kt + 1 < nku) {
+                            // this wave's reads of stage kt done, stage kt + 1 landed; after the
+                            // barrier no wave reads stage kt's buffer any more: refill it
+                            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                            wait_stages<C::LPW, C::ST - 1>(min(C::ST - 2, nku - 2 - kt));
+                            block_barrier();
+                            if (kt + C::ST < nku) issue(kt + C::ST, true, true);
+                            if (wave_rows) {
+                                frag_load(kt + 1, 0, cur ^ 1);
+                                mma(cur);
+                                interleave();
+                            }
+                        } else if (wave_rows) {
+                            mma(cur);
+                        }
+                    }
+                }
+            }
+        } else {
+            // every wave is done with the previous tile's buffers before they are refilled
+            block_barrier();
+    #pragma unroll
+            for (int p = 0; p < C::ST - 1; p++)
+                if (p < nku) issue(p, true, true);
+            if constexpr (C::BX != 0)   // the operand that runs ahead: its step 1 too
+                if (1 < nku) issue(1, C::BX < 0, C::BX > 0);
+
+            for (int kt = 0; kt < nku; kt++) {
+                if constexpr (C::BX != 0) {
+                    // issued after this step's last operand: the ahead operand's step kt + 1, if
+                    // it exists (two stages)
+                    if (kt + 1 < nku) wait_vmcnt<C::L_AHEAD>(); else wait_vmcnt<0>();
+                } else {
+                    wait_stages<C::LPW, C::ST - 2>(min(C::ST - 2, nku - 1 - kt));
+                }
+                block_barrier();
+                // the operand one step ahead, then (ahead rings) the other two steps ahead
+                if (kt + C::ST - 1 < nku) issue(kt + C::ST - 1, C::BX >= 0, C::BX <= 0);
+                if constexpr (C::BX != 0)
+                    if (kt + 2 < nku) issue(kt + 2, C::BX < 0, C::BX > 0);
+                const char *sa = smem + C::a_off(kt), *sb = smem + C::b_off(kt);
+                if (wave_rows) {   // a wave whose rows are all padding only loads and keeps step
+                // Fragments of step k + 1 can be read while the MFMAs of step k run (see DB below).
+                if constexpr (WT == WT_BF16 && C::MS == 32) {
+                    // 32x32x16: lane l holds row l%32, K elements 8*(l/32) .. +7 of the step.
+                    // Double-buffered: the reads of step k + 1 are issued before the MFMAs of
+                    // step k (scheduling barriers keep that order).
+                    constexpr int KPS = C::SB / 32;                 // 16-K steps per slab
+                    constexpr int NK = C::KS * KPS;
+                    bf16x8 af[2][C::FM], bfr[2][C::FN];
+                    auto load = [&](int k, int buf) {
+                        const int sl = k / KPS, ci = (k % KPS) * 2 + (lane >> 5);
+    #pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++) {
+                            const int r = wm * C::TM + fm * 32 + (lane & 31);
+                            af[buf][fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
+                        }
+    #pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++) {
+                            const int r = wn * C::TN + fn * 32 + (lane & 31);
+                            bfr[buf][fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
+                        }
+                    };
+                    load(0, 0);
+    #pragma unroll
+                    for (int k = 0; k < NK; k++) {
+                        if (k + 1 < NK) load(k + 1, (k + 1) & 1);
+                        __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++)
+    #pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++)
+                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k & 1][fm], bfr[k & 1][fn],
+                                                                                     acc[fm][fn], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else if constexpr (WT == WT_BF16) {
+    #pragma unroll
+                    for (int sl = 0; sl < C::KS; sl++)
+    #pragma unroll
+                        for (int kk = 0; kk < C::SB / 64; kk++) {
+                            // 16x16x32: lane l holds row l%16, K elements 8*(l/16) .. +7 of the step
+                            const int ci = kk * 4 + (lane >> 4);
+                            bf16x8 af[C::FM], bfr[C::FN];
+    #pragma unroll
+                            for (int fm = 0; fm < C::FM; fm++) {
+                                const int r = wm * C::TM + fm * 16 + (lane & 15);
+                                af[fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
+                            }
+    #pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++) {
+                                const int r = wn * C::TN + fn * 16 + (lane & 15);
+                                bfr[fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
+                            }
+    #pragma unroll
+                            for (int fm = 0; fm < C::FM; fm++)
+    #pragma unroll
+                                for (int fn = 0; fn < C::FN; fn++)
+                                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+                        }
+                } else if constexpr (C::NW >= 16) {
+                    // fp8 with 16 waves (128 registers a lane): all A fragments of the slab, then
+                    // one B fragment at a time, so that fragments take 8 (FM + 1) registers
+                    const int c0 = 2 * (lane >> 4);
+    #pragma unroll
+                    for (int sl = 0; sl < C::KS; sl++) {
+                        i32x8 af[C::FM];
+    #pragma unroll
                         for (int fm = 0; fm < C::FM; fm++) {
                             const int r = wm * C::TM + fm * 16 + (lane & 15);
-                            af[fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
+                            const char *slab = sa + sl * C::BM * 128;
+                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                            af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                         }
-#pragma unroll
+    #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++) {
                             const int r = wn * C::TN + fn * 16 + (lane & 15);
-                            bfr[fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
+                            const char *slab = sb + sl * C::BN * 128;
+                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                            const i32x8 b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    #pragma unroll
+                            for (int fm = 0; fm < C::FM; fm++)
+                                acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], b, acc[fm][fn], 0, 0, 0,
+                                                                                            127, 0, 127);
+                            __builtin_amdgcn_sched_barrier(0);   // keep the B loads from being hoisted together
                         }
-#pragma unroll
+                    }
+                } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
+                    const int c0 = 2 * (lane >> 4);
+                    i32x8 af[2][C::FM], bfr[2][C::FN];
+                    auto load = [&](int sl, int buf) {
+    #pragma unroll
+                        for (int fm = 0; fm < C::FM; fm++) {
+                            const int r = wm * C::TM + fm * 16 + (lane & 15);
+                            const char *slab = sa + sl * C::BM * 128;
+                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                            af[buf][fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        }
+    #pragma unroll
+                        for (int fn = 0; fn < C::FN; fn++) {
+                            const int r = wn * C::TN + fn * 16 + (lane & 15);
+                            const char *slab = sb + sl * C::BN * 128;
+                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                            bfr[buf][fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        }
+                    };
+                    load(0, 0);
+    #pragma unroll
+                    for (int sl = 0; sl < C::KS; sl++) {
+                        if (sl + 1 < C::KS) load(sl + 1, (sl + 1) & 1);
+    #pragma unroll
                         for (int fm = 0; fm < C::FM; fm++)
-#pragma unroll
+    #pragma unroll
                             for (int fn = 0; fn < C::FN; fn++)
-                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-                    }
-            } else if constexpr (C::NW >= 16) {
-                // fp8 with 16 waves (128 registers a lane): all A fragments of the slab, then
-                // one B fragment at a time, so that fragments take 8 (FM + 1) registers
-                const int c0 = 2 * (lane >> 4);
-#pragma unroll
-                for (int sl = 0; sl < C::KS; sl++) {
-                    i32x8 af[C::FM];
-#pragma unroll
-                    for (int fm = 0; fm < C::FM; fm++) {
-                        const int r = wm * C::TM + fm * 16 + (lane & 15);
-                        const char *slab = sa + sl * C::BM * 128;
-                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
-                        af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    }
-#pragma unroll
-                    for (int fn = 0; fn < C::FN; fn++) {
-                        const int r = wn * C::TN + fn * 16 + (lane & 15);
-                        const char *slab = sb + sl * C::BN * 128;
-                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
-                        const i32x8 b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-                        for (int fm = 0; fm < C::FM; fm++)
-                            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], b, acc[fm][fn], 0, 0, 0,
-                                                                                        127, 0, 127);
-                        __builtin_amdgcn_sched_barrier(0);   // keep the B loads from being hoisted together
+                                acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    af[sl & 1][fm], bfr[sl & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
                     }
                 }
-            } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
-                const int c0 = 2 * (lane >> 4);
-                i32x8 af[2][C::FM], bfr[2][C::FN];
-                auto load = [&](int sl, int buf) {
-#pragma unroll
-                    for (int fm = 0; fm < C::FM; fm++) {
-                        const int r = wm * C::TM + fm * 16 + (lane & 15);
-                        const char *slab = sa + sl * C::BM * 128;
-                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
-                        af[buf][fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    }
-#pragma unroll
-                    for (int fn = 0; fn < C::FN; fn++) {
-                        const int r = wn * C::TN + fn * 16 + (lane & 15);
-                        const char *slab = sb + sl * C::BN * 128;
-                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
-                        bfr[buf][fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    }
-                };
-                load(0, 0);
-#pragma unroll
-                for (int sl = 0; sl < C::KS; sl++) {
-                    if (sl + 1 < C::KS) load(sl + 1, (sl + 1) & 1);
-#pragma unroll
-                    for (int fm = 0; fm < C::FM; fm++)
-#pragma unroll
-                        for (int fn = 0; fn < C::FN; fn++)
-                            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                af[sl & 1][fm], bfr[sl & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
                 }
-            }
             }
         }
 
@@ -501,6 +584,13 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
 //        id  BM   BN  KS ST WM WN MS  SB  BX
 #define PIPE_BF16_TILES_BX(X) X(38, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(39, 256, 256, 1, 2, 4, 4, 16, 128, -1)
 #define PIPE_FP8_TILES_BX(X) X(17, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(18, 256, 256, 1, 2, 4, 4, 16, 128, -1)
+// 8-wave tiles reading the next 32-K substep's fragments while the current MFMAs run (IL)
+//        id  BM   BN  KS ST WM WN MS  SB
+// (twins of tiles 22 and 23; a 128x64 wave tile with two fragment sets exceeds the 256
+// registers a lane has at two waves per SIMD)
+#define PIPE_BF16_TILES_IL(X)           \
+    X(42, 128, 256, 1, 3, 2, 4, 16, 128)     \
+    X(43, 256, 128, 1, 3, 4, 2, 16, 128)
 
 template <class C, int WT, int KIND, bool PARTIAL>
 hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
@@ -553,7 +643,7 @@ bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
 #define PI_FP8(id, bm, bn, ks, st, wm, wn, ms, sb) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
 #define PI_BF16_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
 #define PI_FP8_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
-    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) PIPE_BF16_TILES_BX(PI_BF16_BX) }
+    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) PIPE_BF16_TILES_BX(PI_BF16_BX) PIPE_BF16_TILES_IL(PI_BF16) }
     if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) PIPE_FP8_TILES_BX(PI_FP8_BX) }
     if (wdtype == WT_INT4) return i4_tile_info(tile, info);
     return false;
@@ -569,7 +659,9 @@ hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, c
     if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms, sb, bx>, WT>(kind, partial, a, max_tiles, s);
 #define PL_BF16_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PLAUNCH_BX(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb, bx)
 #define PL_FP8_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PLAUNCH_BX(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb, bx)
-    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) PIPE_BF16_TILES_BX(PL_BF16_BX) }
+#define PL_BF16_IL(id, bm, bn, ks, st, wm, wn, ms, sb) \
+    if (tile == id) return launch_kind<PCfg<WT_BF16, bm, bn, ks, st, wm, wn, ms, sb, 0, 1>, WT_BF16>(kind, partial, a, max_tiles, s);
+    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) PIPE_BF16_TILES_BX(PL_BF16_BX) PIPE_BF16_TILES_IL(PL_BF16_IL) }
     if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) PIPE_FP8_TILES_BX(PL_FP8_BX) }
     if (wdtype == WT_INT4) return launch_gemm_i4(tile, kind, partial, a, max_tiles, s);
     return hipErrorInvalidValue;

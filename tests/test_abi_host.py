@@ -350,8 +350,9 @@ def test_ragged_plan_layout():
     for name, T in (("mixtral", 512), ("qwen2", 300), ("deepseek", 64), ("scout", 1000)):
         cfg = synth.CONFIGS[name]
         layer = fake_layer(cfg)
-        p = abi.moe_default_plan(layer, T)
-        r = abi.Plan(*(p.as_tuple() + (0,) * (8 - len(p.as_tuple()))), 1)
+        head = (abi.moe_default_plan(layer, T).as_tuple() + (0,) * 9)[:8]
+        p, r = abi.Plan(*head, 0), abi.Plan(*head, 1)       # the same plan padded and not
+        assert "ragged=0" in abi.moe_plan_describe(layer, T, p)
         assert "ragged=1" in abi.moe_plan_describe(layer, T, r)
         pad, rag = abi.moe_workspace_offsets(layer, T, p), abi.moe_workspace_offsets(layer, T, r)
         cap = abi.moe_align_capacity(T, cfg.k, cfg.E, p.block_m)
@@ -363,6 +364,6 @@ def test_ragged_plan_layout():
         nxt = {n: rag[order[i + 1]] if i + 1 < len(order) else abi.moe_workspace_bytes(layer, T, r)
                for i, n in enumerate(order)}
         assert nxt["block_start"] - rag["block_start"] >= 4 * (cap // p.block_m + 1)
-        bad = abi.Plan(*(p.as_tuple() + (0,) * (8 - len(p.as_tuple()))), 2)
+        bad = abi.Plan(*head, 2)
         with pytest.raises(abi.MoEError):
             abi.moe_workspace_bytes(layer, T, bad)

@@ -312,7 +312,8 @@ def test_qwen2_fp8_activation_codes_exact(T):
 
 
 @pytest.mark.parametrize("T", [16, 512])
-def test_qwen2_fp8_intermediate_codes(T):
+@pytest.mark.parametrize("ragged", [0, 1])
+def test_qwen2_fp8_intermediate_codes(T, ragged):
     """The intermediate h is quantised from fp32 on both sides (T=16: the one-workgroup
     finishing pass quantises it; T=512: GEMM1's epilogue and the quantisation kernel).
     - The GPU's codes are exactly the oracle's codec applied to the GPU's own fp32 h and
@@ -326,18 +327,19 @@ def test_qwen2_fp8_intermediate_codes(T):
       rounding midpoint: each differing code is one step from the oracle's, and the
       midpoint between them lies between the two scaled values."""
     c = case("qwen2")
-    out, ws = c.gpu(T)
-    plan = c.layer.plan(T)
+    plan = abi.Plan(*(c.layer.plan(T).as_tuple() + (0,) * 9)[:8], ragged)   # the default, in either layout
+    out, ws = c.gpu(T, plan)
     x, lg = c.inputs(T)
     ids, _ = oracle_route(c.cfg, bits(lg), c.bias)
     ref_h, ref_codes, ref_sc = oracle.fp8_intermediate(c.W, bits(x), ids)
     sc = workspace_view(c.layer, T, plan, ws, "scalars", torch.float32, 4).cpu().numpy()
     amax_gpu = np.float32(sc[1])                       # word 1: |h| max as fp32 bits
     assert abs(sc[3] / ref_sc[1] - 1) < 2e-4
-    cap = abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, plan.block_m)
+    # h's rows: the padded capacity, or exactly the T*k pairs without padding
+    rows = T * c.cfg.k if plan.ragged else abi.moe_align_capacity(T, c.cfg.k, c.cfg.E, plan.block_m)
     inv = workspace_view(c.layer, T, plan, ws, "inv_pos", torch.int32, T * c.cfg.k).cpu().numpy()
-    hq = workspace_view(c.layer, T, plan, ws, "h_q", torch.uint8, cap * c.cfg.I).cpu().numpy().reshape(cap, -1)[inv]
-    h = workspace_view(c.layer, T, plan, ws, "h", torch.float32, cap * c.cfg.I).cpu().numpy().reshape(cap, -1)[inv]
+    hq = workspace_view(c.layer, T, plan, ws, "h_q", torch.uint8, rows * c.cfg.I).cpu().numpy().reshape(rows, -1)[inv]
+    h = workspace_view(c.layer, T, plan, ws, "h", torch.float32, rows * c.cfg.I).cpu().numpy().reshape(rows, -1)[inv]
     # the GPU's own quantisation, exactly
     assert np.float32(np.abs(h).max()) == amax_gpu
     assert sc[3] == np.float32(amax_gpu / np.float32(448.0))
