@@ -294,28 +294,46 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
         // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 fragment ----
         float scale = 1.0f;
         if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
+        // the lane's rows, q = fm * 4 + i; their pairs (and GEMM2's weights) are read and
+        // pinned before the stores (see pin)
+        constexpr int EQ = C::FM * 4;
+        auto epi_row = [&](int q) { return wm * C::TM + (q / 4) * 16 + 4 * (lane >> 4) + q % 4; };
         if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
             // split K: this split's gate and up sums in fp32 (the finishing pass adds the
             // splits in order and applies SiLU * up); filler rows are left out
+            int pr[EQ];
 #pragma unroll
-            for (int fm = 0; fm < C::FM; fm++)
+            for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int lr = wm * C::TM + fm * 16 + 4 * (lane >> 4) + i, row = row0 + lr;
-                    if (block_pair(a, br, lr) >= a.pairs) continue;
-                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+            for (int q = 0; q < EQ; q++) pin(pr[q]);
 #pragma unroll
-                    for (int f = 0; f < C::FN / 2; f++) {
-                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
-                        P[col] = acc[fm][f][i] * scale;
-                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
-                    }
+            for (int q = 0; q < EQ; q++) {
+                const int fm = q / 4, i = q % 4, row = row0 + epi_row(q);
+                if (pr[q] >= a.pairs) continue;
+                float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                for (int f = 0; f < C::FN / 2; f++) {
+                    const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
+                    P[col] = acc[fm][f][i] * scale;
+                    P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
                 }
+            }
         } else if constexpr (KIND == GEMM_GATE_UP) {
             float amax = 0.0f;
             uint32_t seen = 0;   // the h maximum so far, read before the stores (see amax_peek)
             if constexpr (WT == WT_FP8)
                 if (lane == 0 && a.amax_out) seen = amax_peek(a.amax_out);
+            bool valid[EQ];   // |h| of filler rows stays out of the maximum (fp8 only)
+            if constexpr (WT == WT_FP8) {
+                int pr[EQ];
+#pragma unroll
+                for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
+#pragma unroll
+                for (int q = 0; q < EQ; q++) {
+                    pin(pr[q]);
+                    valid[q] = pr[q] < a.pairs;
+                }
+            }
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
@@ -324,12 +342,12 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                     for (int i = 0; i < 4; i++) {
                         const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
                         const float hv = silu(g) * u;
-                        const int lr = wm * C::TM + fm * 16 + 4 * (lane >> 4) + i, row = row0 + lr;
+                        const int lr = epi_row(fm * 4 + i), row = row0 + lr;
                         if (lr >= br.n) continue;   // without padding: the next block's row
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + (lane & 15);
                         if constexpr (WT == WT_FP8) {   // fp32: its E4M3 code is decided in fp32
                             ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
-                            if (block_pair(a, br, lr) < a.pairs) amax = fmaxf(amax, fabsf(hv));   // valid rows only
+                            if (valid[fm * 4 + i]) amax = fmaxf(amax, fabsf(hv));   // valid rows only
                         } else {
                             ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
                         }
@@ -340,14 +358,24 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                 if (lane == 0 && a.amax_out) amax_raise(a.amax_out, seen, amax);
             }
         } else {
+            int pr[EQ];
+            float wr[EQ];
+#pragma unroll
+            for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
+#pragma unroll
+            for (int q = 0; q < EQ; q++) pin(pr[q]);
+#pragma unroll
+            for (int q = 0; q < EQ; q++) wr[q] = a.topk_w[pr[q] < a.pairs ? pr[q] : 0] * scale;   // filler: pair 0's
+#pragma unroll
+            for (int q = 0; q < EQ; q++) pin(wr[q]);
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int lr = wm * C::TM + fm * 16 + 4 * (lane >> 4) + i, row = row0 + lr;
-                    const int p = block_pair(a, br, lr);
+                    const int lr = epi_row(fm * 4 + i), row = row0 + lr;
+                    const int p = pr[fm * 4 + i];
                     if (p >= a.pairs) continue;   // filler row: never read back
-                    const float w = a.topk_w[p] * scale;
+                    const float w = wr[fm * 4 + i];
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const int col = nt * C::BN + wn * C::TN + fn * 16 + (lane & 15);

@@ -264,24 +264,31 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
         // ---- epilogue: accumulator value i of fragment (fm, fn) is row frag_row(lane, i),
         //      column lane % 16 of that fragment ----
         const int lcol = lane & 15;
+        // the lane's rows, q = fm * 4 + i; their pairs (and GEMM2's weights) are read and
+        // pinned before the stores (see pin)
+        constexpr int EQ = C::FM * 4;
+        auto epi_row = [&](int q) { return wm * C::TM + (q / 4) * 16 + frag_row<16>(lane, q % 4); };
         if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
             // split K: this split's gate and up sums in fp32, natural column order (the
             // finishing pass adds the splits, applies SiLU * up and permutes); filler rows
             // are left out
+            int pr[EQ];
 #pragma unroll
-            for (int fm = 0; fm < C::FM; fm++)
+            for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int lr = wm * C::TM + fm * 16 + frag_row<16>(lane, i), row = row0 + lr;
-                    if (block_pair(a, br, lr) >= a.pairs) continue;
-                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+            for (int q = 0; q < EQ; q++) pin(pr[q]);
 #pragma unroll
-                    for (int f = 0; f < C::FN / 2; f++) {
-                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + lcol;
-                        P[col] = acc[fm][f][i];
-                        P[a.I + col] = acc[fm][f + C::FN / 2][i];
-                    }
+            for (int q = 0; q < EQ; q++) {
+                const int fm = q / 4, i = q % 4, row = row0 + epi_row(q);
+                if (pr[q] >= a.pairs) continue;
+                float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                for (int f = 0; f < C::FN / 2; f++) {
+                    const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * 16 + lcol;
+                    P[col] = acc[fm][f][i];
+                    P[a.I + col] = acc[fm][f + C::FN / 2][i];
                 }
+            }
         } else if constexpr (KIND == GEMM_GATE_UP) {
             // h = SiLU(gate) * up in bf16, columns in the permuted order GEMM2's A expects
 #pragma unroll
@@ -298,14 +305,24 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                     }
                 }
         } else {
+            int pr[EQ];
+            float wr[EQ];
+#pragma unroll
+            for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
+#pragma unroll
+            for (int q = 0; q < EQ; q++) pin(pr[q]);
+#pragma unroll
+            for (int q = 0; q < EQ; q++) wr[q] = a.topk_w[pr[q] < a.pairs ? pr[q] : 0];   // filler: pair 0's
+#pragma unroll
+            for (int q = 0; q < EQ; q++) pin(wr[q]);
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int lr = wm * C::TM + fm * 16 + frag_row<16>(lane, i), row = row0 + lr;
-                    const int p = block_pair(a, br, lr);
+                    const int lr = epi_row(fm * 4 + i), row = row0 + lr;
+                    const int p = pr[fm * 4 + i];
                     if (p >= a.pairs) continue;   // filler row: never read back
-                    const float w = a.topk_w[p];
+                    const float w = wr[fm * 4 + i];
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const int col = nt * C::BN + wn * C::TN + fn * 16 + lcol;

@@ -68,6 +68,9 @@ struct PCfg {
     static_assert(BX == 0 || ((BX == 1 || BX == -1) && ST == 2 && A_LOADS % NW == 0),
                   "the one-operand-ahead rings are built for two stages with loads split evenly per wave");
     static constexpr int LDS_BYTES = BX ? DA * A_STAGE + DB * B_STAGE : ST * STAGE;
+    // 4-wave tiles of at most 80 KB of LDS are built for two workgroups per CU: at most 256
+    // registers a lane (two waves per SIMD)
+    static constexpr int MINW = NW == 4 && LDS_BYTES <= 80 * 1024 ? 2 : 1;
     // LDS offsets of step k's A and B
     static __device__ __forceinline__ int a_off(int k) { return BX ? (k % DA) * A_STAGE : (k % ST) * STAGE; }
     static __device__ __forceinline__ int b_off(int k) {
@@ -79,7 +82,7 @@ struct PCfg {
 };
 
 template <class C, int WT, int KIND, bool PARTIAL>
-__global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
+__global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -349,6 +352,38 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                                                                                      acc[fm][fn], 0, 0, 0);
                         __builtin_amdgcn_sched_barrier(0);
                     }
+                } else if constexpr (WT == WT_BF16 && C::NW >= 16) {
+                    // 16 waves (128 registers a lane): all FM A fragments do not fit beside the
+                    // accumulators, so A is read two fragments deep: A(fm + 1) is read from LDS
+                    // before the MFMAs of A(fm) are issued, and its latency is spent under them
+                    // (scheduling groups keep that order; the MFMA sequence is unchanged)
+    #pragma unroll
+                    for (int sl = 0; sl < C::KS; sl++)
+    #pragma unroll
+                        for (int kk = 0; kk < C::SB / 64; kk++) {
+                            const int ci = kk * 4 + (lane >> 4);
+                            const char *pa = sa + sl * C::BM * C::SB, *pb = sb + sl * C::BN * C::SB;
+                            bf16x8 af[2], bfr[C::FN];
+    #pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++)
+                                bfr[fn] = *(const bf16x8 *)(pb + slab_off<C::SB>(wn * C::TN + fn * 16 + (lane & 15), ci));
+                            af[0] = *(const bf16x8 *)(pa + slab_off<C::SB>(wm * C::TM + (lane & 15), ci));
+    #pragma unroll
+                            for (int fm = 0; fm < C::FM; fm++) {
+                                if (fm + 1 < C::FM)
+                                    af[(fm + 1) & 1] = *(const bf16x8 *)(pa + slab_off<C::SB>(
+                                                                            wm * C::TM + (fm + 1) * 16 + (lane & 15), ci));
+    #pragma unroll
+                                for (int fn = 0; fn < C::FN; fn++)
+                                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm & 1], bfr[fn], acc[fm][fn], 0, 0, 0);
+                            }
+                            __builtin_amdgcn_sched_group_barrier(0x100, C::FN + 1, 0);   // B, A(0)
+    #pragma unroll
+                            for (int fm = 0; fm < C::FM; fm++) {
+                                if (fm + 1 < C::FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // A(fm + 1)
+                                __builtin_amdgcn_sched_group_barrier(0x008, C::FN, 0);                   // MFMAs of A(fm)
+                            }
+                        }
                 } else if constexpr (WT == WT_BF16) {
     #pragma unroll
                     for (int sl = 0; sl < C::KS; sl++)
@@ -375,31 +410,51 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         }
                 } else if constexpr (C::NW >= 16) {
                     // fp8 with 16 waves (128 registers a lane): all A fragments of the slab, then
-                    // one B fragment at a time, so that fragments take 8 (FM + 1) registers
+                    // the B fragments one or two at a time
                     const int c0 = 2 * (lane >> 4);
+                    // where two B fragments fit beside the A fragments and the accumulators
+                    // (wave tiles of 32x64 and 64x32), B(fn + 1) is read before the MFMAs of
+                    // B(fn) are issued, so that its latency is spent under them
+                    constexpr bool B2 = 8 * (C::FM + 2) + 4 * C::FM * C::FN <= 96;
+                    auto frag = [&](const char *slab, int r) {
+                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
+                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    };
     #pragma unroll
                     for (int sl = 0; sl < C::KS; sl++) {
                         i32x8 af[C::FM];
     #pragma unroll
-                        for (int fm = 0; fm < C::FM; fm++) {
-                            const int r = wm * C::TM + fm * 16 + (lane & 15);
-                            const char *slab = sa + sl * C::BM * 128;
-                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
-                            af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                        }
-    #pragma unroll
-                        for (int fn = 0; fn < C::FN; fn++) {
-                            const int r = wn * C::TN + fn * 16 + (lane & 15);
+                        for (int fm = 0; fm < C::FM; fm++)
+                            af[fm] = frag(sa + sl * C::BM * 128, wm * C::TM + fm * 16 + (lane & 15));
+                        if constexpr (B2) {
                             const char *slab = sb + sl * C::BN * 128;
-                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
-                            const i32x8 b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                            i32x8 bfr[2];
+                            bfr[0] = frag(slab, wn * C::TN + (lane & 15));
     #pragma unroll
-                            for (int fm = 0; fm < C::FM; fm++)
-                                acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], b, acc[fm][fn], 0, 0, 0,
-                                                                                            127, 0, 127);
-                            __builtin_amdgcn_sched_barrier(0);   // keep the B loads from being hoisted together
+                            for (int fn = 0; fn < C::FN; fn++) {
+                                if (fn + 1 < C::FN) bfr[(fn + 1) & 1] = frag(slab, wn * C::TN + (fn + 1) * 16 + (lane & 15));
+    #pragma unroll
+                                for (int fm = 0; fm < C::FM; fm++)
+                                    acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                        af[fm], bfr[fn & 1], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+                            }
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::FM + 2, 0);   // A, B(0)
+    #pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++) {
+                                if (fn + 1 < C::FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // B(fn + 1)
+                                __builtin_amdgcn_sched_group_barrier(0x008, C::FM, 0);                   // MFMAs of B(fn)
+                            }
+                        } else {   // one B fragment at a time: fragments take 8 (FM + 1) registers
+    #pragma unroll
+                            for (int fn = 0; fn < C::FN; fn++) {
+                                const i32x8 b = frag(sb + sl * C::BN * 128, wn * C::TN + fn * 16 + (lane & 15));
+    #pragma unroll
+                                for (int fm = 0; fm < C::FM; fm++)
+                                    acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], b, acc[fm][fn], 0, 0,
+                                                                                                0, 127, 0, 127);
+                                __builtin_amdgcn_sched_barrier(0);   // keep the B loads from being hoisted together
+                            }
                         }
                     }
                 } else {   // fp8: one 16x16x128 MFMA per slab; a lane's 32 bytes are two swizzled chunks
@@ -446,15 +501,25 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
         float scale = 1.0f;
         if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
         const int lcol = lane & (C::MS - 1);
+        // The rows of this lane's accumulators, q = fm * NR + i, in chunks of at most 16: a
+        // chunk's pairs (and GEMM2's weights) are read and pinned before its stores (see pin)
+        constexpr int EQ = C::FM * NR, EQC = EQ < 16 ? EQ : 16;
+        auto epi_row = [&](int q) { return wm * C::TM + (q / NR) * C::MS + frag_row<C::MS>(lane, q % NR); };
+        auto epi_pair = [&](int q) { return block_pair_nb(a, br, epi_row(q)); };
         if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
             // split K: this split's gate and up sums in fp32 (the finishing pass adds the
             // splits in order and applies SiLU * up); filler rows are left out
 #pragma unroll
-            for (int fm = 0; fm < C::FM; fm++)
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                int pr[EQC];
 #pragma unroll
-                for (int i = 0; i < NR; i++) {
-                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
-                    if (block_pair(a, br, lr) >= a.pairs) continue;
+                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(pr[j]);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, row = row0 + epi_row(q0 + j);
+                    if (pr[j] >= a.pairs) continue;
                     float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
@@ -463,15 +528,21 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
                     }
                 }
+            }
         } else if (KIND == GEMM_GATE_UP && tail) {
             // split tail: this split's gate and up sums in fp32 (the finishing pass adds the
             // splits in order and applies SiLU * up; for fp8 it also folds |h|)
 #pragma unroll
-            for (int fm = 0; fm < C::FM; fm++)
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                int pr[EQC];
 #pragma unroll
-                for (int i = 0; i < NR; i++) {
-                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
-                    if (block_pair(a, br, lr) >= a.pairs) continue;
+                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(pr[j]);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, row = row0 + epi_row(q0 + j);
+                    if (pr[j] >= a.pairs) continue;
                     float *P = a.tail_P + s * tail_plane + (int64_t)(row - tail_row0) * tail_ld;
 #pragma unroll
                     for (int f = 0; f < C::FN / 2; f++) {
@@ -480,17 +551,31 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
                     }
                 }
+            }
         } else if constexpr (KIND == GEMM_GATE_UP) {
             float amax = 0.0f;
             uint32_t seen = 0;   // the h maximum so far, read before the stores (see amax_peek)
             if constexpr (WT == WT_FP8)
                 if (lane == 0 && a.amax_out) seen = amax_peek(a.amax_out);
 #pragma unroll
-            for (int fm = 0; fm < C::FM; fm++)
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                bool valid[EQC];   // |h| of filler rows stays out of the maximum (fp8 only)
+                if constexpr (WT == WT_FP8) {
+                    int pr[EQC];
 #pragma unroll
-                for (int i = 0; i < NR; i++) {
-                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
-                    const bool valid = block_pair(a, br, lr) < a.pairs;
+                    for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) {
+                        pin(pr[j]);
+                        valid[j] = pr[j] < a.pairs;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) valid[j] = true;
+                }
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, lr = epi_row(q0 + j), row = row0 + lr;
                     // without padding the rows past the block are the next block's: not written
                     if (lr >= br.n) continue;
 #pragma unroll
@@ -500,30 +585,46 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                         const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
                         if constexpr (WT == WT_FP8) {
                             ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
-                            if (valid) amax = fmaxf(amax, fabsf(hv));
+                            if (valid[j]) amax = fmaxf(amax, fabsf(hv));
                         } else {
                             ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
                         }
                     }
                 }
+            }
             if constexpr (WT == WT_FP8) {
 #pragma unroll
                 for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
                 if (lane == 0 && a.amax_out) amax_raise(a.amax_out, seen, amax);
             }
         } else {
+            // per chunk of rows: every row's pair, then every row's weight, then the stores
 #pragma unroll
-            for (int fm = 0; fm < C::FM; fm++)
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                int pr[EQC];
+                float wr[EQC];
 #pragma unroll
-                for (int i = 0; i < NR; i++) {
-                    const int lr = wm * C::TM + fm * C::MS + frag_row<C::MS>(lane, i), row = row0 + lr;
-                    const int p = block_pair(a, br, lr);
+                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(pr[j]);
+                if (a.topk_w) {   // filler rows read pair 0's weight
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) wr[j] = a.topk_w[pr[j] < a.pairs ? pr[j] : 0] * scale;
+                } else {          // the grouped GEMM has no weight
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) wr[j] = scale;
+                }
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(wr[j]);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR;
+                    const int lr = epi_row(q0 + j), row = row0 + lr, p = pr[j];
                     if (p >= a.pairs) continue;   // filler row: never read back
-                    const float w = (a.topk_w ? a.topk_w[p] : 1.0f) * scale;   // the grouped GEMM has no weight
 #pragma unroll
                     for (int fn = 0; fn < C::FN; fn++) {
                         const int col = nt * C::BN + wn * C::TN + fn * C::MS + lcol;
-                        const float v = acc[fm][fn][i] * w;
+                        const float v = acc[fm][fn][i] * wr[j];
                         if constexpr (PARTIAL)
                             ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
                         else if (tail)
@@ -532,11 +633,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
                             ((uint16_t *)a.C)[(a.out_by_pair ? (int64_t)p : row) * a.ldc + col] = f32_to_bf16_bits(v);
                     }
                 }
+            }
         }
     }
 }
 
 // ---- tile tables (ids continue gemm.hip's per weight type) --------------------------------
+// Tiles of at most 80 KB of LDS and 4 waves (bf16 44/45, fp8 19/20: two stages of a 128x128
+// or 64x256 tile) run two workgroups per CU, so one can load or store while the other
+// computes: for short K (the fp8 GEMM2 of a small I) a tile's fill and epilogue are a large
+// part of its time.
 //        id  BM   BN  KS ST WM WN MS  SB
 #define PIPE_BF16_TILES(X)              \
     X(7, 128, 256, 1, 3, 2, 2, 16, 128)      \
@@ -568,7 +674,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     X(34, 256, 256, 1, 5, 2, 4, 32, 64)  \
     X(35, 256, 128, 1, 5, 4, 2, 32, 64)  \
     X(36, 128, 256, 1, 5, 2, 4, 32, 64)  \
-    X(37, 256, 128, 1, 3, 4, 4, 16, 128)
+    X(37, 256, 128, 1, 3, 4, 4, 16, 128) \
+    X(44, 128, 128, 1, 2, 2, 2, 16, 128) \
+    X(45, 64, 256, 1, 2, 1, 4, 16, 128)
 #define PIPE_FP8_TILES(X)               \
     X(7, 128, 256, 1, 3, 2, 2, 16, 128)      \
     X(8, 128, 128, 1, 4, 2, 2, 16, 128)      \
@@ -579,7 +687,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_pipe(GemmArgs a) {
     X(13, 128, 256, 1, 3, 2, 4, 16, 128)     \
     X(14, 256, 256, 1, 2, 4, 4, 16, 128) \
     X(15, 256, 128, 1, 3, 4, 4, 16, 128) \
-    X(16, 128, 256, 1, 3, 4, 4, 16, 128)
+    X(16, 128, 256, 1, 3, 4, 4, 16, 128) \
+    X(19, 128, 128, 1, 2, 2, 2, 16, 128) \
+    X(20, 64, 256, 1, 2, 1, 4, 16, 128)
 // tiles whose B (BX = 1) or A (BX = -1) runs a stage ahead of the other operand
 //        id  BM   BN  KS ST WM WN MS  SB  BX
 #define PIPE_BF16_TILES_BX(X) X(38, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(39, 256, 256, 1, 2, 4, 4, 16, 128, -1)

@@ -92,6 +92,21 @@ __device__ __forceinline__ BlockRows block_rows(const GemmArgs &a, int mb, int B
 __device__ __forceinline__ int block_pair(const GemmArgs &a, BlockRows b, int r) {
     return r < b.n ? a.sorted[b.row0 + r] : a.pairs;
 }
+// The same without a branch around the load (a row past the block reads the block's first
+// entry): the GEMM epilogues read a chunk of rows' pairs back to back.
+__device__ __forceinline__ int block_pair_nb(const GemmArgs &a, BlockRows b, int r) {
+    const int v = a.sorted[b.row0 + (r < b.n ? r : 0)];
+    return r < b.n ? v : a.pairs;
+}
+// A loaded value taken into a register here: the wait for its load is placed at this point,
+// once for a chunk of loads, instead of next to each row's stores, where the compiler would
+// sink it and where it would also drain every store issued before (the wait counter counts
+// stores too).  The GEMM epilogues read all of a chunk's pairs and weights, pin them, then
+// store.
+template <class T>
+__device__ __forceinline__ void pin(T &v) {
+    asm volatile("" : "+v"(v));
+}
 
 struct TileInfo {
     int BM, BN, BK, WM, WN;      // tile rows, B rows per tile, K step, wave grid
