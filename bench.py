@@ -215,14 +215,19 @@ def kernel_roofline(cfg, m):
                 algorithmic_flops=flops, algorithmic_bytes=nbytes)
 
 
-KERNEL_SOURCES = tuple("moe_layer_02_amd/csrc/" + f for f in
-                       ("gemm.hip", "gemm_pipe.hip", "gemm_i4.hip", "pipe.h", "common.h", "kernels.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_sha():
+def kernel_sources(wdtype):
+    """The sources of the GEMM kernels a layer of this weight type runs at large T: the
+    pipelined kernels (bf16, fp8) or the int4 kernels, and the headers they share."""
+    own = "gemm_i4.hip" if wdtype == synth.WDT_INT4 else "gemm_pipe.hip"
+    return tuple("moe_layer_02_amd/csrc/" + f for f in (own, "pipe.h", "common.h", "kernels.h"))
+
+
+def kernel_source_sha(wdtype):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources(wdtype):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -238,7 +243,7 @@ def measured_traffic(cfg, T, kernel):
     except (OSError, ValueError):
         return None
     rec = data.get("%s:T%d:%s" % (cfg.name, T, kernel))
-    if not rec or rec.get("kernel_sha") != kernel_source_sha():
+    if not rec or rec.get("kernel_sha") != kernel_source_sha(cfg.wdtype):
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
