@@ -128,7 +128,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
             if (ins < C::A_LOADS) {
                 const int slab = ins / (C::BM / 8), rb = ins % (C::BM / 8) * 8;
                 const int r = rb + (lane >> 3);
-                const int chunk = (lane & 7) ^ swz(r);
+                const int chunk = (lane & 7) ^ swz_key<2>(r);   // A's layout key (pipe.h)
                 const int p = block_pair(a, br, r);
                 // a row past the block's pairs reads its block's first row (never stored)
                 const int64_t arow = KIND == GEMM_GATE_UP ? (p < a.pairs ? p / a.top_k : 0) : row0 + (r < br.n ? r : 0);
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
 #pragma unroll
                     for (int fm = 0; fm < C::FM; fm++) {
                         const int r = wm * C::TM + fm * 16 + (lane & 15);
-                        const bf16x8 af = *(const bf16x8 *)(sa + (slab * C::BM + r) * 128 + ((chunk ^ swz(r)) << 4));
+                        const bf16x8 af = *(const bf16x8 *)(sa + (slab * C::BM + r) * 128 + ((chunk ^ swz_key<2>(r)) << 4));
                         rs[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, d ? rs[fm] : zero, 0, 0, 0);
 #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++)

@@ -12,7 +12,8 @@
 // the 64 banks, and 8 pairs cover all positions -- measured on gfx950 at the full
 // ds_read_b128 rate for both the 16x16 and the 32x32 fragment patterns, where c ^ (r & 7)
 // loses 20-35% to conflicts.  Lane l of an instruction (8 rows from a multiple of 8)
-// therefore fetches the chunk (l & 7) ^ swz(row of l).
+// therefore fetches the chunk (l & 7) ^ swz(row of l).  The fp8 tiles, whose fragment reads
+// take chunks 2g and 2g + 1, use the key that is conflict-free for that pattern (pipe.h).
 //
 // K loop, per step kt: wait until this wave's loads of stage kt have landed (s_waitcnt
 // vmcnt with the later stages still counted), s_barrier (so every wave's part has
@@ -49,6 +50,7 @@ struct PCfg {
     static constexpr int DA = ST + (BX < 0), DB = ST + (BX > 0);   // ring depths
     static constexpr int MS = MS_;                            // MFMA output tile: 16x16 or 32x32
     static constexpr int SB = SB_;                            // bytes of K per row and slab: 128 or 64
+    static constexpr int SWZ = WT == WT_FP8 ? 1 : 0;          // LDS layout key (pipe.h: swz_key)
     static constexpr int NW = WM * WN, NT = NW * kWave;
     static constexpr int SLAB_K = WT == WT_FP8 ? SB : SB / 2; // K elements in a slab row
     static constexpr int BK = KS * SLAB_K;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
             if (ins < C::A_LOADS) {
                 const int slab = ins / (C::BM / C::RPI), rb = ins % (C::BM / C::RPI) * C::RPI;
                 int r, chunk;
-                dma_lane<C::SB>(lane, rb, r, chunk);
+                dma_lane<C::SB, C::SWZ>(lane, rb, r, chunk);
                 const int p = block_pair(a, br, r);
                 // a row past the block's pairs reads its block's first row (in bounds; its
                 // products are never stored)
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 const int j = ins - C::A_LOADS;
                 const int slab = j / (C::BN / C::RPI), rb = j % (C::BN / C::RPI) * C::RPI;
                 int rr, chunk;
-                dma_lane<C::SB>(lane, rb, rr, chunk);
+                dma_lane<C::SB, C::SWZ>(lane, rb, rr, chunk);
                 int64_t grow;
                 if (KIND == GEMM_GATE_UP) {   // LDS rows of wave column w: its gate half, then its up half
                     const int wcol = rr / C::TN, i = rr % C::TN, half = C::TN / 2;
@@ -239,10 +241,10 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 const int ci = q * 4 + (lane >> 4);
 #pragma unroll
                 for (int fm = 0; fm < C::FM; fm++)
-                    af[buf][fm] = *(const bf16x8 *)(sa + slab_off<C::SB>(wm * C::TM + fm * 16 + (lane & 15), ci));
+                    af[buf][fm] = *(const bf16x8 *)(sa + slab_off<C::SB, C::SWZ>(wm * C::TM + fm * 16 + (lane & 15), ci));
 #pragma unroll
                 for (int fn = 0; fn < C::FN; fn++)
-                    bfr[buf][fn] = *(const bf16x8 *)(sb + slab_off<C::SB>(wn * C::TN + fn * 16 + (lane & 15), ci));
+                    bfr[buf][fn] = *(const bf16x8 *)(sb + slab_off<C::SB, C::SWZ>(wn * C::TN + fn * 16 + (lane & 15), ci));
             };
             auto mma = [&](int buf) {
 #pragma unroll
@@ -331,12 +333,12 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
     #pragma unroll
                         for (int fm = 0; fm < C::FM; fm++) {
                             const int r = wm * C::TM + fm * 32 + (lane & 31);
-                            af[buf][fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
+                            af[buf][fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB, C::SWZ>(r, ci));
                         }
     #pragma unroll
                         for (int fn = 0; fn < C::FN; fn++) {
                             const int r = wn * C::TN + fn * 32 + (lane & 31);
-                            bfr[buf][fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
+                            bfr[buf][fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB, C::SWZ>(r, ci));
                         }
                     };
                     load(0, 0);
@@ -366,12 +368,12 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                             bf16x8 af[2], bfr[C::FN];
     #pragma unroll
                             for (int fn = 0; fn < C::FN; fn++)
-                                bfr[fn] = *(const bf16x8 *)(pb + slab_off<C::SB>(wn * C::TN + fn * 16 + (lane & 15), ci));
-                            af[0] = *(const bf16x8 *)(pa + slab_off<C::SB>(wm * C::TM + (lane & 15), ci));
+                                bfr[fn] = *(const bf16x8 *)(pb + slab_off<C::SB, C::SWZ>(wn * C::TN + fn * 16 + (lane & 15), ci));
+                            af[0] = *(const bf16x8 *)(pa + slab_off<C::SB, C::SWZ>(wm * C::TM + (lane & 15), ci));
     #pragma unroll
                             for (int fm = 0; fm < C::FM; fm++) {
                                 if (fm + 1 < C::FM)
-                                    af[(fm + 1) & 1] = *(const bf16x8 *)(pa + slab_off<C::SB>(
+                                    af[(fm + 1) & 1] = *(const bf16x8 *)(pa + slab_off<C::SB, C::SWZ>(
                                                                             wm * C::TM + (fm + 1) * 16 + (lane & 15), ci));
     #pragma unroll
                                 for (int fn = 0; fn < C::FN; fn++)
@@ -395,12 +397,12 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
     #pragma unroll
                             for (int fm = 0; fm < C::FM; fm++) {
                                 const int r = wm * C::TM + fm * 16 + (lane & 15);
-                                af[fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB>(r, ci));
+                                af[fm] = *(const bf16x8 *)(sa + sl * C::BM * C::SB + slab_off<C::SB, C::SWZ>(r, ci));
                             }
     #pragma unroll
                             for (int fn = 0; fn < C::FN; fn++) {
                                 const int r = wn * C::TN + fn * 16 + (lane & 15);
-                                bfr[fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB>(r, ci));
+                                bfr[fn] = *(const bf16x8 *)(sb + sl * C::BN * C::SB + slab_off<C::SB, C::SWZ>(r, ci));
                             }
     #pragma unroll
                             for (int fm = 0; fm < C::FM; fm++)
@@ -417,8 +419,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                     // B(fn) are issued, so that its latency is spent under them
                     constexpr bool B2 = 8 * (C::FM + 2) + 4 * C::FM * C::FN <= 96;
                     auto frag = [&](const char *slab, int r) {
-                        const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                        const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                        const uint4 lo = *(const uint4 *)(slab + slab_off<128, C::SWZ>(r, c0));
+                        const uint4 hi = *(const uint4 *)(slab + slab_off<128, C::SWZ>(r, c0 + 1));
                         return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     };
     #pragma unroll
@@ -465,8 +467,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                         for (int fm = 0; fm < C::FM; fm++) {
                             const int r = wm * C::TM + fm * 16 + (lane & 15);
                             const char *slab = sa + sl * C::BM * 128;
-                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                            const uint4 lo = *(const uint4 *)(slab + slab_off<128, C::SWZ>(r, c0));
+                            const uint4 hi = *(const uint4 *)(slab + slab_off<128, C::SWZ>(r, c0 + 1));
                             af[buf][fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                         }
@@ -474,8 +476,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                         for (int fn = 0; fn < C::FN; fn++) {
                             const int r = wn * C::TN + fn * 16 + (lane & 15);
                             const char *slab = sb + sl * C::BN * 128;
-                            const uint4 lo = *(const uint4 *)(slab + slab_off<128>(r, c0));
-                            const uint4 hi = *(const uint4 *)(slab + slab_off<128>(r, c0 + 1));
+                            const uint4 lo = *(const uint4 *)(slab + slab_off<128, C::SWZ>(r, c0));
+                            const uint4 hi = *(const uint4 *)(slab + slab_off<128, C::SWZ>(r, c0 + 1));
                             bfr[buf][fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                         }

@@ -90,26 +90,41 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // reading one chunk of 16 consecutive rows hit 64 distinct banks
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// Other read patterns want other keys (measured on gfx950 with SQ_LDS_BANK_CONFLICT, which
+// shows that a ds_read_b128 is not served as four groups of 16 consecutive lanes): where the
+// four 16-lane groups read chunks 0, 2, 4, 6 (or 1, 3, 5, 7) of 16 rows -- an fp8 fragment
+// takes 32 bytes a lane, chunks 2g and 2g + 1 -- swz costs 4 conflict cycles per read and
+// key 1 = 2 (r & 3) + ((r >> 2) & 1) none; where groups read chunk c of a slab and c + 4 of
+// the slab after it (int4's A fragments) key 2 = (r >> 1) & 3 has none.  Key 0 is swz.
+template <int K>
+__device__ __forceinline__ int swz_key(int r) {
+    if constexpr (K == 1) return 2 * (r & 3) + ((r >> 2) & 1);
+    else if constexpr (K == 2) return (r >> 1) & 3;
+    else return swz(r);
+}
+
 // Slabs of SB = 64-byte rows (32 bf16 of K) pack two rows into each 128-byte line: row r
 // is line r / 2, half r % 2, and its chunk c (0..3) sits at position (4 (r % 2) + c) ^ s
 // with s = (line / 2) % 4.  16 lanes reading one chunk of 16 consecutive rows touch 8
 // lines; lines alternate between the two halves of the banks, and within a half the four
 // lines have four different s, so the 16 positions are all distinct: conflict-free like
 // the 128-byte layout.
-template <int SB>
+template <int SB, int K = 0>
 __device__ __forceinline__ int slab_off(int r, int c) {
-    if constexpr (SB == 128) return r * 128 + ((c ^ swz(r)) << 4);
+    static_assert(SB == 128 || K == 0, "the 64-byte slabs have one layout");
+    if constexpr (SB == 128) return r * 128 + ((c ^ swz_key<K>(r)) << 4);
     else return (r >> 1) * 128 + (((((r & 1) << 2) | c) ^ ((r >> 2) & 3)) << 4);
 }
 
 // The row and chunk that lane `lane` of a DMA instruction filling the 1024 LDS bytes of
 // rows rb .. rb + 1024 / SB - 1 (rb a multiple of that count) must load: lane l writes
 // LDS bytes 16 l .. 16 l + 15 of the instruction's range, i.e. slab_off(row, chunk).
-template <int SB>
+template <int SB, int K = 0>
 __device__ __forceinline__ void dma_lane(int lane, int rb, int &row, int &chunk) {
+    static_assert(SB == 128 || K == 0, "the 64-byte slabs have one layout");
     if constexpr (SB == 128) {
         row = rb + (lane >> 3);
-        chunk = (lane & 7) ^ swz(row);
+        chunk = (lane & 7) ^ swz_key<K>(row);
     } else {
         const int line = (rb >> 1) + (lane >> 3);
         const int v = (lane & 7) ^ ((line >> 1) & 3);
