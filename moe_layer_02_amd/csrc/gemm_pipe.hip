@@ -30,7 +30,8 @@ namespace {
 
 enum { WT_BF16 = 0, WT_FP8 = 2, WT_INT4 = 3 };
 
-template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_, int BX_ = 0, int IL_ = 0>
+template <int WT, int BM_, int BN_, int KS_, int ST_, int WM_, int WN_, int MS_, int SB_, int BX_ = 0, int IL_ = 0,
+          int XT_ = 0>
 struct PCfg {
     static constexpr int BM = BM_, BN = BN_, KS = KS_, ST = ST_, WM = WM_, WN = WN_;
     // BX = 1 (-1): B (A) gets one stage more than the other operand, each operand in a ring
@@ -45,6 +46,11 @@ struct PCfg {
     // at two waves per SIMD a lane has 256 registers, room for two fragment sets beside the
     // accumulators.
     static constexpr int IL = IL_;
+    // XT = 1: a unit's epilogue is deferred into the next unit's start, after that unit's
+    // first stages are issued, so their loads land while the stores go out (the units of a
+    // round otherwise read, compute and store in lockstep across the device: the first-stage
+    // wait and the store burst add up per unit, which dominates at short K)
+    static constexpr int XT = XT_;
     static_assert(!IL || (WT == WT_BF16 && MS_ == 16 && BX == 0 && SB_ == 128 && KS == 1),
                   "interleaved fragments: bf16 16x16 tiles of one 128-byte slab per stage");
     static constexpr int DA = ST + (BX < 0), DB = ST + (BX > 0);   // ring depths
@@ -133,6 +139,172 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
     const int64_t tail_plane = (int64_t)(mblocks - mb_dp) * C::BM * tail_ld;   // at least the tail's rows
     const int tail_row0 = tail_tiles ? block_rows(a, mb_dp, C::BM).row0 : 0;
 
+    using Acc = typename AccOf<C::MS>::type;
+    constexpr int NR = C::MS == 32 ? 16 : 4;              // accumulator values per lane per fragment
+    Acc acc[C::FM][C::FN];
+    // the epilogue of a unit (its accumulators in acc); before_stores() runs once, after the
+    // epilogue's loads have landed and before its first store
+    auto epilogue = [&](const bool tail, const int s, const int nt, const int e, const BlockRows br,
+                        auto &&before_stores) {
+        const int row0 = br.row0;
+        // ---- epilogue: accumulator value i of fragment (fm, fn) is row frag_row(lane, i),
+        //      column lane % MS of that fragment ----
+        float scale = 1.0f;
+        if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
+        // before the first store: every load of the epilogue has landed (a wait placed later
+        // would also wait for whatever before_stores issues)
+        auto ready = [&]() {
+            pin(scale);
+            before_stores();
+        };
+        const int lcol = lane & (C::MS - 1);
+        // The rows of this lane's accumulators, q = fm * NR + i, in chunks of at most 16: a
+        // chunk's pairs (and GEMM2's weights) are read and pinned before its stores (see pin)
+        constexpr int EQ = C::FM * NR, EQC = EQ < 16 ? EQ : 16;
+        auto epi_row = [&](int q) { return wm * C::TM + (q / NR) * C::MS + frag_row<C::MS>(lane, q % NR); };
+        auto epi_pair = [&](int q) { return block_pair_nb(a, br, epi_row(q)); };
+        if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
+            // split K: this split's gate and up sums in fp32 (the finishing pass adds the
+            // splits in order and applies SiLU * up); filler rows are left out
+#pragma unroll
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                int pr[EQC];
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(pr[j]);
+                if (q0 == 0) ready();
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, row = row0 + epi_row(q0 + j);
+                    if (pr[j] >= a.pairs) continue;
+                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
+                        P[col] = acc[fm][f][i] * scale;
+                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
+                    }
+                }
+            }
+        } else if (KIND == GEMM_GATE_UP && tail) {
+            // split tail: this split's gate and up sums in fp32 (the finishing pass adds the
+            // splits in order and applies SiLU * up; for fp8 it also folds |h|)
+#pragma unroll
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                int pr[EQC];
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(pr[j]);
+                if (q0 == 0) ready();
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, row = row0 + epi_row(q0 + j);
+                    if (pr[j] >= a.pairs) continue;
+                    float *P = a.tail_P + s * tail_plane + (int64_t)(row - tail_row0) * tail_ld;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
+                        P[col] = acc[fm][f][i] * scale;
+                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
+                    }
+                }
+            }
+        } else if constexpr (KIND == GEMM_GATE_UP) {
+            float amax = 0.0f;
+            uint32_t seen = 0;   // the h maximum so far, read before the stores (see amax_peek)
+            if constexpr (WT == WT_FP8)
+                if (lane == 0 && a.amax_out) seen = amax_peek(a.amax_out);
+#pragma unroll
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                bool valid[EQC];   // |h| of filler rows stays out of the maximum (fp8 only)
+                if constexpr (WT == WT_FP8) {
+                    int pr[EQC];
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) {
+                        pin(pr[j]);
+                        valid[j] = pr[j] < a.pairs;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) valid[j] = true;
+                }
+                if (q0 == 0) {   // the maximum so far has landed too
+                    pin(seen);
+                    ready();
+                }
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, lr = epi_row(q0 + j), row = row0 + lr;
+                    // without padding the rows past the block are the next block's: not written
+                    if (lr >= br.n) continue;
+#pragma unroll
+                    for (int f = 0; f < C::FN / 2; f++) {
+                        const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
+                        const float hv = silu(g) * u;
+                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
+                        if constexpr (WT == WT_FP8) {
+                            ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
+                            if (valid[j]) amax = fmaxf(amax, fabsf(hv));
+                        } else {
+                            ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
+                        }
+                    }
+                }
+            }
+            if constexpr (WT == WT_FP8) {
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                if (lane == 0 && a.amax_out) amax_raise(a.amax_out, seen, amax);
+            }
+        } else {
+            // per chunk of rows: every row's pair, then every row's weight, then the stores
+#pragma unroll
+            for (int q0 = 0; q0 < EQ; q0 += EQC) {
+                int pr[EQC];
+                float wr[EQC];
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(pr[j]);
+                if (a.topk_w) {   // filler rows read pair 0's weight
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) wr[j] = a.topk_w[pr[j] < a.pairs ? pr[j] : 0] * scale;
+                } else {          // the grouped GEMM has no weight
+#pragma unroll
+                    for (int j = 0; j < EQC; j++) wr[j] = scale;
+                }
+#pragma unroll
+                for (int j = 0; j < EQC; j++) pin(wr[j]);
+                if (q0 == 0) ready();
+#pragma unroll
+                for (int j = 0; j < EQC; j++) {
+                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR;
+                    const int lr = epi_row(q0 + j), row = row0 + lr, p = pr[j];
+                    if (p >= a.pairs) continue;   // filler row: never read back
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; fn++) {
+                        const int col = nt * C::BN + wn * C::TN + fn * C::MS + lcol;
+                        const float v = acc[fm][fn][i] * wr[j];
+                        if constexpr (PARTIAL)
+                            ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
+                        else if (tail)
+                            a.tail_P[s * tail_plane + (int64_t)(row - tail_row0) * a.ldc + col] = v;
+                        else
+                            ((uint16_t *)a.C)[(a.out_by_pair ? (int64_t)p : row) * a.ldc + col] = f32_to_bf16_bits(v);
+                    }
+                }
+            }
+        }
+    };
+    // XT: the unit whose epilogue is pending
+    bool pv_valid = false, pv_tail = false;
+    int pv_s = 0, pv_nt = 0, pv_e = 0;
+    BlockRows pv_br{0, 0};
+
     for (int tile = xcd_first_tile(blockIdx.x, G); tile < total; tile += G) {
         // unit: whole-K tile (or one of split_k splits), or one split of a tail tile
         const bool tail = TAIL && tile >= mn_dp;
@@ -215,9 +387,27 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
         // with no real row starts with padding: such waves (the tail block of an expert at
         // large block heights) skip their LDS reads and MFMAs but still load and synchronise
         const bool wave_rows = __builtin_amdgcn_readfirstlane(block_pair(a, br, wm * C::TM) < a.pairs);
-        using Acc = typename AccOf<C::MS>::type;
-        constexpr int NR = C::MS == 32 ? 16 : 4;              // accumulator values per lane per fragment
-        Acc acc[C::FM][C::FN];
+        // this unit's first stages (after every wave is done with the previous unit's buffers)
+        auto start_stages = [&]() {
+            block_barrier();
+            if constexpr (C::IL) {
+#pragma unroll
+                for (int p = 0; p < C::ST; p++)
+                    if (p < nku) issue(p, true, true);
+            } else {
+#pragma unroll
+                for (int p = 0; p < C::ST - 1; p++)
+                    if (p < nku) issue(p, true, true);
+                if constexpr (C::BX != 0)   // the operand that runs ahead: its step 1 too
+                    if (1 < nku) issue(1, C::BX < 0, C::BX > 0);
+            }
+        };
+        if constexpr (C::XT) {
+            if (pv_valid) epilogue(pv_tail, pv_s, pv_nt, pv_e, pv_br, start_stages);
+            else start_stages();
+        } else {
+            start_stages();
+        }
 #pragma unroll
         for (int i = 0; i < C::FM; i++)
 #pragma unroll
@@ -229,10 +419,6 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
             // every buffer filled ahead; a stage's buffer is refilled after the barrier that
             // follows every wave's last read of it
             constexpr int NK = C::SB / 64;                  // 32-K substeps per stage (2)
-            block_barrier();
-#pragma unroll
-            for (int p = 0; p < C::ST; p++)
-                if (p < nku) issue(p, true, true);
             bf16x8 af[2][C::FM], bfr[2][C::FN];
             // fragments of substep q of stage k into set buf: lane l holds row l % 16 and K
             // elements 8 (l / 16) .. +7 of the substep
@@ -297,14 +483,6 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 }
             }
         } else {
-            // every wave is done with the previous tile's buffers before they are refilled
-            block_barrier();
-    #pragma unroll
-            for (int p = 0; p < C::ST - 1; p++)
-                if (p < nku) issue(p, true, true);
-            if constexpr (C::BX != 0)   // the operand that runs ahead: its step 1 too
-                if (1 < nku) issue(1, C::BX < 0, C::BX > 0);
-
             for (int kt = 0; kt < nku; kt++) {
                 if constexpr (C::BX != 0) {
                     // issued after this step's last operand: the ahead operand's step kt + 1, if
@@ -498,146 +676,19 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
             }
         }
 
-        // ---- epilogue: accumulator value i of fragment (fm, fn) is row frag_row(lane, i),
-        //      column lane % MS of that fragment ----
-        float scale = 1.0f;
-        if constexpr (WT == WT_FP8) scale = a.a_scale[0] * a.b_scale[e];
-        const int lcol = lane & (C::MS - 1);
-        // The rows of this lane's accumulators, q = fm * NR + i, in chunks of at most 16: a
-        // chunk's pairs (and GEMM2's weights) are read and pinned before its stores (see pin)
-        constexpr int EQ = C::FM * NR, EQC = EQ < 16 ? EQ : 16;
-        auto epi_row = [&](int q) { return wm * C::TM + (q / NR) * C::MS + frag_row<C::MS>(lane, q % NR); };
-        auto epi_pair = [&](int q) { return block_pair_nb(a, br, epi_row(q)); };
-        if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
-            // split K: this split's gate and up sums in fp32 (the finishing pass adds the
-            // splits in order and applies SiLU * up); filler rows are left out
-#pragma unroll
-            for (int q0 = 0; q0 < EQ; q0 += EQC) {
-                int pr[EQC];
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(pr[j]);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) {
-                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, row = row0 + epi_row(q0 + j);
-                    if (pr[j] >= a.pairs) continue;
-                    float *P = (float *)a.C + (int64_t)s * a.partial_stride + (int64_t)row * a.ldc;
-#pragma unroll
-                    for (int f = 0; f < C::FN / 2; f++) {
-                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
-                        P[col] = acc[fm][f][i] * scale;
-                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
-                    }
-                }
-            }
-        } else if (KIND == GEMM_GATE_UP && tail) {
-            // split tail: this split's gate and up sums in fp32 (the finishing pass adds the
-            // splits in order and applies SiLU * up; for fp8 it also folds |h|)
-#pragma unroll
-            for (int q0 = 0; q0 < EQ; q0 += EQC) {
-                int pr[EQC];
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(pr[j]);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) {
-                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, row = row0 + epi_row(q0 + j);
-                    if (pr[j] >= a.pairs) continue;
-                    float *P = a.tail_P + s * tail_plane + (int64_t)(row - tail_row0) * tail_ld;
-#pragma unroll
-                    for (int f = 0; f < C::FN / 2; f++) {
-                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
-                        P[col] = acc[fm][f][i] * scale;
-                        P[a.I + col] = acc[fm][f + C::FN / 2][i] * scale;
-                    }
-                }
-            }
-        } else if constexpr (KIND == GEMM_GATE_UP) {
-            float amax = 0.0f;
-            uint32_t seen = 0;   // the h maximum so far, read before the stores (see amax_peek)
-            if constexpr (WT == WT_FP8)
-                if (lane == 0 && a.amax_out) seen = amax_peek(a.amax_out);
-#pragma unroll
-            for (int q0 = 0; q0 < EQ; q0 += EQC) {
-                bool valid[EQC];   // |h| of filler rows stays out of the maximum (fp8 only)
-                if constexpr (WT == WT_FP8) {
-                    int pr[EQC];
-#pragma unroll
-                    for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
-#pragma unroll
-                    for (int j = 0; j < EQC; j++) {
-                        pin(pr[j]);
-                        valid[j] = pr[j] < a.pairs;
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < EQC; j++) valid[j] = true;
-                }
-#pragma unroll
-                for (int j = 0; j < EQC; j++) {
-                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR, lr = epi_row(q0 + j), row = row0 + lr;
-                    // without padding the rows past the block are the next block's: not written
-                    if (lr >= br.n) continue;
-#pragma unroll
-                    for (int f = 0; f < C::FN / 2; f++) {
-                        const float g = acc[fm][f][i] * scale, u = acc[fm][f + C::FN / 2][i] * scale;
-                        const float hv = silu(g) * u;
-                        const int col = nt * (C::BN / 2) + wn * (C::TN / 2) + f * C::MS + lcol;
-                        if constexpr (WT == WT_FP8) {
-                            ((float *)a.C)[(int64_t)row * a.ldc + col] = hv;
-                            if (valid[j]) amax = fmaxf(amax, fabsf(hv));
-                        } else {
-                            ((uint16_t *)a.C)[(int64_t)row * a.ldc + col] = f32_to_bf16_bits(hv);
-                        }
-                    }
-                }
-            }
-            if constexpr (WT == WT_FP8) {
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-                if (lane == 0 && a.amax_out) amax_raise(a.amax_out, seen, amax);
-            }
+        if constexpr (C::XT) {
+            pv_valid = true;
+            pv_tail = tail;
+            pv_s = s;
+            pv_nt = nt;
+            pv_e = e;
+            pv_br = br;
         } else {
-            // per chunk of rows: every row's pair, then every row's weight, then the stores
-#pragma unroll
-            for (int q0 = 0; q0 < EQ; q0 += EQC) {
-                int pr[EQC];
-                float wr[EQC];
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(pr[j]);
-                if (a.topk_w) {   // filler rows read pair 0's weight
-#pragma unroll
-                    for (int j = 0; j < EQC; j++) wr[j] = a.topk_w[pr[j] < a.pairs ? pr[j] : 0] * scale;
-                } else {          // the grouped GEMM has no weight
-#pragma unroll
-                    for (int j = 0; j < EQC; j++) wr[j] = scale;
-                }
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(wr[j]);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) {
-                    const int fm = (q0 + j) / NR, i = (q0 + j) % NR;
-                    const int lr = epi_row(q0 + j), row = row0 + lr, p = pr[j];
-                    if (p >= a.pairs) continue;   // filler row: never read back
-#pragma unroll
-                    for (int fn = 0; fn < C::FN; fn++) {
-                        const int col = nt * C::BN + wn * C::TN + fn * C::MS + lcol;
-                        const float v = acc[fm][fn][i] * wr[j];
-                        if constexpr (PARTIAL)
-                            ((float *)a.C)[(int64_t)s * a.partial_stride + (int64_t)row * a.ldc + col] = v;
-                        else if (tail)
-                            a.tail_P[s * tail_plane + (int64_t)(row - tail_row0) * a.ldc + col] = v;
-                        else
-                            ((uint16_t *)a.C)[(a.out_by_pair ? (int64_t)p : row) * a.ldc + col] = f32_to_bf16_bits(v);
-                    }
-                }
-            }
+            epilogue(tail, s, nt, e, br, []() {});
         }
     }
+    if constexpr (C::XT)
+        if (pv_valid) epilogue(pv_tail, pv_s, pv_nt, pv_e, pv_br, []() {});
 }
 
 // ---- tile tables (ids continue gemm.hip's per weight type) --------------------------------
@@ -696,6 +747,17 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
 //        id  BM   BN  KS ST WM WN MS  SB  BX
 #define PIPE_BF16_TILES_BX(X) X(38, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(39, 256, 256, 1, 2, 4, 4, 16, 128, -1)
 #define PIPE_FP8_TILES_BX(X) X(17, 256, 256, 1, 2, 4, 4, 16, 128, 1) X(18, 256, 256, 1, 2, 4, 4, 16, 128, -1)
+// deferred-epilogue twins (XT) of the large-T tiles
+//        id  BM   BN  KS ST WM WN MS  SB  BX IL
+#define PIPE_BF16_TILES_XT(X)                    \
+    X(48, 256, 256, 1, 2, 4, 4, 16, 128, 0, 0)   \
+    X(50, 256, 256, 1, 2, 4, 4, 16, 128, 1, 0)   \
+    X(51, 128, 256, 1, 3, 2, 4, 16, 128, 0, 1)   \
+    X(52, 256, 128, 1, 3, 4, 2, 16, 128, 0, 1)   \
+    X(53, 128, 256, 1, 3, 2, 4, 16, 128, 0, 0)
+#define PIPE_FP8_TILES_XT(X)                     \
+    X(23, 128, 256, 1, 3, 4, 4, 16, 128, 0, 0)   \
+    X(24, 128, 256, 1, 3, 2, 4, 16, 128, 0, 0)
 // 8-wave tiles reading the next 32-K substep's fragments while the current MFMAs run (IL)
 //        id  BM   BN  KS ST WM WN MS  SB
 // (twins of tiles 22 and 23; a 128x64 wave tile with two fragment sets exceeds the 256
@@ -755,8 +817,12 @@ bool pipe_tile_info(int wdtype, int tile, TileInfo *info) {
 #define PI_FP8(id, bm, bn, ks, st, wm, wn, ms, sb) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
 #define PI_BF16_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
 #define PI_FP8_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
-    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PI_BF16) PIPE_BF16_TILES_BX(PI_BF16_BX) PIPE_BF16_TILES_IL(PI_BF16) }
-    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) PIPE_FP8_TILES_BX(PI_FP8_BX) }
+#define PI_BF16_XT(id, bm, bn, ks, st, wm, wn, ms, sb, bx, il) PINFO(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb)
+#define PI_FP8_XT(id, bm, bn, ks, st, wm, wn, ms, sb, bx, il) PINFO(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb)
+    if (wdtype == WT_BF16) {
+        PIPE_BF16_TILES(PI_BF16) PIPE_BF16_TILES_BX(PI_BF16_BX) PIPE_BF16_TILES_IL(PI_BF16) PIPE_BF16_TILES_XT(PI_BF16_XT)
+    }
+    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PI_FP8) PIPE_FP8_TILES_BX(PI_FP8_BX) PIPE_FP8_TILES_XT(PI_FP8_XT) }
     if (wdtype == WT_INT4) return i4_tile_info(tile, info);
     return false;
 }
@@ -773,8 +839,14 @@ hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, c
 #define PL_FP8_BX(id, bm, bn, ks, st, wm, wn, ms, sb, bx) PLAUNCH_BX(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb, bx)
 #define PL_BF16_IL(id, bm, bn, ks, st, wm, wn, ms, sb) \
     if (tile == id) return launch_kind<PCfg<WT_BF16, bm, bn, ks, st, wm, wn, ms, sb, 0, 1>, WT_BF16>(kind, partial, a, max_tiles, s);
-    if (wdtype == WT_BF16) { PIPE_BF16_TILES(PL_BF16) PIPE_BF16_TILES_BX(PL_BF16_BX) PIPE_BF16_TILES_IL(PL_BF16_IL) }
-    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) PIPE_FP8_TILES_BX(PL_FP8_BX) }
+#define PLAUNCH_XT(WT, id, bm, bn, ks, st, wm, wn, ms, sb, bx, il) \
+    if (tile == id) return launch_kind<PCfg<WT, bm, bn, ks, st, wm, wn, ms, sb, bx, il, 1>, WT>(kind, partial, a, max_tiles, s);
+#define PL_BF16_XT(id, bm, bn, ks, st, wm, wn, ms, sb, bx, il) PLAUNCH_XT(WT_BF16, id, bm, bn, ks, st, wm, wn, ms, sb, bx, il)
+#define PL_FP8_XT(id, bm, bn, ks, st, wm, wn, ms, sb, bx, il) PLAUNCH_XT(WT_FP8, id, bm, bn, ks, st, wm, wn, ms, sb, bx, il)
+    if (wdtype == WT_BF16) {
+        PIPE_BF16_TILES(PL_BF16) PIPE_BF16_TILES_BX(PL_BF16_BX) PIPE_BF16_TILES_IL(PL_BF16_IL) PIPE_BF16_TILES_XT(PL_BF16_XT)
+    }
+    if (wdtype == WT_FP8) { PIPE_FP8_TILES(PL_FP8) PIPE_FP8_TILES_BX(PL_FP8_BX) PIPE_FP8_TILES_XT(PL_FP8_XT) }
     if (wdtype == WT_INT4) return launch_gemm_i4(tile, kind, partial, a, max_tiles, s);
     return hipErrorInvalidValue;
 }
