@@ -127,6 +127,65 @@ __device__ __forceinline__ uint64_t wave_argmax(uint64_t r) {
     return r;
 }
 
+// A key's order-preserving unsigned image (-0 folded into +0, as in rank_of); 0 stands for
+// no candidate (every key maps above it).  code_key inverts it.
+__device__ __forceinline__ uint32_t key_code(float key) {
+    const uint32_t u = __float_as_uint(key + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float code_key(uint32_t u) {
+    if (!u) return -INFINITY;
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Maximum of 32-bit codes over each aligned group of 2^g lanes (g <= 6), for N independent
+// codes step by step; every lane of a group ends with the group's maximum.  A selection
+// round is a 32-bit maximum followed by one ballot per slot that names the smallest index
+// holding it -- the same (key descending, index ascending) order as the 64-bit ranks in
+// about a quarter of the instructions of a 64-bit arg-max.
+template <int S>
+__device__ __forceinline__ void max_step(uint32_t &u) {
+    const uint32_t o = (uint32_t)partner<S>((int)u);
+    u = o > u ? o : u;
+}
+template <int N>
+__device__ __forceinline__ void group_max_n(uint32_t (&u)[N], int g) {
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 0) max_step<0>(u[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 1) max_step<1>(u[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 2) max_step<2>(u[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 3) max_step<3>(u[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 4) max_step<4>(u[i]);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (g > 5) max_step<5>(u[i]);
+}
+__device__ __forceinline__ uint32_t wave_max_code(uint32_t u) {
+    max_step<0>(u);
+    max_step<1>(u);
+    max_step<2>(u);
+    max_step<3>(u);
+    max_step<4>(u);
+    max_step<5>(u);
+    return u;
+}
+// The lowest lane of mask inside this lane's aligned group of 2^g lanes (64: none).
+__device__ __forceinline__ int group_first_lane(uint64_t mask, int g) {
+    const int base = g >= 6 ? 0 : (lane_id() & ~((1 << g) - 1));
+    const uint64_t span = g >= 6 ? ~0ull : (((1ull << (1 << g)) - 1) << base);
+    const uint64_t s = mask & span;
+    return s ? __builtin_ctzll(s) : 64;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, partner<0>(v));
     v = fmaxf(v, partner<1>(v));
@@ -202,31 +261,44 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         const int G = E / a.n_group;
         const int gbits = __builtin_ctz(G);
         float score[EPL];
-        uint64_t r1[EPL], r2[EPL];
-#pragma unroll
-        for (int i = 0; i < EPL; i++) r1[i] = live[i] ? rank_of(key[i], lane + kWave * i) : 0;
-        group_argmax_n(r1, gbits);
+        uint32_t u[EPL], m1[EPL], m2[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
-            const int e = lane + kWave * i;
-            r2[i] = (live[i] && e != rank_index(r1[i])) ? rank_of(key[i], e) : 0;
+            u[i] = live[i] ? key_code(key[i]) : 0u;
+            m1[i] = u[i];
         }
-        group_argmax_n(r2, gbits);
+        group_max_n(m1, gbits);
+        // the second key: the group's largest without its first (lowest-index) holder of the
+        // largest, so a tie keeps the value
 #pragma unroll
-        for (int i = 0; i < EPL; i++) score[i] = G >= 2 ? rank_key(r1[i]) + rank_key(r2[i]) : rank_key(r1[i]);
-        // keep the topk_group best groups; the first lane of each segment stands for its group
+        for (int i = 0; i < EPL; i++) {
+            const uint64_t at = __ballot(u[i] != 0u && u[i] == m1[i]);
+            m2[i] = lane == group_first_lane(at, gbits) ? 0u : u[i];
+        }
+        group_max_n(m2, gbits);
+#pragma unroll
+        for (int i = 0; i < EPL; i++) score[i] = G >= 2 ? code_key(m1[i]) + code_key(m2[i]) : code_key(m1[i]);
+        // keep the topk_group best groups (ties: the lower group); the first lane of each
+        // segment stands for its group
         uint64_t kept = 0;
         for (int q = 0; q < a.topk_group; q++) {
-            uint64_t gr = 0;
+            uint32_t sc[EPL], m = 0u;
 #pragma unroll
             for (int i = 0; i < EPL; i++) {
                 const int e = lane + kWave * i, g = e / G;
-                if (e < E && (lane % G) == 0 && !((kept >> g) & 1ull)) {
-                    const uint64_t c = rank_of(score[i], g);
-                    if (c > gr) gr = c;
+                sc[i] = (e < E && (lane % G) == 0 && !((kept >> g) & 1ull)) ? key_code(score[i]) : 0u;
+                m = sc[i] > m ? sc[i] : m;
+            }
+            m = wave_max_code(m);
+            if (!m) break;
+#pragma unroll
+            for (int i = 0; i < EPL; i++) {
+                const uint64_t at = __ballot(sc[i] == m);
+                if (at) {
+                    kept |= 1ull << ((__builtin_ctzll(at) + kWave * i) / G);
+                    break;
                 }
             }
-            kept |= 1ull << rank_index(wave_argmax(gr));
         }
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
@@ -285,30 +357,33 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
     // fp64 exp of a softmax slot is not on the chain of arg-max rounds.
     int my_id = 0;
     float my_bv = 0.0f;
+    uint32_t uk[EPL];   // the candidates' codes, 0 once taken or not allowed
+#pragma unroll
+    for (int i = 0; i < EPL; i++) uk[i] = live[i] ? key_code(key[i]) : 0u;
     for (int j = 0; j < a.k; j++) {
-        uint64_t br = 0;
+        uint32_t m = uk[0];
 #pragma unroll
-        for (int i = 0; i < EPL; i++) {
-            if (live[i]) {
-                const uint64_t c = rank_of(key[i], lane + kWave * i);
-                if (c > br) br = c;
-            }
-        }
-        br = wave_argmax(br);
-        const int bi = rank_index(br);
-        // the winner's payload from the lane that holds it (bi is the same on every lane)
+        for (int i = 1; i < EPL; i++) m = uk[i] > m ? uk[i] : m;
+        m = wave_max_code(m);
+        // the smallest index holding the largest key, and its payload (bi is the same on
+        // every lane)
+        int bi = INT32_MAX;
         float bv = 0.0f;
-        if (br) {
-            const int slot = bi / kWave;
-            float own = val[0];
+        if (m) {
 #pragma unroll
-            for (int i = 1; i < EPL; i++)
-                if (slot == i) own = val[i];
-            bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own), bi % kWave));
+            for (int i = 0; i < EPL; i++) {
+                const uint64_t at = __ballot(uk[i] == m);
+                if (at) {
+                    const int l = __builtin_ctzll(at);
+                    bi = l + kWave * i;
+                    bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), l));
+                    break;
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < EPL; i++)
-            if (lane + kWave * i == bi) live[i] = false;
+            if (lane + kWave * i == bi) uk[i] = 0u;
         if (lane == j) {
             my_id = bi;
             my_bv = bv;

@@ -83,7 +83,7 @@ def valid_plans(layer, T, split1=(1, 2, 4), splits=(1, 2, 4, 8), tails=(0,), max
                 ragged=(0,)):
     """Every (block_m, tile1, tile2, split, split1, split_tail, split_tail1, ragged) the
     library accepts for this layer (grids capped at max_workgroups)."""
-    n = 48
+    n = 64   # every tile id the library compiles (ids run below 64)
     out = []
     for rg in ragged:
         for g1 in range(n):
