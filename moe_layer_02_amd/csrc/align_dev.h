@@ -10,14 +10,18 @@ namespace align_dev {
 constexpr int kWaves = 16;
 constexpr int kMaxE = 256;
 
+// Inclusive prefix sum over the wave: four DPP row shifts (1, 2, 4, 8 lanes) scan each row
+// of 16 lanes in registers, then the row totals (lanes 15, 31, 47) are added to the rows
+// after them -- no LDS round trips (a shuffle is an LDS permute).
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(v, off, kWave);
-        if (lane >= off) v += o;
-    }
-    return v;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane_id() >> 4;
+    return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
 // Lanes of the wave holding the same expert as this lane (only lanes with valid set).
