@@ -185,5 +185,57 @@ __device__ __forceinline__ void align_group(const AlignArgs &a) {
     scatter_range(a.ids, beg, end, E, a.nbits, hist[w], a.sorted, a.inv_pos);
 }
 
+// The align of one token's k pairs (a decode step): a top-k of one token names k distinct
+// experts, so each selected expert holds one pair and the layout is the selected experts in
+// ascending order -- what align_group produces for it, written directly.  my_id: on wave 0,
+// lane j < k holds the expert of slot j (the route's result); every thread of the workgroup
+// calls.  Returns false, having written nothing, when a slot holds no expert (the caller
+// then runs align_group on the pairs in memory).
+__device__ __forceinline__ bool align_one_token(const AlignArgs &a, int my_id) {
+    __shared__ int sel_s[kWave];                  // expert of rank r (ascending)
+    __shared__ int pair_s[kWave];                 // its pair (= slot)
+    __shared__ uint32_t bits_s[kMaxE / 32];       // the selected experts
+    __shared__ int ok_s;
+    const int tid = threadIdx.x, k = a.k, E = a.E, BM = a.BM, P = k;
+    if (tid < kMaxE / 32) bits_s[tid] = 0u;
+    __syncthreads();
+    if (tid < kWave) {
+        const bool mine = tid < k;
+        const bool ok = __ballot(mine && (unsigned)my_id < (unsigned)E) == __ballot(mine);
+        if (tid == 0) ok_s = ok;
+        if (ok && mine) {
+            int rank = 0;
+            for (int j = 0; j < k; j++) rank += __builtin_amdgcn_readlane(my_id, j) < my_id;
+            sel_s[rank] = my_id;
+            pair_s[rank] = tid;
+            atomicOr(&bits_s[my_id >> 5], 1u << (my_id & 31));
+        }
+    }
+    __syncthreads();
+    if (!ok_s) return false;
+    if (tid < E) a.counts[tid] = (int)((bits_s[tid >> 5] >> (tid & 31)) & 1u);
+    if (tid == 0) *a.npp = k * BM;   // one block of padded rows per selected expert
+    // block b < k belongs to the expert of rank b and starts at unpadded row b
+    const int64_t nb = a.cap / BM;
+    for (int64_t b = tid; b <= nb; b += 1024) {
+        const int e = b < k ? sel_s[b] : -1;
+        if (b < nb) a.eids[b] = e;
+        if (a.blk_start) a.blk_start[b] = e >= 0 ? (int)b : P;
+    }
+    if (a.blk_start) {
+        if (tid < k) {
+            a.sorted[tid] = pair_s[tid];
+            a.inv_pos[pair_s[tid]] = tid;
+        }
+    } else {   // the padded layout: filler entries except each block's first row
+        for (int64_t r = tid; r < a.cap; r += 1024) {
+            const int64_t b = r / BM;
+            a.sorted[r] = (r == b * BM && b < k) ? pair_s[b] : P;
+        }
+        if (tid < k) a.inv_pos[pair_s[tid]] = tid * BM;
+    }
+    return true;
+}
+
 }  // namespace align_dev
 }  // namespace moe

@@ -4,7 +4,8 @@
 // latency, comparable to the whole weight-streaming time of a small layer.  One launch of
 // 1024-thread workgroups does them all, with the same results as the separate kernels:
 //   workgroup 0: wave w routes tokens w, w + 16, ... (route_dev.h), a barrier makes the
-//                pairs visible, then the one-workgroup align (align_dev.h) lays them out;
+//                pairs visible, then the one-workgroup align (align_dev.h) lays them out
+//                (one token: its k distinct experts are laid out directly);
 //   workgroups 1..: the activation pass, independent of the routing --
 //                fp8 (one workgroup): the batch into registers, its largest |x| (reduced
 //                inside the workgroup, no atomics), then every code with that scale
@@ -23,7 +24,12 @@ template <int EPL, int V>
 __global__ __launch_bounds__(1024) void k_prologue(PrologueArgs p) {
     if (blockIdx.x == 0) {
         if (threadIdx.x == 0 && p.h_amax) *p.h_amax = 0u;   // GEMM1's |h| maximum starts at 0
-        for (int t = threadIdx.x >> 6; t < p.route.T; t += 16) route_dev::route_token<EPL, V>(p.route, t);
+        if (p.route.T == 1) {   // one token: its distinct experts lay out directly
+            const int id = threadIdx.x < kWave ? route_dev::route_token<EPL, V>(p.route, 0) : 0;
+            if (align_dev::align_one_token(p.align, id)) return;
+        } else {
+            for (int t = threadIdx.x >> 6; t < p.route.T; t += 16) route_dev::route_token<EPL, V>(p.route, t);
+        }
         __syncthreads();
         align_dev::align_group(p.align);
         return;

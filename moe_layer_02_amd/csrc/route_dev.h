@@ -213,9 +213,9 @@ __device__ __forceinline__ float sigmoid_f64_rounded(float x) {
 }
 
 // Route token t with the calling wavefront (every lane of the wave must call); V is
-// route_variant(a.kind, a.E, a.n_group).
+// route_variant(a.kind, a.E, a.n_group).  Returns, on lane j < k, the expert of slot j.
 template <int EPL, int V>
-__device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
+__device__ __forceinline__ int route_token(const RouteArgs &a, int t) {
     constexpr bool softmax = V == V_SOFTMAX;
     const int lane = lane_id();
     const int E = a.E;
@@ -390,13 +390,19 @@ __device__ __forceinline__ void route_token(const RouteArgs &a, int t) {
         }
     }
     const double my_val = softmax ? exp((double)my_bv - m) / z : (double)my_bv;
-    double norm = 0.0;   // summed over the slots in order 0 .. k-1
-    for (int j = 0; j < a.k; j++) norm += __shfl(my_val, j, kWave);
+    double norm = 0.0;   // summed over the slots in order 0 .. k-1 (lane reads, not LDS shuffles)
+    const int64_t vb = __double_as_longlong(my_val);
+    for (int j = 0; j < a.k; j++) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)vb, j);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(vb >> 32), j);
+        norm += __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+    }
     if (lane < a.k) {
         const double w = a.renorm ? my_val / norm : my_val;
         a.ids[(int64_t)t * a.k + lane] = my_id;
         a.weights[(int64_t)t * a.k + lane] = (float)(w * (double)a.scale);
     }
+    return my_id;
 }
 
 }  // namespace route_dev

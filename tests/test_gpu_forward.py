@@ -478,6 +478,38 @@ def test_ragged_every_plan(name, T):
         check_intermediates(c, T, p, c.gpu(T, p)[1])
 
 
+@pytest.mark.parametrize("name", ["tiny", "tiny_top1", "fp8small", "i4small"])
+def test_one_token_layouts(name):
+    """One token (a decode step): its k distinct experts are laid out directly by the
+    prologue. Every block height, with and without padding: routing and the layout
+    bit-exact against the oracle's align, the output within tolerance."""
+    cfg = {"tiny_top1": TINY_TOP1, "fp8small": FP8_SMALL, "i4small": I4_SMALL}.get(name)
+    c = case(name) if cfg is None else small_case(cfg)
+    plans = valid_plans(c.layer, 1, split1=(1,), splits=(1,), ragged=(0, 1))
+    picked = {}
+    for p in plans:   # the first plan of every (block height, layout)
+        picked.setdefault((p.block_m, p.ragged), p)
+    assert len(picked) >= 4
+    ref, _, _ = c.oracle(1)
+    for (bm, rg), p in sorted(picked.items()):
+        out, ws = c.gpu(1, p)
+        assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype], p.as_tuple()
+        check_intermediates(c, 1, p, ws)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "qwen2", "deepseek", "scout"])
+def test_one_token_full_layers(name):
+    """The layers' own plans at T = 1, and the same tiles with the other layout."""
+    c = case(name)
+    dp = c.layer.plan(1)
+    head = (dp.as_tuple() + (0,) * 9)[:8]
+    for p in (dp, abi.Plan(*head, 1 - dp.ragged)):
+        out, ws = c.gpu(1, p)
+        ref, _, _ = c.oracle(1)
+        assert rel_l2(bf16_to_f64(out), ref) <= TOL[c.cfg.wdtype], p.as_tuple()
+        check_intermediates(c, 1, p, ws)
+
+
 @pytest.mark.parametrize("T", [100, 300])
 def test_ragged_split_tails(T):
     """Both split tails and the K splits on grids capped so that whole tiles are followed by
