@@ -786,10 +786,10 @@ hipError_t launch_one(const GemmArgs &a, int64_t max_tiles, hipStream_t s) {
     GemmArgs b = a;
     b.group_m = 1;
     while (b.group_m * b.group_m * 4 <= grid / 8 && b.group_m < 16) b.group_m *= 2;
-    // GEMM1 with large blocks: groups of an expert's blocks (at most 8) -- Mixtral T=4096
-    // GEMM1 862 -> 845 us, Scout T=8192 1520 -> 1460 us; GEMM2 gains ~1% and the fp8 GEMM2
-    // of Qwen2 loses 5%, so it keeps group_m
-    b.expert_groups = KIND == GEMM_GATE_UP && C::BM >= 128 ? 8 : 0;
+    // Large blocks: groups of an expert's blocks (at most 8) -- Mixtral T=4096 GEMM1 862 ->
+    // 845 us, Scout T=8192 1520 -> 1460 us; the bf16 GEMM2 too (Scout T=4096 -1.4%, T=2048
+    // -0.5%), while the fp8 GEMM2 of Qwen2 loses 5% with them and keeps group_m
+    b.expert_groups = (KIND == GEMM_GATE_UP || WT == WT_BF16) && C::BM >= 128 ? 8 : 0;
     hipLaunchKernelGGL((k_gemm_pipe<C, WT, KIND, PARTIAL>), dim3((unsigned)grid), dim3(C::NT), 0, s, b);
     return hipGetLastError();
 }
