@@ -17,6 +17,11 @@ struct RouteArgs {
     float *weights;
     uint32_t *zero_ptr;          // words cleared by the launch (scratch counters), may be null
     int zero_n;                  // <= 256
+    // fp8: the hidden states [T, x_cols] bf16, and one word per workgroup receiving the
+    // largest |x| of its tokens as float bits (null: none)
+    const uint16_t *x;
+    int64_t x_cols;
+    uint32_t *x_parts;
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 
@@ -170,12 +175,6 @@ hipError_t launch_gate_up_finish_quant(const GateUpFinishArgs &a, const int32_t 
                                        hipStream_t s);
 
 // fp8 activation quantisation
-struct AbsmaxArgs {
-    const uint16_t *x;           // bf16
-    int64_t n;                   // elements
-    uint32_t *amax;              // float bits, atomicMax
-};
-hipError_t launch_absmax(const AbsmaxArgs &a, hipStream_t s);
 
 struct QuantArgs {
     const void *x;               // bf16 rows, or fp32 rows when x_f32
@@ -187,6 +186,11 @@ struct QuantArgs {
     const int32_t *row_valid;    // optional: sorted ids; rows with value >= pairs are zeroed
     const int32_t *npp;          // optional: rows past *npp are skipped
     int pairs;
+    // optional: the maximum comes as n_parts partial maxima (float bits) instead of *amax;
+    // block 0 stores it to amax_out
+    const uint32_t *amax_parts;
+    int n_parts;
+    uint32_t *amax_out;
 };
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 

@@ -295,6 +295,14 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         if ((err = mark(MOE_STAGE_ROUTE)) != hipSuccess) return MOE_ERR_HIP;
         ra.zero_ptr = scal;
         ra.zero_n = kScalarWords;
+        // fp8: the route's workgroups also take the largest |x| of their tokens, one word each,
+        // in h's space (free until GEMM1 writes h); the quantisation reduces them
+        uint32_t *x_parts = fp8 ? (uint32_t *)(ws + w.h) : nullptr;
+        if (fp8) {
+            ra.x = (const uint16_t *)hidden;
+            ra.x_cols = H;
+            ra.x_parts = x_parts;
+        }
         if ((err = launch_route(ra, stream)) != hipSuccess) return fail(err);
 
         // 2. align
@@ -305,9 +313,8 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         // 3. fp8: quantise the hidden states with one dynamic scale
         if (fp8) {
             if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-            AbsmaxArgs ab{(const uint16_t *)hidden, (int64_t)T * H, &scal[0]};
-            if ((err = launch_absmax(ab, stream)) != hipSuccess) return fail(err);
-            QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs};
+            QuantArgs q{hidden, 0, (uint8_t *)(ws + w.xq), T, H, &scal[0], (float *)&scal[2], nullptr, nullptr, pairs,
+                        x_parts, (T + 3) / 4, &scal[0]};
             if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
             a1 = ws + w.xq;
         } else if (perm_activations(L, &plan)) {

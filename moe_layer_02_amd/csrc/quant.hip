@@ -2,12 +2,13 @@
 //
 // fp8 w8a8 with per-tensor scales is how SGLang PR #2333 serves Qwen2-57B-A14B-FP8 and what
 // the FBGEMM article's grouped GEMM supports.  A tensor's scale is its largest magnitude
-// over 448 (the largest E4M3 value), so the largest element lands on +-448.  Two kernels:
-//   absmax: largest |x| over the tensor, combined across workgroups with an integer
-//           atomicMax on the fp32 bit pattern (non-negative floats order like their bits;
-//           max is order-independent, so the result is exact and reproducible);
-//   quant:  code = RNE_E4M3(x * (448 / amax)) (the product in fp32, clamped to +-448), and
-//           block 0 publishes scale = amax / 448 (1 when amax is 0) for the GEMM epilogue.
+// over 448 (the largest E4M3 value), so the largest element lands on +-448.  The largest
+// |x| comes from the pass before this one: for the hidden states as one partial maximum per
+// route workgroup (reduced here by every workgroup; non-negative floats order like their
+// bits, and max is order-independent, so the result is exact and reproducible), for the
+// intermediate h from GEMM1's epilogue atomics.  quant: code = RNE_E4M3(x * (448 / amax))
+// (the product in fp32, clamped to +-448), and block 0 publishes scale = amax / 448 (1 when
+// amax is 0) for the GEMM epilogue.
 #include "common.h"
 #include "kernels.h"
 #include "quant_dev.h"
@@ -17,48 +18,24 @@ namespace {
 
 using namespace quant_dev;
 
-// Same-address atomics serialise (about 16 ns each here), so the pass runs as at most one
-// 1024-thread workgroup per CU, each with one atomic, and keeps four 16-byte loads in
-// flight per thread (the maximum does not depend on the order).
-constexpr int kAbsmaxThreads = 1024;
-
-__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(AbsmaxArgs a) {
-    float m = 0.0f;
-    const int64_t n8 = a.n / 8, stride = (int64_t)gridDim.x * kAbsmaxThreads;
-    constexpr int U = 4;
-    for (int64_t i0 = (int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x; i0 < n8; i0 += U * stride) {
-        uint4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t i = i0 + u * stride;
-            v[u] = i < n8 ? ((const uint4 *)a.x)[i] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
-                m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
-            }
-        }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    __shared__ float wmax[kAbsmaxThreads / kWave];
-    if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float b = 0.0f;
-        for (int w = 0; w < kAbsmaxThreads / kWave; w++) b = fmaxf(b, wmax[w]);
-        amax_raise(a.amax, amax_peek(a.amax), b);
-    }
-}
-
 // 8 elements (bf16 or fp32) per thread -> 8 codes (one 8-byte store)
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     float scale, inv;
-    scales_from_amax(*a.amax, &scale, &inv);
+    uint32_t amax_bits;
+    if (a.amax_parts) {   // the largest of the partial maxima, by every workgroup
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < a.n_parts; i += 256) m = fmaxf(m, __uint_as_float(a.amax_parts[i]));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+        __shared__ float wmax[4];
+        if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
+        __syncthreads();
+        amax_bits = __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+        if (blockIdx.x == 0 && threadIdx.x == 0 && a.amax_out) *a.amax_out = amax_bits;
+    } else {
+        amax_bits = *a.amax;
+    }
+    scales_from_amax(amax_bits, &scale, &inv);
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.scale_out = scale;
     const int64_t c8 = a.cols / 8;
     int64_t rows = a.rows;
@@ -98,15 +75,6 @@ hipError_t launch_bf16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStrea
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(k_bf16_perm, dim3((unsigned)blocks), dim3(256), 0, s, x, y, n8);
-    return hipGetLastError();
-}
-
-hipError_t launch_absmax(const AbsmaxArgs &a, hipStream_t s) {
-    int64_t blocks = (a.n / 8 + kAbsmaxThreads - 1) / kAbsmaxThreads;
-    const int64_t cap = device_cu_count();
-    if (blocks > cap) blocks = cap;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(k_absmax, dim3((unsigned)blocks), dim3(kAbsmaxThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -8,7 +8,38 @@ template <int EPL, int V>
 __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
     if (blockIdx.x == 0 && a.zero_ptr && (int)threadIdx.x < a.zero_n) a.zero_ptr[threadIdx.x] = 0u;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // fp8: the token's hidden row is requested before the routing, which runs under its latency
+    constexpr int XP = 8;   // 16-byte groups of the row per lane held from before the routing
+    uint4 xv[XP];
+    const uint4 *row = (const uint4 *)(a.x + (int64_t)(t < a.T ? t : 0) * a.x_cols);
+    const int64_t n8 = a.x_parts && t < a.T ? a.x_cols / 8 : 0;
+#pragma unroll
+    for (int j = 0; j < XP; j++) {
+        const int64_t i = lane_id() + (int64_t)j * kWave;
+        xv[j] = i < n8 ? row[i] : make_uint4(0, 0, 0, 0);
+    }
     if (t < a.T) route_dev::route_token<EPL, V>(a, t);
+    if (a.x_parts) {   // the largest |x| of this workgroup's tokens (the quantisation reduces the parts)
+        float m = 0.0f;
+        auto fold = [&](const uint4 &g) {
+            const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                m = fmaxf(m, fabsf(__uint_as_float(w[q] << 16)));
+                m = fmaxf(m, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < XP; j++) fold(xv[j]);
+        for (int64_t i = lane_id() + (int64_t)XP * kWave; i < n8; i += kWave) fold(row[i]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+        __shared__ float wmax[4];
+        if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            a.x_parts[blockIdx.x] = __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+    }
 }
 
 // one instantiation per (experts per lane, routing variant): each holds only its own path
