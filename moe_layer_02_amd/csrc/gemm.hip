@@ -304,8 +304,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
             int pr[EQ];
 #pragma unroll
             for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
-#pragma unroll
-            for (int q = 0; q < EQ; q++) pin(pr[q]);
+            pin_all(pr);
 #pragma unroll
             for (int q = 0; q < EQ; q++) {
                 const int fm = q / 4, i = q % 4, row = row0 + epi_row(q);
@@ -328,11 +327,9 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
                 int pr[EQ];
 #pragma unroll
                 for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
+                pin_all(pr);
 #pragma unroll
-                for (int q = 0; q < EQ; q++) {
-                    pin(pr[q]);
-                    valid[q] = pr[q] < a.pairs;
-                }
+                for (int q = 0; q < EQ; q++) valid[q] = pr[q] < a.pairs;
             }
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
@@ -362,12 +359,12 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs a) {
             float wr[EQ];
 #pragma unroll
             for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
+            pin_all(pr);
 #pragma unroll
-            for (int q = 0; q < EQ; q++) pin(pr[q]);
+            for (int q = 0; q < EQ; q++) wr[q] = a.topk_w[pr[q] < a.pairs ? pr[q] : 0];   // filler: pair 0's
+            pin_all(wr);
 #pragma unroll
-            for (int q = 0; q < EQ; q++) wr[q] = a.topk_w[pr[q] < a.pairs ? pr[q] : 0] * scale;   // filler: pair 0's
-#pragma unroll
-            for (int q = 0; q < EQ; q++) pin(wr[q]);
+            for (int q = 0; q < EQ; q++) wr[q] *= scale;
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll

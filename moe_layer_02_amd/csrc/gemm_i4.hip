@@ -158,8 +158,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
                 kind[q] = which ? LD_Z : LD_S;
             }
         }
-        // weight streaming: each tile starts its K walk at its own step (see gemm_pipe.hip)
-        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nk : 0;
+        // weight streaming: each tile starts its K walk at a step of its expert and column
+        // tile, so an expert's row blocks stay in step (see gemm_pipe.hip)
+        const int krot = a.rotate_k ? (nt * 3 + e * 5) % nk : 0;
         // operand bases at the split's first K (wave-uniform); a K step advances A by 512
         // bytes (256 bf16), B by 128 (256 nibbles), scales and zeros by 4 (two groups)
         const char *base_a = uniform_ptr((const char *)a.A + (int64_t)s * a.ksplit * 2);
@@ -275,8 +276,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
             int pr[EQ];
 #pragma unroll
             for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
-#pragma unroll
-            for (int q = 0; q < EQ; q++) pin(pr[q]);
+            pin_all(pr);
 #pragma unroll
             for (int q = 0; q < EQ; q++) {
                 const int fm = q / 4, i = q % 4, row = row0 + epi_row(q);
@@ -309,12 +309,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_i4(GemmArgs a) {
             float wr[EQ];
 #pragma unroll
             for (int q = 0; q < EQ; q++) pr[q] = block_pair_nb(a, br, epi_row(q));
-#pragma unroll
-            for (int q = 0; q < EQ; q++) pin(pr[q]);
+            pin_all(pr);
 #pragma unroll
             for (int q = 0; q < EQ; q++) wr[q] = a.topk_w[pr[q] < a.pairs ? pr[q] : 0];   // filler: pair 0's
-#pragma unroll
-            for (int q = 0; q < EQ; q++) pin(wr[q]);
+            pin_all(wr);
 #pragma unroll
             for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll

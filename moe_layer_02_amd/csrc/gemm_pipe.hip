@@ -161,6 +161,10 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
         // The rows of this lane's accumulators, q = fm * NR + i, in chunks of at most 16: a
         // chunk's pairs (and GEMM2's weights) are read and pinned before its stores (see pin)
         constexpr int EQ = C::FM * NR, EQC = EQ < 16 ? EQ : 16;
+        // a chunk's loads pinned together where the tile has room for them (up to 128 x 256
+        // outputs, not the 16-wave tiles of 32 x 32 fragments); the others pin value by value
+        // and take the weight times the scale per value, which spills less there
+        constexpr int PG = C::BM * C::BN <= 128 * 256 && !(C::NW >= 16 && C::MS == 32) ? EQC : 1;
         auto epi_row = [&](int q) { return wm * C::TM + (q / NR) * C::MS + frag_row<C::MS>(lane, q % NR); };
         auto epi_pair = [&](int q) { return block_pair_nb(a, br, epi_row(q)); };
         if constexpr (KIND == GEMM_GATE_UP && PARTIAL) {
@@ -171,8 +175,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 int pr[EQC];
 #pragma unroll
                 for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(pr[j]);
+                pin_groups<1>(pr);
                 if (q0 == 0) ready();
 #pragma unroll
                 for (int j = 0; j < EQC; j++) {
@@ -195,8 +198,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 int pr[EQC];
 #pragma unroll
                 for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(pr[j]);
+                pin_groups<1>(pr);
                 if (q0 == 0) ready();
 #pragma unroll
                 for (int j = 0; j < EQC; j++) {
@@ -223,11 +225,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                     int pr[EQC];
 #pragma unroll
                     for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+                    pin_groups<1>(pr);
 #pragma unroll
-                    for (int j = 0; j < EQC; j++) {
-                        pin(pr[j]);
-                        valid[j] = pr[j] < a.pairs;
-                    }
+                    for (int j = 0; j < EQC; j++) valid[j] = pr[j] < a.pairs;
                 } else {
 #pragma unroll
                     for (int j = 0; j < EQC; j++) valid[j] = true;
@@ -268,17 +268,23 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 float wr[EQC];
 #pragma unroll
                 for (int j = 0; j < EQC; j++) pr[j] = epi_pair(q0 + j);
+                pin_groups<PG>(pr);
+                if (a.topk_w && PG > 1) {   // filler rows read pair 0's weight
 #pragma unroll
-                for (int j = 0; j < EQC; j++) pin(pr[j]);
-                if (a.topk_w) {   // filler rows read pair 0's weight
+                    for (int j = 0; j < EQC; j++) wr[j] = a.topk_w[pr[j] < a.pairs ? pr[j] : 0];
+                    pin_groups<PG>(wr);
 #pragma unroll
-                    for (int j = 0; j < EQC; j++) wr[j] = a.topk_w[pr[j] < a.pairs ? pr[j] : 0] * scale;
-                } else {          // the grouped GEMM has no weight
+                    for (int j = 0; j < EQC; j++) wr[j] *= scale;
+                } else {
+                    if (a.topk_w) {
 #pragma unroll
-                    for (int j = 0; j < EQC; j++) wr[j] = scale;
+                        for (int j = 0; j < EQC; j++) wr[j] = a.topk_w[pr[j] < a.pairs ? pr[j] : 0] * scale;
+                    } else {      // the grouped GEMM has no weight
+#pragma unroll
+                        for (int j = 0; j < EQC; j++) wr[j] = scale;
+                    }
+                    pin_groups<1>(wr);
                 }
-#pragma unroll
-                for (int j = 0; j < EQC; j++) pin(wr[j]);
                 if (q0 == 0) ready();
 #pragma unroll
                 for (int j = 0; j < EQC; j++) {
@@ -363,12 +369,14 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
                 dst[q] = C::A_STAGE + (slab * C::BN + rb) * C::SB;
             }
         }
-        // with rotate_k (weight streaming: no two tiles share operands) each tile walks its K
-        // range from its own starting step, cyclically, so that concurrent tiles spread over
-        // DRAM channels instead of all reading the same column slice of rows that share
-        // address bits; tiles that share A or B rows keep K in step for L2 reuse.  The
-        // order is fixed per tile, so results stay reproducible.
-        const int krot = a.rotate_k ? (nt * 3 + mb * 5) % nku : 0;
+        // with rotate_k (weight streaming: about one block of rows per expert) each tile walks
+        // its K range from its own starting step, cyclically, so that concurrent tiles spread
+        // over DRAM channels instead of all reading the same column slice of rows that share
+        // address bits.  The start depends on the expert and the column tile, not on the row
+        // block, so that the blocks of an expert with more rows than one block stream their
+        // common weight tile in step (L2 reuse); without rotate_k every tile keeps K in step.
+        // The order is fixed per tile, so results stay reproducible.
+        const int krot = a.rotate_k ? (nt * 3 + e * 5) % nku : 0;
         const char *base_a = uniform_ptr((const char *)a.A + kb);
         const char *base_b = uniform_ptr((const char *)a.B + (int64_t)e * a.b_expert_stride + kb);
         // the loads of step kstep: A's, B's or both (dst holds B's offsets past A_STAGE)

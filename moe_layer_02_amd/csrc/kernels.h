@@ -112,6 +112,35 @@ template <class T>
 __device__ __forceinline__ void pin(T &v) {
     asm volatile("" : "+v"(v));
 }
+// Values of a chunk taken into registers G at a time, each group by one statement: the loads
+// of a group are all in flight before its wait.  With a pin per value (G = 1) the compiler
+// may, under register pressure, place the wait for one load (and the arithmetic that uses
+// it) before it issues the next, one memory latency per value; a larger group keeps up to G
+// more values live at once, which the register-tight tiles pay for in spills.
+template <int G, class T, int N>
+__device__ __forceinline__ void pin_groups(T (&v)[N]) {
+    static_assert(N % G == 0 && (G == 1 || G == 4 || G == 8 || G == 16), "groups of 1, 4, 8 or 16");
+#pragma unroll
+    for (int c = 0; c < N; c += G) {
+        if constexpr (G == 1) {
+            asm volatile("" : "+v"(v[c]));
+        } else if constexpr (G == 4) {
+            asm volatile("" : "+v"(v[c]), "+v"(v[c + 1]), "+v"(v[c + 2]), "+v"(v[c + 3]));
+        } else if constexpr (G == 8) {
+            asm volatile("" : "+v"(v[c]), "+v"(v[c + 1]), "+v"(v[c + 2]), "+v"(v[c + 3]), "+v"(v[c + 4]),
+                         "+v"(v[c + 5]), "+v"(v[c + 6]), "+v"(v[c + 7]));
+        } else {
+            asm volatile("" : "+v"(v[c]), "+v"(v[c + 1]), "+v"(v[c + 2]), "+v"(v[c + 3]), "+v"(v[c + 4]),
+                         "+v"(v[c + 5]), "+v"(v[c + 6]), "+v"(v[c + 7]), "+v"(v[c + 8]), "+v"(v[c + 9]),
+                         "+v"(v[c + 10]), "+v"(v[c + 11]), "+v"(v[c + 12]), "+v"(v[c + 13]), "+v"(v[c + 14]),
+                         "+v"(v[c + 15]));
+        }
+    }
+}
+template <class T, int N>
+__device__ __forceinline__ void pin_all(T (&v)[N]) {
+    pin_groups<N>(v);
+}
 
 struct TileInfo {
     int BM, BN, BK, WM, WN;      // tile rows, B rows per tile, K step, wave grid
