@@ -38,6 +38,14 @@ __device__ __forceinline__ uint4 bf16x8_perm(uint4 v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// SiLU(g) = g sigmoid(g) in fp32 for the gate/up epilogues: the hardware exp and reciprocal
+// (each within about an ulp) in place of a correctly rounded division, which costs about ten
+// dependent instructions per value where this takes two.  The result is within a few ulps of
+// the exact value, far inside what the product's later rounding (h to bf16, or the fp8
+// codes decided from this h) and the tolerance allow.  Large negative g: the reciprocal of
+// +inf is 0 and the result -0, as the division gives; large positive g: g.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 // A maximum of non-negative floats kept as their bits (which order like the floats) in one
 // device word.  Atomics on one address serialise (about 16 ns each on these GPUs), so a
 // caller reads the word first (amax_peek, a device-scope load that may be issued early)

@@ -50,8 +50,6 @@ struct Cfg {
     static_assert(WT != WT_INT4 || BK % 128 == 0, "int4 K step must hold whole groups");
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
 // 8 nibbles (k = 0..7 of one row, byte b = k/2, low nibble first) -> bf16 (q - z) * s in
 // the natural order.  q - z is an integer of at most 4 bits and s an fp16 value, so the
 // fp32 product is exact and the bf16 weight is rounded once (to nearest even).

@@ -83,8 +83,6 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
 // LDS position of 16-byte chunk c of tile row r is c ^ swz(r): a pair of rows shares a
 // position in the two halves of the 64 banks, 8 pairs cover the 8 positions, so 16 lanes
 // reading one chunk of 16 consecutive rows hit 64 distinct banks

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_gate_up_finish(GateUpFinishArgs a) {
         }
         float h[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) h[j] = g[j] / (1.0f + __expf(-g[j])) * u[j];
+        for (int j = 0; j < 8; j++) h[j] = silu(g[j]) * u[j];
         if (a.h_kind == GATE_UP_H_F32) {
             float *o = (float *)a.h + r * a.I + c;
             *(float4 *)o = make_float4(h[0], h[1], h[2], h[3]);
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(1024) void k_gate_up_finish_quant(GateUpFinishArgs 
         float h[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            h[j] = g[j] / (1.0f + __expf(-g[j])) * u[j];
+            h[j] = silu(g[j]) * u[j];
             m = fmaxf(m, fabsf(h[j]));
         }
         float *o = (float *)a.h + r * a.I + c;
