@@ -320,8 +320,13 @@ __global__ __launch_bounds__(C::NT, C::MINW) void k_gemm_pipe(GemmArgs a) {
         const int s = tc.s, mb = tail ? mb_dp + tc.mb : tc.mb, nt = tc.nt;
         const int kbeg = tail ? s * nk / tail_s : s * nk;     // first K step and number of steps
         const int nku = tail ? (s + 1) * nk / tail_s - kbeg : nk;
-        const int e = __builtin_amdgcn_readfirstlane(a.eids[mb]);
-        const BlockRows br = block_rows(a, mb, C::BM);
+        // the block's expert and rows through the scalar cache (see sload)
+        const int e = sload(a.eids + mb);
+        BlockRows br{mb * C::BM, C::BM};
+        if (a.blk_start) {
+            const int2 be = sload_pair(a.blk_start + mb);
+            br = BlockRows{be.x, be.y - be.x};
+        }
         const int row0 = br.row0;   // first row of the block in h / y (the layout's)
         const int64_t kb = (int64_t)kbeg * C::BK * ebytes;    // byte offset of this unit's K
 

@@ -57,6 +57,28 @@ __device__ __forceinline__ void lds_dma_off(const void *base, uint32_t voff, uin
 }
 #pragma clang diagnostic pop
 
+// A wave-uniform 32-bit read through the scalar data cache, waited for in the same statement:
+// the value lands in an SGPR, and the wait (lgkmcnt) leaves the wave's vector loads and
+// stores in flight, where a vector load's vmcnt wait would drain them -- the stores of the
+// previous tile's epilogue, or stages already issued.  For the tile walk's small read-only
+// arrays (expert of each row block, block starts), written by an earlier launch.
+__device__ __forceinline__ int sload(const int32_t *p) {
+    const int32_t *q = uniform_ptr(p);
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(v) : "s"(q) : "memory");
+    return v;
+}
+// p[0] and p[1], both in flight before the one wait
+__device__ __forceinline__ int2 sload_pair(const int32_t *p) {
+    const int32_t *q = uniform_ptr(p);
+    int v0, v1;
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %2, 0x4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(v0), "=&s"(v1)
+                 : "s"(q)
+                 : "memory");
+    return make_int2(v0, v1);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -168,11 +190,11 @@ __device__ __forceinline__ TileCoord tile_coord_expert(int tile, int mn, int mbl
     c.s = tile / mn;
     const int rest = tile - c.s * mn;
     const int bt = rest / ntiles;                 // a block of rest's group (groups span all column tiles)
-    const int e = eids[bt];
+    const int e = sload(eids + bt);
     int lo = 0, hi = bt;                          // first block of expert e
     while (lo < hi) {
         const int m = (lo + hi) / 2;
-        if (eids[m] < e) lo = m + 1;
+        if (sload(eids + m) < e) lo = m + 1;
         else hi = m;
     }
     const int efirst = lo;
@@ -180,7 +202,7 @@ __device__ __forceinline__ TileCoord tile_coord_expert(int tile, int mn, int mbl
     hi = mblocks;
     while (lo < hi) {
         const int m = (lo + hi) / 2;
-        if (eids[m] <= e) lo = m + 1;
+        if (sload(eids + m) <= e) lo = m + 1;
         else hi = m;
     }
     const int b0 = efirst + (bt - efirst) / gmax * gmax;
