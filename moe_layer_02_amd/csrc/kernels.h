@@ -17,11 +17,13 @@ struct RouteArgs {
     float *weights;
     uint32_t *zero_ptr;          // words cleared by the launch (scratch counters), may be null
     int zero_n;                  // <= 256
-    // fp8: the hidden states [T, x_cols] bf16, and one word per workgroup receiving the
-    // largest |x| of its tokens as float bits (null: none)
+    // the hidden states [T, x_cols] bf16 where the route also reads them: fp8, one word per
+    // workgroup receiving the largest |x| of its tokens as float bits (x_parts); int4, the
+    // rows in the nibble order of the int4 GEMM's A (x_perm, [T, x_cols]); null: neither
     const uint16_t *x;
     int64_t x_cols;
     uint32_t *x_parts;
+    uint16_t *x_perm;
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 
@@ -158,8 +160,9 @@ hipError_t launch_gemm(int wdtype, int tile, GemmKind kind, bool partial, const 
 bool pipe_tile_info(int wdtype, int tile, TileInfo *info);
 hipError_t launch_gemm_pipe(int wdtype, int tile, GemmKind kind, bool partial, const GemmArgs &a,
                             int64_t max_tiles, hipStream_t s);
-// int4 tiles of the pipelined kind (gemm_i4.hip): A is fp16 in the (0,4,1,5,2,6,3,7) order
-// inside every 8 columns (launch_bf16_perm), and GEMM1 writes h as bf16 in the same order
+// int4 tiles of the pipelined kind (gemm_i4.hip): A is bf16 in the (0,4,1,5,2,6,3,7) order
+// inside every 8 columns (bf16x8_perm, written by the route or the prologue), and GEMM1
+// writes h as bf16 in the same order
 bool i4_tile_info(int tile, TileInfo *info);
 hipError_t launch_gemm_i4(int tile, GemmKind kind, bool partial, const GemmArgs &a, int64_t max_tiles,
                           hipStream_t s);
@@ -224,7 +227,6 @@ struct QuantArgs {
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 
 // bf16 [n8 * 8] with each group of 8 reordered (0,4,1,5,2,6,3,7) (int4 GEMM1's A)
-hipError_t launch_bf16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream_t s);
 
 // Route + align (+ the activation pass) of a batch of at most kPrologueMaxT tokens in one
 // launch (prologue.hip); results identical to launch_route, launch_align and the fp8 /

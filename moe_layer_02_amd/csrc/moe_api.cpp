@@ -298,10 +298,13 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
         // fp8: the route's workgroups also take the largest |x| of their tokens, one word each,
         // in h's space (free until GEMM1 writes h); the quantisation reduces them
         uint32_t *x_parts = fp8 ? (uint32_t *)(ws + w.h) : nullptr;
-        if (fp8) {
+        // int4: the route's waves also write their tokens' rows in the GEMM's nibble order
+        const bool perm = !fp8 && perm_activations(L, &plan);
+        if (fp8 || perm) {
             ra.x = (const uint16_t *)hidden;
             ra.x_cols = H;
             ra.x_parts = x_parts;
+            ra.x_perm = perm ? (uint16_t *)(ws + w.xq) : nullptr;
         }
         if ((err = launch_route(ra, stream)) != hipSuccess) return fail(err);
 
@@ -317,12 +320,10 @@ moe_status forward_impl(const moe_layer *L, int32_t T, const void *hidden, const
                         x_parts, (T + 3) / 4, &scal[0]};
             if ((err = launch_quant(q, stream)) != hipSuccess) return fail(err);
             a1 = ws + w.xq;
-        } else if (perm_activations(L, &plan)) {
-            // int4: the hidden states in the order the kernel unpacks nibbles
+        } else if (perm) {
+            // int4: the hidden states in the order the kernel unpacks nibbles (written by the
+            // route above)
             if ((err = mark(MOE_STAGE_ACT_QUANT)) != hipSuccess) return MOE_ERR_HIP;
-            if ((err = launch_bf16_perm((const uint16_t *)hidden, (uint16_t *)(ws + w.xq), (int64_t)T * H / 8, stream)) !=
-                hipSuccess)
-                return fail(err);
             a1 = ws + w.xq;
         }
     }

@@ -60,23 +60,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a) {
     }
 }
 
-// int4 GEMM1's A: each 8 bf16 reordered into the packed-nibble order, one 16-byte load and
-// store
-__global__ __launch_bounds__(256) void k_bf16_perm(const uint16_t *x, uint16_t *y, int64_t n8) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
-        ((uint4 *)y)[i] = bf16x8_perm(((const uint4 *)x)[i]);
-}
-
 }  // namespace
-
-hipError_t launch_bf16_perm(const uint16_t *x, uint16_t *y, int64_t n8, hipStream_t s) {
-    int64_t blocks = (n8 + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 8;
-    if (blocks > cap) blocks = cap;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(k_bf16_perm, dim3((unsigned)blocks), dim3(256), 0, s, x, y, n8);
-    return hipGetLastError();
-}
 
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s) {
     int64_t blocks = (a.rows * (a.cols / 8) + 255) / 256;

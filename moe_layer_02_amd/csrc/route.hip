@@ -1,4 +1,5 @@
-// route.hip -- router top-k, one wavefront per token (the selection itself: route_dev.h).
+// route.hip -- router top-k, one wavefront per token (the selection itself: route_dev.h); the
+// same waves read their tokens' hidden rows for the activation pass of the fp8 and int4 layers.
 #include "route_dev.h"
 
 namespace moe {
@@ -8,17 +9,27 @@ template <int EPL, int V>
 __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
     if (blockIdx.x == 0 && a.zero_ptr && (int)threadIdx.x < a.zero_n) a.zero_ptr[threadIdx.x] = 0u;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    // fp8: the token's hidden row is requested before the routing, which runs under its latency
+    // fp8 and int4: the token's hidden row is requested before the routing, which runs under
+    // its latency
     constexpr int XP = 8;   // 16-byte groups of the row per lane held from before the routing
     uint4 xv[XP];
     const uint4 *row = (const uint4 *)(a.x + (int64_t)(t < a.T ? t : 0) * a.x_cols);
-    const int64_t n8 = a.x_parts && t < a.T ? a.x_cols / 8 : 0;
+    const int64_t n8 = (a.x_parts || a.x_perm) && t < a.T ? a.x_cols / 8 : 0;
 #pragma unroll
     for (int j = 0; j < XP; j++) {
         const int64_t i = lane_id() + (int64_t)j * kWave;
         xv[j] = i < n8 ? row[i] : make_uint4(0, 0, 0, 0);
     }
     if (t < a.T) route_dev::route_token<EPL, V>(a, t);
+    if (a.x_perm) {   // int4: the row with each 8 values in the nibble order (bf16x8_perm)
+        uint4 *out = (uint4 *)(a.x_perm + (int64_t)t * a.x_cols);
+#pragma unroll
+        for (int j = 0; j < XP; j++) {
+            const int64_t i = lane_id() + (int64_t)j * kWave;
+            if (i < n8) out[i] = bf16x8_perm(xv[j]);
+        }
+        for (int64_t i = lane_id() + (int64_t)XP * kWave; i < n8; i += kWave) out[i] = bf16x8_perm(row[i]);
+    }
     if (a.x_parts) {   // the largest |x| of this workgroup's tokens (the quantisation reduces the parts)
         float m = 0.0f;
         auto fold = [&](const uint4 &g) {
