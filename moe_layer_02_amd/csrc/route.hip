@@ -28,7 +28,20 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
             const int64_t i = lane_id() + (int64_t)j * kWave;
             if (i < n8) out[i] = bf16x8_perm(xv[j]);
         }
-        for (int64_t i = lane_id() + (int64_t)XP * kWave; i < n8; i += kWave) out[i] = bf16x8_perm(row[i]);
+        // the rest of the row in batches of XP groups, each batch's loads in flight together
+        for (int64_t b = (int64_t)XP * kWave; b < n8; b += (int64_t)XP * kWave) {
+            uint4 v[XP];
+#pragma unroll
+            for (int j = 0; j < XP; j++) {
+                const int64_t i = b + lane_id() + (int64_t)j * kWave;
+                v[j] = i < n8 ? row[i] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < XP; j++) {
+                const int64_t i = b + lane_id() + (int64_t)j * kWave;
+                if (i < n8) out[i] = bf16x8_perm(v[j]);
+            }
+        }
     }
     if (a.x_parts) {   // the largest |x| of this workgroup's tokens (the quantisation reduces the parts)
         float m = 0.0f;
@@ -42,7 +55,16 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
         };
 #pragma unroll
         for (int j = 0; j < XP; j++) fold(xv[j]);
-        for (int64_t i = lane_id() + (int64_t)XP * kWave; i < n8; i += kWave) fold(row[i]);
+        for (int64_t b = (int64_t)XP * kWave; b < n8; b += (int64_t)XP * kWave) {   // the rest, XP at a time
+            uint4 v[XP];
+#pragma unroll
+            for (int j = 0; j < XP; j++) {
+                const int64_t i = b + lane_id() + (int64_t)j * kWave;
+                v[j] = i < n8 ? row[i] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < XP; j++) fold(v[j]);
+        }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
         __shared__ float wmax[4];
